@@ -1,0 +1,256 @@
+"""qi4 oracle -- TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+
+A plain fp64 CPU implementation of the int4 group-quantized linear layer and
+the routed MoE expert FFN (see ``qi4_oracle.c`` for the definitions and the
+page passages they follow).  Only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s CPU-baseline leg may import this package.  It shares no code
+with the GPU library and never imports it.
+
+This module is a thin ctypes shim: it widens activations to float64, checks
+shapes and calls the C functions.  All arithmetic of the method is in C.
+Every exported function is pinned by tests in ``tests/test_oracle_*.py``; a
+function whose pin is missing would say "parity unpinned" here (none does).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqi4_oracle.so")
+_lib = None
+
+#: relative tolerance factor of one linear layer: |gpu - oracle| <= C_TOL * sum|w*x|
+C_TOL = 2e-3
+#: bound on the error of the fp32 combine weights relative to the fp64 ones
+EPS_P = 1e-5
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64 = ctypes.c_int64
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, no fast-math, no FP contraction)."""
+    from oracle.build import build_oracle
+    return build_oracle(verbose=verbose)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.qi4o_abi_version.restype = ctypes.c_int
+        L.qi4o_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.qi4o_f16_to_f64.restype = ctypes.c_double
+        L.qi4o_f64_to_f16.argtypes = [ctypes.c_double]
+        L.qi4o_f64_to_f16.restype = ctypes.c_uint16
+        L.qi4o_silu.argtypes = [ctypes.c_double]
+        L.qi4o_silu.restype = ctypes.c_double
+        L.qi4o_unpack.argtypes = [_u8p, _i64, _i64, _u8p]
+        L.qi4o_dequant.argtypes = [_u8p, _u16p, _u8p, _i64, _i64, _i64, _dp]
+        L.qi4o_linear.argtypes = [_dp, _i64, _i64, _u8p, _u16p, _u8p, _i64, _i64,
+                                  _dp, _dp, ctypes.c_int]
+        L.qi4o_gate_up_silu.argtypes = [_dp, _i64, _i64, _u8p, _u16p, _u8p, _i64, _i64,
+                                        ctypes.c_double, _dp, _dp, ctypes.c_int]
+        L.qi4o_topk_softmax.argtypes = [_fp, _i64, _i64, ctypes.c_int, _i32p, _dp]
+        L.qi4o_sort.argtypes = [_i32p, _i64, ctypes.c_int, _i64, _i32p, _i32p, _i32p]
+        L.qi4o_moe.argtypes = ([_dp, _i64, _i64, _i64, _i64, ctypes.c_int, _i32p, _dp]
+                               + [_u8p, _u16p, _u8p] * 4
+                               + [_i64, ctypes.c_double, ctypes.c_double, _dp, _dp, ctypes.c_int])
+        L.qi4o_quantize.argtypes = [_dp, _i64, _i64, _i64, _u8p, _u16p, _u8p]
+        for f in ("qi4o_unpack", "qi4o_dequant", "qi4o_linear", "qi4o_gate_up_silu",
+                  "qi4o_topk_softmax", "qi4o_sort", "qi4o_moe", "qi4o_quantize"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None, t):
+    if a is None:
+        return ctypes.cast(None, t)
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(t)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ---- activations --------------------------------------------------------
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Activations to float64.  ``dtype`` 'bf16' means x holds bf16 bit patterns
+    (uint16): the value is those 16 bits followed by 16 zero bits read as an IEEE
+    binary32 number, which widens exactly to binary64."""
+    if dtype == "bf16":
+        assert x.dtype == np.uint16
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.ascontiguousarray(x, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+# ---- scalar helpers -----------------------------------------------------
+
+def f16_to_f64(bits: int) -> float:
+    return lib().qi4o_f16_to_f64(int(bits))
+
+
+def f64_to_f16(v: float) -> int:
+    return int(lib().qi4o_f64_to_f16(float(v)))
+
+
+def silu(v: float) -> float:
+    return lib().qi4o_silu(float(v))
+
+
+# ---- the format ----------------------------------------------------------
+
+def unpack(qweight: np.ndarray, N: int, K: int) -> np.ndarray:
+    qweight = np.ascontiguousarray(qweight, dtype=np.uint8)
+    assert qweight.size == N * (K // 2)
+    q = np.empty((N, K), dtype=np.uint8)
+    _check(lib().qi4o_unpack(_ptr(qweight, _u8p), N, K, _ptr(q, _u8p)), "unpack")
+    return q
+
+
+def dequant(qweight, scales, zeros, N: int, K: int, group: int = 128) -> np.ndarray:
+    qweight = np.ascontiguousarray(qweight, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    assert qweight.size == N * (K // 2) and scales.size == N * (K // group) == zeros.size
+    w = np.empty((N, K), dtype=np.float64)
+    _check(lib().qi4o_dequant(_ptr(qweight, _u8p), _ptr(scales, _u16p), _ptr(zeros, _u8p),
+                              N, K, group, _ptr(w, _dp)), "dequant")
+    return w
+
+
+# ---- the linear layer ------------------------------------------------------
+
+def linear(x64: np.ndarray, qweight, scales, zeros, N: int, K: int, group: int = 128,
+           threads: int | None = None):
+    """Return (y, S): y = x . dequant(W)^T and S = sum_k |x*w|, both [T][N] float64."""
+    x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(-1, K)
+    T = x64.shape[0]
+    qweight = np.ascontiguousarray(qweight, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    assert qweight.size == N * (K // 2) and scales.size == N * (K // group) == zeros.size
+    y = np.empty((T, N), dtype=np.float64)
+    S = np.empty((T, N), dtype=np.float64)
+    _check(lib().qi4o_linear(_ptr(x64, _dp), T, K, _ptr(qweight, _u8p), _ptr(scales, _u16p),
+                             _ptr(zeros, _u8p), N, group, _ptr(y, _dp), _ptr(S, _dp),
+                             threads or default_threads()), "linear")
+    return y, S
+
+
+def gate_up_silu(x64: np.ndarray, qweight, scales, zeros, I: int, K: int, group: int = 128,
+                 c: float = C_TOL, threads: int | None = None):
+    """Return (h, tol_h) for the fused SiLU(gate)*up of a [gate; up] weight (2I x K)."""
+    x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(-1, K)
+    T = x64.shape[0]
+    h = np.empty((T, I), dtype=np.float64)
+    tol = np.empty((T, I), dtype=np.float64)
+    _check(lib().qi4o_gate_up_silu(_ptr(x64, _dp), T, K,
+                                   _ptr(np.ascontiguousarray(qweight, dtype=np.uint8), _u8p),
+                                   _ptr(np.ascontiguousarray(scales, dtype=np.uint16), _u16p),
+                                   _ptr(np.ascontiguousarray(zeros, dtype=np.uint8), _u8p),
+                                   I, group, c, _ptr(h, _dp), _ptr(tol, _dp),
+                                   threads or default_threads()), "gate_up_silu")
+    return h, tol
+
+
+# ---- router and permutation ----------------------------------------------
+
+def topk_softmax(logits: np.ndarray, k: int):
+    """Return (ids int32 [T][k], p float64 [T][k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    p = np.empty((T, k), dtype=np.float64)
+    _check(lib().qi4o_topk_softmax(_ptr(logits, _fp), T, E, k, _ptr(ids, _i32p), _ptr(p, _dp)),
+           "topk_softmax")
+    return ids, p
+
+
+def sort_tokens(ids: np.ndarray, E: int):
+    """Return (sorted_pairs [T*k], offsets [E+1], pair_to_sorted [T*k]), all int32."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    sp = np.empty(T * k, dtype=np.int32)
+    off = np.empty(E + 1, dtype=np.int32)
+    inv = np.empty(T * k, dtype=np.int32)
+    _check(lib().qi4o_sort(_ptr(ids, _i32p), T, k, E, _ptr(sp, _i32p), _ptr(off, _i32p),
+                           _ptr(inv, _i32p)), "sort")
+    return sp, off, inv
+
+
+# ---- the MoE FFN -------------------------------------------------------------
+
+def moe(x64: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: dict, shared: dict | None,
+        H: int, I: int, E: int, group: int = 128, c: float = C_TOL, eps_p: float = EPS_P,
+        threads: int | None = None):
+    """Return (out, tol), both [T][H] float64.
+
+    ``experts`` holds canonical arrays for all E routed experts:
+    gu_q [E][2I][H/2], gu_s/gu_z [E][2I][H/G], dn_q [E][H][I/2], dn_s/dn_z [E][H][I/G].
+    ``shared`` holds the same keys for one expert (no leading E), or None.
+    """
+    x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(-1, H)
+    T = x64.shape[0]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    k = ids.shape[1]
+    out = np.empty((T, H), dtype=np.float64)
+    tol = np.empty((T, H), dtype=np.float64)
+
+    def arrs(d):
+        if d is None:
+            return [None] * 6
+        return [np.ascontiguousarray(d["gu_q"], dtype=np.uint8),
+                np.ascontiguousarray(d["gu_s"], dtype=np.uint16),
+                np.ascontiguousarray(d["gu_z"], dtype=np.uint8),
+                np.ascontiguousarray(d["dn_q"], dtype=np.uint8),
+                np.ascontiguousarray(d["dn_s"], dtype=np.uint16),
+                np.ascontiguousarray(d["dn_z"], dtype=np.uint8)]
+
+    ea, sa = arrs(experts), arrs(shared)
+    types = [_u8p, _u16p, _u8p] * 2
+    _check(lib().qi4o_moe(_ptr(x64, _dp), T, H, I, E, k, _ptr(ids, _i32p), _ptr(p, _dp),
+                          *[_ptr(a, t) for a, t in zip(ea, types)],
+                          *[_ptr(a, t) for a, t in zip(sa, types)],
+                          group, c, eps_p, _ptr(out, _dp), _ptr(tol, _dp),
+                          threads or default_threads()), "moe")
+    return out, tol
+
+
+# ---- reference quantizer -------------------------------------------------
+
+def quantize(w: np.ndarray, group: int = 128):
+    """Min/max asymmetric quantizer; returns canonical (qweight, scales, zeros)."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    N, K = w.shape
+    qw = np.empty((N, K // 2), dtype=np.uint8)
+    s = np.empty((N, K // group), dtype=np.uint16)
+    z = np.empty((N, K // group), dtype=np.uint8)
+    _check(lib().qi4o_quantize(_ptr(w, _dp), N, K, group, _ptr(qw, _u8p), _ptr(s, _u16p),
+                               _ptr(z, _u8p)), "quantize")
+    return qw, s, z
