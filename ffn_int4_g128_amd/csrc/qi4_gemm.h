@@ -1,0 +1,47 @@
+// The int4-g128 GEMM core shared by the dense linear layer and the grouped
+// expert GEMMs of the MoE FFN.
+#pragma once
+
+#include "qi4_dev.h"
+
+namespace qi4 {
+
+enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_SPLIT2 = 2 };
+
+// One launch computes out[dst(s)][n] = epi(sum_k A[src(s)][k] * W[n][k]) for the
+// "slots" s of one or more problems (a problem = one weight matrix and the rows
+// of A that use it).  blockIdx.y picks the problem, blockIdx.x a block of tiles.
+struct GemmArgs {
+    // weights (packed)
+    const uint8_t *w;          // dense matrix, or routed expert 0
+    int64_t w_stride;          // bytes between routed experts
+    const uint8_t *w_shared;   // shared expert (moe) or nullptr
+    int64_t N, K;              // rows and reduction length of each matrix
+    int flags;                 // QI4_PACK_GATEUP or 0
+    // activations
+    const void *a;             // bf16 bits, or float32 when a_f32
+    int64_t lda;               // elements per A source row
+    int a_f32;                 // float32 rows, split into 4 bf16 terms in registers
+    int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
+    // problems
+    int moe;                   // 0: one dense problem with T slots
+    int64_t T;                 // tokens
+    int top_k;
+    const int32_t *sorted_pairs;  // moe gate/up: slot -> pair -> token
+    const int32_t *offsets;       // moe: expert segment starts (E + 1)
+    const int32_t *active;        // moe: [count, experts...]
+    int routed_slots;             // moe: problem slots for routed experts in grid.y
+    int gather_tokens;            // moe: A rows are tokens (gate/up) rather than slots (down)
+    // output
+    void *out;
+    int64_t ldo;               // elements per output row
+    int out_mode;              // OutMode
+    int epi;                   // QI4_EPI_NONE or QI4_EPI_SILU_MUL
+    int64_t n_out;             // valid output columns
+};
+
+// Launch the GEMM for `n_problems` problems (grid.y); `max_slots` bounds the
+// slots of any one problem and picks the M tiling.  Returns a QI4 status.
+int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t stream);
+
+}  // namespace qi4

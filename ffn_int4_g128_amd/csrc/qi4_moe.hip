@@ -1,0 +1,505 @@
+// Routed mixture-of-experts FFN on int4-g128 experts: router top-k, the
+// token-by-expert permutation, the grouped expert GEMMs and the combine.
+//
+// The pages describe MoE layers whose experts hold most of the parameters while
+// each token activates only a few of them (FastLLM notes, wmrh.cn, part 1), the
+// number of routed experts per token as a knob (--moe_experts) and a shared
+// expert that always runs (--cuda_se) (fastllm README, "other parameters").
+// Here the routed experts a batch touches are found on the device (sort), and
+// one launch per projection covers all of them: grid.y enumerates the touched
+// experts plus the shared one, grid.x the 16-row tiles of each expert's matrix.
+// Only touched experts' weights are read.
+#include <limits.h>
+
+#include "qi4_gemm.h"
+#include "qi4_host.h"
+
+namespace qi4 {
+namespace {
+
+constexpr int kRouteWaves = 4;
+constexpr int kSortWaves = 8;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+// ---- router: one wave per token --------------------------------------------------
+
+template <int VPL>
+__global__ void __launch_bounds__(kRouteWaves * 64)
+route_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
+             int32_t *__restrict__ ids, float *__restrict__ wts) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float v[VPL];
+    bool taken[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = i * 64 + lane;
+        float x = e < E ? logits[t * E + e] : -INFINITY;
+        if (x != x) x = -INFINITY;   // NaN ranks like -inf
+        v[i] = x;
+        taken[i] = e >= E;
+    }
+    float myv = -INFINITY;
+    int myi = 0;
+    for (int jj = 0; jj < k; ++jj) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int e = i * 64 + lane;
+            if (!taken[i] && (v[i] > bv || (v[i] == bv && e < bi))) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (bi == i * 64 + lane) taken[i] = true;
+        if (lane == jj) {
+            myv = bv;
+            myi = bi;
+        }
+    }
+    const float l0 = __shfl(myv, 0);
+    float ex = lane < k ? expf(myv - l0) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane < k) {
+        ids[t * k + lane] = myi;
+        wts[t * k + lane] = ex / sum;
+    }
+}
+
+// ---- stable counting sort of the (token, slot) pairs by expert ----------------------
+
+// Lanes of this wave holding the same expert id (valid lanes only).
+__device__ inline uint64_t match_expert(int e, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+__global__ void __launch_bounds__(kSortWaves * 64)
+sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
+            int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ offsets,
+            int32_t *__restrict__ pair_to_sorted, int32_t *__restrict__ active) {
+    __shared__ int cnt[kSortWaves][kMaxExperts];
+    __shared__ int off_s[kMaxExperts + 1];
+    __shared__ int tot_s[kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    int64_t chunk = (npairs + kSortWaves - 1) / kSortWaves;
+    chunk = (chunk + 63) & ~int64_t(63);
+    const int64_t pb = wave * chunk;
+    const int64_t pe = pb + chunk < npairs ? pb + chunk : npairs;
+
+    for (int i = threadIdx.x; i < kSortWaves * E; i += blockDim.x) cnt[i / E][i % E] = 0;
+    __syncthreads();
+
+    // histogram of this wave's chunk (ids outside [0, E) are left out)
+    for (int64_t pos = pb; pos < pe; pos += 64) {
+        const int64_t i = pos + lane;
+        int e = i < pe ? ids[i] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        if (!valid) e = 0;
+        const uint64_t m = match_expert(e, valid, nbits);
+        if (valid && (__ffsll((unsigned long long)m) - 1) == lane) cnt[wave][e] += __popcll(m);
+    }
+    __syncthreads();
+
+    // per expert: exclusive prefix over the waves, and the total
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int c = cnt[w][e];
+            cnt[w][e] = run;
+            run += c;
+        }
+        tot_s[e] = run;
+    }
+    __syncthreads();
+
+    // exclusive scan over the experts (wave 0), plus the list of nonempty experts
+    if (wave == 0) {
+        const int per = (E + 63) / 64;
+        const int e0 = lane * per;
+        int s = 0, a = 0;
+        for (int e = e0; e < e0 + per && e < E; ++e) {
+            s += tot_s[e];
+            a += tot_s[e] > 0;
+        }
+        int ps = s, pa = a;   // inclusive scans across lanes
+        for (int d = 1; d < 64; d <<= 1) {
+            const int ys = __shfl_up(ps, d), ya = __shfl_up(pa, d);
+            if (lane >= d) {
+                ps += ys;
+                pa += ya;
+            }
+        }
+        int run = ps - s, arun = pa - a;
+        for (int e = e0; e < e0 + per && e < E; ++e) {
+            off_s[e] = run;
+            offsets[e] = run;
+            if (tot_s[e] > 0) {
+                if (active) active[1 + arun] = e;
+                ++arun;
+            }
+            run += tot_s[e];
+        }
+        if (lane == 63) {
+            off_s[E] = ps;
+            offsets[E] = ps;
+            if (active) active[0] = pa;
+        }
+    }
+    __syncthreads();
+
+    // scatter, stable within each expert: waves in pair order, lanes in pair order
+    for (int64_t pos = pb; pos < pe; pos += 64) {
+        const int64_t i = pos + lane;
+        int e = i < pe ? ids[i] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        if (i < pe && !valid) pair_to_sorted[i] = -1;   // dropped: out-of-range id
+        if (!valid) e = 0;
+        const uint64_t m = match_expert(e, valid, nbits);
+        int base = 0;
+        if (valid) base = off_s[e] + cnt[wave][e];
+        const int rank = __popcll(m & lt_mask);
+        if (valid) {
+            const int dst = base + rank;
+            sorted_pairs[dst] = (int32_t)i;
+            pair_to_sorted[i] = dst;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (__ffsll((unsigned long long)m) - 1) == lane) cnt[wave][e] = base - off_s[e] + __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ---- combine: fixed order, slots then the shared expert -------------------------------
+
+__global__ void __launch_bounds__(256)
+combine_kernel(const float *__restrict__ y, const float *__restrict__ wts,
+               const int32_t *__restrict__ p2s, int64_t T, int k, int64_t H, int has_shared,
+               uint16_t *__restrict__ out) {
+    const int64_t t = blockIdx.y;
+    const int64_t n4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n4 >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float p = wts[t * k + j];
+        const int64_t r = p2s[t * k + j];
+        if (r < 0) continue;
+        const float4 v = *reinterpret_cast<const float4 *>(y + r * H + n4);
+        acc.x += p * v.x;
+        acc.y += p * v.y;
+        acc.z += p * v.z;
+        acc.w += p * v.w;
+    }
+    if (has_shared) {
+        const float4 v = *reinterpret_cast<const float4 *>(y + (T * k + t) * H + n4);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint2 o;
+    o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2 *>(out + t * H + n4) = o;
+}
+
+// ---- host helpers ------------------------------------------------------------------------
+
+int check_desc(const qi4_moe_desc *d) {
+    if (!d) return QI4_ERR_NULL;
+    if (d->group_size != 128) return QI4_ERR_GROUP;
+    if (d->flags != 0 || (d->has_shared != 0 && d->has_shared != 1)) return QI4_ERR_UNSUPPORTED;
+    if (d->num_experts < 1 || d->num_experts > kMaxExperts) return QI4_ERR_SHAPE;
+    if (d->hidden < 128 || d->hidden % 128 || d->inter < 128 || d->inter % 128) return QI4_ERR_SHAPE;
+    if (d->hidden > (1 << 20) || d->inter > (1 << 20)) return QI4_ERR_SHAPE;
+    if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return QI4_ERR_SHAPE;
+    return QI4_OK;
+}
+
+inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+struct MoeWorkspace {
+    int64_t ids, wts, sorted, offsets, p2s, active, h, y, total;
+    MoeWorkspace(const qi4_moe_desc *d, int64_t T) {
+        const int64_t P = T * d->top_k;
+        const int64_t R = P + (d->has_shared ? T : 0);
+        int64_t o = 0;
+        ids = o;     o += align256(P * 4);
+        wts = o;     o += align256(P * 4);
+        sorted = o;  o += align256(P * 4);
+        offsets = o; o += align256((d->num_experts + 1) * 4);
+        p2s = o;     o += align256(P * 4);
+        active = o;  o += align256((d->num_experts + 1) * 4);
+        h = o;       o += align256(R * 2 * d->inter * 2);
+        y = o;       o += align256(R * d->hidden * 4);
+        total = o;
+    }
+};
+
+int bits_for(int64_t E) {
+    int b = 0;
+    while ((int64_t(1) << b) < E) ++b;
+    return b;
+}
+
+int launch_route(const float *logits, int64_t T, int E, int k, int32_t *ids, float *wts,
+                 hipStream_t st) {
+    const int64_t blocks = ceil_div(T, kRouteWaves);
+    if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
+    const int vpl = (E + 63) / 64;
+    const dim3 g((unsigned)blocks), b(kRouteWaves * 64);
+    if (vpl <= 1) route_kernel<1><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
+    else if (vpl <= 2) route_kernel<2><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
+    else if (vpl <= 4) route_kernel<4><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
+    else if (vpl <= 8) route_kernel<8><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
+    else route_kernel<16><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
+    return launch_status();
+}
+
+int launch_sort(const int32_t *ids, int64_t npairs, int E, int32_t *sorted, int32_t *offsets,
+                int32_t *p2s, int32_t *active, hipStream_t st) {
+    sort_kernel<<<1, kSortWaves * 64, 0, st>>>(ids, npairs, E, bits_for(E), sorted, offsets, p2s,
+                                               active);
+    return launch_status();
+}
+
+GemmArgs gate_up_args(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *sorted,
+                      const int32_t *offsets, const int32_t *active, const void *w_gu,
+                      const void *sh_gu, void *h) {
+    GemmArgs a = {};
+    a.w = static_cast<const uint8_t *>(w_gu);
+    a.w_stride = PackedLayout(2 * d->inter, d->hidden, QI4_PACK_GATEUP).bytes;
+    a.w_shared = static_cast<const uint8_t *>(sh_gu);
+    a.N = 2 * d->inter;
+    a.K = d->hidden;
+    a.flags = QI4_PACK_GATEUP;
+    a.a = x;
+    a.lda = d->hidden;
+    a.a_f32 = 0;
+    a.P = 1;
+    a.moe = 1;
+    a.T = T;
+    a.top_k = d->top_k;
+    a.sorted_pairs = sorted;
+    a.offsets = offsets;
+    a.active = active;
+    a.routed_slots = (int)(T * d->top_k < d->num_experts ? T * d->top_k : d->num_experts);
+    a.gather_tokens = 1;
+    a.out = h;
+    a.ldo = d->inter;
+    a.out_mode = OUT_SPLIT2;
+    a.epi = QI4_EPI_SILU_MUL;
+    a.n_out = d->inter;
+    return a;
+}
+
+GemmArgs down_args(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *offsets,
+                   const int32_t *active, const void *w_dn, const void *sh_dn, float *y) {
+    GemmArgs a = {};
+    a.w = static_cast<const uint8_t *>(w_dn);
+    a.w_stride = PackedLayout(d->hidden, d->inter, 0).bytes;
+    a.w_shared = static_cast<const uint8_t *>(sh_dn);
+    a.N = d->hidden;
+    a.K = d->inter;
+    a.flags = 0;
+    a.a = h;
+    a.lda = d->inter;
+    a.a_f32 = 0;
+    a.P = 2;
+    a.moe = 1;
+    a.T = T;
+    a.top_k = d->top_k;
+    a.offsets = offsets;
+    a.active = active;
+    a.routed_slots = (int)(T * d->top_k < d->num_experts ? T * d->top_k : d->num_experts);
+    a.gather_tokens = 0;
+    a.out = y;
+    a.ldo = d->hidden;
+    a.out_mode = OUT_F32;
+    a.epi = QI4_EPI_NONE;
+    a.n_out = d->hidden;
+    return a;
+}
+
+int launch_combine(const qi4_moe_desc *d, const float *y, const float *wts, const int32_t *p2s,
+                   int64_t T, void *out, hipStream_t st) {
+    if (T > 65535) return QI4_ERR_SHAPE;   // grid.y limit; check_T enforces it
+    const dim3 g((unsigned)ceil_div(d->hidden, 1024), (unsigned)T);
+    combine_kernel<<<g, 256, 0, st>>>(y, wts, p2s, T, d->top_k, d->hidden, d->has_shared,
+                                      static_cast<uint16_t *>(out));
+    return launch_status();
+}
+
+int check_T(int64_t T, const qi4_moe_desc *d) {
+    if (T < 0 || T > 65535) return QI4_ERR_SHAPE;
+    if (T * d->top_k > (int64_t(1) << 30)) return QI4_ERR_SHAPE;
+    return QI4_OK;
+}
+
+}  // namespace
+}  // namespace qi4
+
+using namespace qi4;
+
+extern "C" {
+
+int moe_route_topk(const float *logits, int64_t T, int64_t E, int32_t top_k, int32_t *topk_ids,
+                   float *topk_weights, void *stream) {
+    if (E < 1 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK || top_k > E) return QI4_ERR_SHAPE;
+    if (T < 0 || T > (int64_t(1) << 31)) return QI4_ERR_SHAPE;
+    if (T == 0) return QI4_OK;
+    if (!logits || !topk_ids || !topk_weights) return QI4_ERR_NULL;
+    if (overlaps(topk_ids, T * top_k * 4, logits, T * E * 4) ||
+        overlaps(topk_weights, T * top_k * 4, logits, T * E * 4) ||
+        overlaps(topk_ids, T * top_k * 4, topk_weights, T * top_k * 4))
+        return QI4_ERR_ALIAS;
+    int rc = check_device();
+    if (rc) return rc;
+    return launch_route(logits, T, (int)E, top_k, topk_ids, topk_weights, as_stream(stream));
+}
+
+int moe_sort_tokens(const int32_t *topk_ids, int64_t T, int32_t top_k, int64_t E,
+                    int32_t *sorted_pairs, int32_t *expert_offsets, int32_t *pair_to_sorted,
+                    int32_t *active, void *stream) {
+    if (E < 1 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK) return QI4_ERR_SHAPE;
+    if (T < 0 || T * top_k > (int64_t(1) << 30)) return QI4_ERR_SHAPE;
+    if (!topk_ids || !sorted_pairs || !expert_offsets || !pair_to_sorted) return QI4_ERR_NULL;
+    const int64_t P = T * top_k;
+    if (overlaps(sorted_pairs, P * 4, topk_ids, P * 4) ||
+        overlaps(pair_to_sorted, P * 4, topk_ids, P * 4) ||
+        overlaps(expert_offsets, (E + 1) * 4, topk_ids, P * 4) ||
+        overlaps(active, (E + 1) * 4, topk_ids, P * 4))
+        return QI4_ERR_ALIAS;
+    int rc = check_device();
+    if (rc) return rc;
+    return launch_sort(topk_ids, P, (int)E, sorted_pairs, expert_offsets, pair_to_sorted, active,
+                       as_stream(stream));
+}
+
+int64_t moe_ffn_int4_workspace_bytes(const qi4_moe_desc *d, int64_t T) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    return MoeWorkspace(d, T).total;
+}
+
+int moe_expert_gate_up(const qi4_moe_desc *d, const void *x, int64_t T,
+                       const int32_t *sorted_pairs, const int32_t *expert_offsets,
+                       const int32_t *active, const void *w_gate_up, const void *shared_gate_up,
+                       void *h, void *stream) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    if (T == 0) return QI4_OK;
+    if (!x || !sorted_pairs || !expert_offsets || !active || !w_gate_up || !h) return QI4_ERR_NULL;
+    if ((d->has_shared != 0) != (shared_gate_up != nullptr)) return QI4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(h, 4) ||
+        (shared_gate_up && !aligned(shared_gate_up, 16)))
+        return QI4_ERR_SHAPE;
+    if ((rc = check_device())) return rc;
+    GemmArgs a = gate_up_args(d, x, T, sorted_pairs, expert_offsets, active, w_gate_up,
+                              shared_gate_up, h);
+    return launch_qgemm(a, a.routed_slots + d->has_shared, T, as_stream(stream));
+}
+
+int moe_expert_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *expert_offsets,
+                    const int32_t *active, const void *w_down, const void *shared_down, float *y,
+                    void *stream) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    if (T == 0) return QI4_OK;
+    if (!h || !expert_offsets || !active || !w_down || !y) return QI4_ERR_NULL;
+    if ((d->has_shared != 0) != (shared_down != nullptr)) return QI4_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(w_down, 16) || !aligned(y, 4) ||
+        (shared_down && !aligned(shared_down, 16)))
+        return QI4_ERR_SHAPE;
+    if ((rc = check_device())) return rc;
+    GemmArgs a = down_args(d, h, T, expert_offsets, active, w_down, shared_down, y);
+    return launch_qgemm(a, a.routed_slots + d->has_shared, T, as_stream(stream));
+}
+
+int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights,
+                const int32_t *pair_to_sorted, int64_t T, void *out, void *stream) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    if (T == 0) return QI4_OK;
+    if (!y || !topk_weights || !pair_to_sorted || !out) return QI4_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(out, 8)) return QI4_ERR_SHAPE;
+    const int64_t R = T * d->top_k + (d->has_shared ? T : 0);
+    if (overlaps(out, T * d->hidden * 2, y, R * d->hidden * 4)) return QI4_ERR_ALIAS;
+    if ((rc = check_device())) return rc;
+    return launch_combine(d, y, topk_weights, pair_to_sorted, T, out, as_stream(stream));
+}
+
+int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *router_logits,
+                 int32_t *topk_ids, float *topk_weights, const void *w_gate_up, const void *w_down,
+                 const void *shared_gate_up, const void *shared_down, void *out, void *workspace,
+                 int64_t ws_bytes, void *stream) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    if (T == 0) return QI4_OK;
+    if (!x || !w_gate_up || !w_down || !out || !workspace) return QI4_ERR_NULL;
+    if (!router_logits && (!topk_ids || !topk_weights)) return QI4_ERR_NULL;
+    if ((d->has_shared != 0) != (shared_gate_up != nullptr) ||
+        (d->has_shared != 0) != (shared_down != nullptr))
+        return QI4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(out, 8) ||
+        !aligned(workspace, 256) || (shared_gate_up && !aligned(shared_gate_up, 16)) ||
+        (shared_down && !aligned(shared_down, 16)))
+        return QI4_ERR_SHAPE;
+    const MoeWorkspace L(d, T);
+    if (ws_bytes < L.total) return QI4_ERR_WORKSPACE;
+    const int64_t H = d->hidden;
+    if (overlaps(out, T * H * 2, x, T * H * 2) || overlaps(out, T * H * 2, workspace, ws_bytes) ||
+        overlaps(workspace, ws_bytes, x, T * H * 2))
+        return QI4_ERR_ALIAS;
+    if ((rc = check_device())) return rc;
+
+    hipStream_t st = as_stream(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int E = (int)d->num_experts, k = d->top_k;
+    int32_t *ids = topk_ids ? topk_ids : reinterpret_cast<int32_t *>(ws + L.ids);
+    float *wts = topk_weights ? topk_weights : reinterpret_cast<float *>(ws + L.wts);
+    int32_t *sorted = reinterpret_cast<int32_t *>(ws + L.sorted);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    int32_t *p2s = reinterpret_cast<int32_t *>(ws + L.p2s);
+    int32_t *active = reinterpret_cast<int32_t *>(ws + L.active);
+    void *h = ws + L.h;
+    float *y = reinterpret_cast<float *>(ws + L.y);
+
+    if (router_logits && (rc = launch_route(router_logits, T, E, k, ids, wts, st))) return rc;
+    if ((rc = launch_sort(ids, T * k, E, sorted, offsets, p2s, active, st))) return rc;
+    GemmArgs gu = gate_up_args(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h);
+    if ((rc = launch_qgemm(gu, gu.routed_slots + d->has_shared, T, st))) return rc;
+    GemmArgs dn = down_args(d, h, T, offsets, active, w_down, shared_down, y);
+    if ((rc = launch_qgemm(dn, dn.routed_slots + d->has_shared, T, st))) return rc;
+    return launch_combine(d, y, wts, p2s, T, out, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+/*
+ * qi4.h -- C ABI of libqi4: int4 group-quantized (groups of 128 along K, one
+ * binary16 scale and one 4-bit zero point per group) linear layer and routed
+ * mixture-of-experts FFN for AMD MI355X (gfx950).
+ *
+ * What is computed follows these pages:
+ *  - "FastLLM: zero-dependency CPU inference framework ..." (pgsm.cn),
+ *    section 3.1 "4-bit quantization and weight reordering": weights are 4-bit
+ *    codes in groups of 128 that share one scale and one zero point, stored
+ *    group by group so the product reads contiguous memory, and the product
+ *    runs "read 4-bit weight -> dequantize -> multiply" with no extra pass;
+ *    section 2.3: the matrix multiply is a core operator below the model layer.
+ *  - fastllm README (gittoolsai.com), "other parameters": --moe_experts sets
+ *    how many routed experts each token uses; --cuda_se runs the shared expert
+ *    on the GPU.  "Inference precision": int4g is the grouped int4 type.
+ *  - FastLLM notes (wmrh.cn), part 1: a MoE layer holds many experts but each
+ *    token activates only a few of them.
+ * Dequantization is w = scale * (q - zero).  Expert FFN is
+ * h = SiLU(x.Wg^T) * (x.Wu^T), y = h.Wd^T; SiLU(v) = v / (1 + e^-v).
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless the comment says "host".
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Calls only enqueue work on `stream` and return; they never synchronize,
+ *    never allocate and never free.  The caller owns every buffer.
+ *  - Errors are return codes (QI4_OK == 0, negative on error).  All argument
+ *    checks run on the host before anything is enqueued: on an error return
+ *    nothing was launched and no output was touched.  A failed launch returns
+ *    QI4_ERR_HIP.  No C++ exception crosses this ABI.
+ *  - Outputs must not overlap inputs (QI4_ERR_ALIAS where checked).
+ *  - Only group_size == 128 is built (QI4_ERR_GROUP otherwise); K must be a
+ *    multiple of 128 (QI4_ERR_SHAPE).  The device must be gfx950
+ *    (QI4_ERR_UNSUPPORTED otherwise).
+ *  - Calls are reentrant; the only global state is a cached per-device
+ *    architecture check.
+ *
+ * Canonical (interchange) format of a quantized matrix W [N][K] (out x in):
+ *    qweight uint8  [N][K/2]    code of (n, k) in byte k/2, even k in the low nibble
+ *    scales  uint16 [N][K/128]  IEEE binary16 bit patterns
+ *    zeros   uint8  [N][K/128]  zero point, 0..15
+ * A [gate; up] matrix of an FFN has N = 2*I rows: rows [0, I) gate, [I, 2I) up.
+ *
+ * Packed (device) format, produced by qi4_pack: rows are cut into 16-row tiles
+ * (with QI4_PACK_GATEUP, tile 2m holds gate rows 16m.. and tile 2m+1 the up rows
+ * with the same index, so a tile pair yields 16 outputs of SiLU(gate)*up).
+ * Let nt = number of tiles and G = K/128.  Three regions follow each other:
+ *    codes  nt*G*1024 bytes  [tile][group][lane 0..63][16 bytes]
+ *    scales nt*G*32 bytes    [tile][group][row 0..15] binary16
+ *    zeros  nt*G*8 bytes     [tile][group][8 bytes] row r in nibble r&1 of byte r/2
+ * Lane 16*j + r of a tile/group block holds row r's codes for k in
+ * 128*g + 32*s + 8*j + [0, 8) in its dword s (s = 0..3), so one 16-byte load per
+ * lane brings a wave exactly one group of 16 rows.  Missing rows (N not a multiple
+ * of 16) are packed as zeros.  The layout is private to this library: only
+ * qi4_pack writes it and only the calls below read it.
+ */
+#ifndef QI4_H
+#define QI4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QI4_ABI_VERSION 1
+
+enum {
+    QI4_OK = 0,
+    QI4_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    QI4_ERR_SHAPE = -2,       /* a size is out of range or K % 128 != 0               */
+    QI4_ERR_DTYPE = -3,       /* unknown dtype or epilogue code                       */
+    QI4_ERR_GROUP = -4,       /* group_size != 128                                    */
+    QI4_ERR_WORKSPACE = -5,   /* workspace too small                                  */
+    QI4_ERR_ALIAS = -6,       /* an output overlaps an input                          */
+    QI4_ERR_UNSUPPORTED = -7, /* device is not gfx950, or flags/epilogue combination */
+    QI4_ERR_HIP = -8          /* a HIP runtime call or launch failed                  */
+};
+
+enum { QI4_F32 = 0, QI4_BF16 = 1 };          /* activation / output element types */
+enum { QI4_EPI_NONE = 0, QI4_EPI_SILU_MUL = 1 };
+enum { QI4_PACK_GATEUP = 1 };                 /* pack flag: pair gate/up tiles      */
+
+/* ABI version of the loaded library (QI4_ABI_VERSION). */
+int qi4_abi_version(void);
+
+/* Static, host-side, human-readable name of a status code. Never NULL. */
+const char *qi4_status_string(int status);
+
+/* Bytes of the packed format for an N x K matrix; negative status on bad
+   arguments (N < 1, K < 128, K % 128, group_size != 128, unknown flags, or
+   QI4_PACK_GATEUP with odd N). */
+int64_t qi4_packed_bytes(int64_t N, int64_t K, int group_size, int flags);
+
+/* Canonical -> packed (the offline reorder: each group of 16 rows becomes one
+   contiguous kilobyte per wave load).  Exact: qi4_unpack inverts it bit for
+   bit.  `packed` must hold qi4_packed_bytes(N, K, 128, flags) bytes. */
+int qi4_pack(const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
+             int64_t N, int64_t K, int group_size, int flags, void *packed, void *stream);
+
+/* Packed -> canonical; the exact inverse of qi4_pack (zero values beyond 15
+   cannot occur). */
+int qi4_unpack(const void *packed, int64_t N, int64_t K, int group_size, int flags,
+               uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream);
+
+/* Dequantize a packed matrix to float32 w [N][K] in canonical row order:
+   w = float(scale) * (q - zero).  Exact (the product of a binary16 scale and an
+   integer in [-15, 15] is representable in binary32). */
+int qi4_dequant_f32(const void *packed, int64_t N, int64_t K, int group_size, int flags,
+                    float *w, void *stream);
+
+/* The linear layer: y[t][n'] = epilogue( sum_k x[t][k] * dequant(W)[n][k] ).
+ *   x        [T][K] of x_dtype (QI4_BF16 or QI4_F32), row-major, contiguous
+ *   packed_w packed N x K matrix (flags as given to qi4_pack)
+ *   y        [T][N'] of y_dtype (QI4_BF16 or QI4_F32);
+ *            N' = N for QI4_EPI_NONE, N/2 for QI4_EPI_SILU_MUL
+ *   epilogue QI4_EPI_SILU_MUL needs flags == QI4_PACK_GATEUP and gives
+ *            y[t][i] = SiLU(g) * u with g, u the rows i and N/2 + i of [gate; up].
+ * Accumulation is float32; the result is rounded once to y_dtype.  T == 0 is a
+ * valid no-op.  float32 activations are used exactly (split into bf16 terms). */
+int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,
+                      const void *packed_w, int64_t N, int flags,
+                      void *y, int y_dtype, int epilogue, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Routed mixture-of-experts FFN (decode and prefill).
+ * Routed expert e uses packed gate/up block w_gate_up + e * qi4_packed_bytes(2I, H,
+ * 128, QI4_PACK_GATEUP) and packed down block w_down + e * qi4_packed_bytes(H, I,
+ * 128, 0).  The shared expert (has_shared != 0) has the same two shapes and is
+ * added with weight 1.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int64_t num_experts;   /* E, routed experts (1..1024)                      */
+    int64_t hidden;        /* H, multiple of 128                                */
+    int64_t inter;         /* I, expert intermediate size, multiple of 128      */
+    int32_t top_k;         /* routed experts per token (1..min(E, 32))           */
+    int32_t group_size;    /* must be 128                                       */
+    int32_t has_shared;    /* 0 or 1                                            */
+    int32_t flags;         /* must be 0                                         */
+} qi4_moe_desc;            /* host struct                                       */
+
+/* Router: for each token the top_k largest logits in descending order (ties to
+ * the lower expert index) and softmax weights over those top_k only.
+ *   logits [T][E] float32;  topk_ids [T][top_k] int32;  topk_weights [T][top_k] float32
+ * Logits must not be NaN. */
+int moe_route_topk(const float *logits, int64_t T, int64_t E, int32_t top_k,
+                   int32_t *topk_ids, float *topk_weights, void *stream);
+
+/* Token-by-expert permutation (stable counting sort of the T*top_k pairs
+ * p = t*top_k + j by expert):
+ *   sorted_pairs   [T*top_k]  pairs grouped by expert ascending, tokens ascending
+ *   expert_offsets [E+1]      segment starts; expert_offsets[E] = T*top_k
+ *   pair_to_sorted [T*top_k]  inverse permutation
+ *   active         [E+1] or NULL: active[0] = number of experts with a nonempty
+ *                  segment, active[1..] those experts ascending
+ * Ids must lie in [0, E); a pair with an id outside it is left out of the
+ * permutation (pair_to_sorted = -1, and expert_offsets[E] counts only the pairs
+ * kept; moe_combine skips it).  Deterministic. */
+int moe_sort_tokens(const int32_t *topk_ids, int64_t T, int32_t top_k, int64_t E,
+                    int32_t *sorted_pairs, int32_t *expert_offsets, int32_t *pair_to_sorted,
+                    int32_t *active, void *stream);
+
+/* Bytes of workspace moe_ffn_int4 needs for T tokens (negative status on bad
+   descriptor). */
+int64_t moe_ffn_int4_workspace_bytes(const qi4_moe_desc *d, int64_t T);
+
+/* Stage calls.  moe_ffn_int4 below is route -> sort -> gate_up -> down -> combine
+ * with exactly these kernels; they are exported for callers that route
+ * elsewhere or time one stage.  Let P = T*top_k routed pairs and R = P + T*has_shared.
+ * Row s < P of the intermediates belongs to sorted position s (see
+ * moe_sort_tokens); row P + t belongs to token t's shared expert.
+ *   h  [R][2][I] bf16 bits: SiLU(gate)*up as an unevaluated sum hi + lo of two
+ *      bf16 numbers (hi = bf16(h), lo = bf16(h - hi)), about 16 significant bits
+ *   y  [R][H] float32: each expert's down-projection output, before weighting
+ * `active` is the array moe_sort_tokens fills. */
+int moe_expert_gate_up(const qi4_moe_desc *d, const void *x, int64_t T,
+                       const int32_t *sorted_pairs, const int32_t *expert_offsets,
+                       const int32_t *active, const void *w_gate_up,
+                       const void *shared_gate_up, void *h, void *stream);
+int moe_expert_down(const qi4_moe_desc *d, const void *h, int64_t T,
+                    const int32_t *expert_offsets, const int32_t *active,
+                    const void *w_down, const void *shared_down, float *y, void *stream);
+/* out[t] = sum_j topk_weights[t][j] * y[pair_to_sorted[t*top_k+j]] (+ y[P+t]),
+   summed in that order in float32, rounded once to bf16. */
+int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights,
+                const int32_t *pair_to_sorted, int64_t T, void *out, void *stream);
+
+/* out[t] = sum_j p[t][j] * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t).
+ *   x    [T][H] bf16 bits;  out [T][H] bf16 bits
+ *   router_logits [T][E] float32, or NULL: then topk_ids/topk_weights
+ *                 ([T][top_k] int32 / float32) supply the routing.  When the
+ *                 logits are given, topk_ids/topk_weights may be NULL, or receive
+ *                 the routing the call computed.
+ *   shared_gate_up / shared_down: NULL iff has_shared == 0.
+ *   workspace: moe_ffn_int4_workspace_bytes(d, T) bytes, 256-byte aligned.
+ * The combine runs in a fixed order (slots 0..top_k-1, then the shared expert),
+ * so results are deterministic. */
+int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T,
+                 const float *router_logits, int32_t *topk_ids, float *topk_weights,
+                 const void *w_gate_up, const void *w_down,
+                 const void *shared_gate_up, const void *shared_down,
+                 void *out, void *workspace, int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI4_H */

@@ -1,0 +1,102 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qi4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)
+    kw = {"if", "sizeof", "defined"}
+    return [n for n in dict.fromkeys(names) if n not in kw]
+
+
+@pytest.fixture(scope="module")
+def q():
+    import ffn_int4_g128_amd as q
+    if not os.path.exists(q.LIB_PATH):
+        q.build()
+    q.lib()
+    return q
+
+
+def test_header_and_binding_agree(q):
+    assert _declared() == q.EXPORTED
+
+
+def test_every_declared_symbol_is_exported(q):
+    L = ctypes.CDLL(q.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(q):
+    L = q.lib()
+    assert L.qi4_abi_version() == 1
+    for s in range(-8, 1):
+        assert L.qi4_status_string(s)
+    assert L.qi4_status_string(-99) == b"unknown status"
+
+
+def test_packed_bytes(q):
+    L = q.lib()
+    # 16-row tiles x 128-wide groups: 1024 B codes + 32 B scales + 8 B zeros each
+    assert L.qi4_packed_bytes(16, 128, 128, 0) == 1280  # 1064 rounded up to 256
+    assert L.qi4_packed_bytes(4096, 4096, 128, 0) == 256 * 32 * 1064
+    assert L.qi4_packed_bytes(17, 256, 128, 0) == ((2 * 2 * 1064 + 255) // 256) * 256
+    # gate/up: each half padded to whole tiles
+    assert L.qi4_packed_bytes(48, 128, 128, 1) == ((4 * 1064 + 255) // 256) * 256
+    assert L.qi4_packed_bytes(16, 100, 128, 0) == -2
+    assert L.qi4_packed_bytes(16, 128, 64, 0) == -4
+    assert L.qi4_packed_bytes(17, 128, 128, 1) == -2
+    assert L.qi4_packed_bytes(0, 128, 128, 0) == -2
+    assert L.qi4_packed_bytes(16, 128, 128, 4) == -7
+
+
+def test_argument_errors_return_before_any_launch(q):
+    L = q.lib()
+    p = ctypes.c_void_p(0x1000)
+    # K not a multiple of 128, group size, dtype, epilogue/flags combination, NULL, alias
+    assert L.qlinear_int4_g128(p, 1, 1, 100, p, 16, 0, p, 1, 0, None) == -2
+    assert L.qlinear_int4_g128(p, 7, 1, 128, p, 16, 0, p, 1, 0, None) == -3
+    assert L.qlinear_int4_g128(p, 1, 1, 128, p, 16, 0, p, 9, 0, None) == -3
+    assert L.qlinear_int4_g128(p, 1, 1, 128, p, 16, 0, p, 1, 1, None) == -7
+    assert L.qlinear_int4_g128(None, 1, 1, 128, p, 16, 0, p, 1, 0, None) == -1
+    assert L.qlinear_int4_g128(p, 1, -1, 128, p, 16, 0, p, 1, 0, None) == -2
+    assert L.qlinear_int4_g128(p, 1, 0, 128, p, 16, 0, p, 1, 0, None) == 0   # T == 0: no-op
+    x = ctypes.c_void_p(0x100000)
+    assert L.qlinear_int4_g128(x, 1, 4, 128, ctypes.c_void_p(0x200000), 16, 0,
+                               ctypes.c_void_p(0x100000 + 64), 1, 0, None) == -6
+    assert L.qlinear_int4_g128(ctypes.c_void_p(0x1004), 1, 1, 128, p, 16, 0, p, 1, 0, None) == -2
+    assert L.qi4_pack(p, p, p, 16, 128, 64, 0, p, None) == -4
+    assert L.qi4_pack(None, p, p, 16, 128, 128, 0, p, None) == -1
+    assert L.qi4_dequant_f32(p, 16, 96, 128, 0, p, None) == -2
+    assert L.moe_route_topk(p, 4, 8, 9, p, p, None) == -2
+    assert L.moe_route_topk(p, 4, 2000, 8, p, p, None) == -2
+    assert L.moe_sort_tokens(None, 4, 8, 256, p, p, p, None, None) == -1
+
+
+def test_moe_descriptor_errors(q):
+    L = q.lib()
+    D = q._MoeDesc
+    ok = D(256, 7168, 2048, 8, 128, 1, 0)
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(ok), 32) > 0
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 64, 1, 0)), 1) == -4
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7000, 2048, 8, 128, 1, 0)), 1) == -2
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(4, 7168, 2048, 8, 128, 1, 0)), 1) == -2
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 2, 0)), 1) == -7
+    p = ctypes.c_void_p(0x1000)
+    small = ctypes.c_void_p(0x10000000)
+    # workspace too small
+    assert L.moe_ffn_int4(ctypes.byref(ok), ctypes.c_void_p(0x20000000), 4, p, None, None, p, p,
+                          p, p, ctypes.c_void_p(0x30000000), small, 256, None) == -5
+    # shared pointers must match has_shared
+    assert L.moe_ffn_int4(ctypes.byref(ok), p, 4, p, None, None, p, p, None, p, p, small,
+                          1 << 40, None) == -1
