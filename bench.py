@@ -1,0 +1,266 @@
+"""Benchmark: int4-g128 MoE FFN decode on one MI355X.
+
+Workload (one "step" = one forward of one MoE layer over a decode batch):
+DeepSeek-V3-shaped layer, hidden 7168, expert intermediate 2048, 256 routed
+experts + 1 shared, top-8 routing with softmax over the selected logits, all
+weights int4 with groups of 128 (one binary16 scale and one 4-bit zero per
+group), bf16 activations, fp32 accumulation, bf16 output.  Two independent
+layers are alternated step by step (11.8 GB of packed weights) so each step
+reads its experts from HBM rather than from the 256 MB last-level cache, and
+every step routes a different batch of tokens.  Inputs are seeded synthetic
+data already resident in HBM when timing starts.
+
+The step runs the five stages through the C ABI (route, sort, grouped
+gate/up + SiLU, grouped down, combine); HIP events on the launch stream time
+each grouped GEMM inside the timed region.  The JSON line reports tokens/s of
+the main batch size, the roofline of the dominant kernel (grouped gate/up),
+and the oracle's CPU time on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, decimal GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=32, help="tokens of the main decode batch")
+    ap.add_argument("--sweep", type=str, default="1,8", help="other decode batch sizes to report")
+    ap.add_argument("--layers", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(c, layer, q, torch):
+    import numpy as np
+    import workloads
+    ex = workloads.moe_experts(c["seed"], layer, c["E"], c["H"], c["I"], *c["scale"])
+    sh = workloads.moe_shared(c["seed"], layer, c["H"], c["I"], *c["scale"])
+    mw = q.pack_moe(ex, sh, c["E"], c["H"], c["I"], device="cuda")
+    torch.cuda.synchronize()
+    del ex, sh
+    return mw
+
+
+class Stepper:
+    """Runs the five stages of one MoE forward through the C ABI, with events
+    around the two grouped GEMMs."""
+
+    def __init__(self, q, torch, layers, T, top_k, n_batches, c):
+        import numpy as np
+        import workloads
+        self.q, self.torch, self.layers, self.T, self.k = q, torch, layers, T, top_k
+        self.c = c
+        E, H = c["E"], c["H"]
+        self.x = [q_bf16(torch, workloads.activations(c["seed"], 500 + 10 * b + T, T, H, "bf16"))
+                  for b in range(n_batches)]
+        self.logits = [torch.from_numpy(workloads.logits_normal(c["seed"], 600 + 10 * b + T, T, E)).cuda()
+                       for b in range(n_batches)]
+        dev = "cuda"
+        P = T * top_k
+        R = P + T
+        self.ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        self.wts = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        self.sp = torch.empty(P, dtype=torch.int32, device=dev)
+        self.off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.inv = torch.empty(P, dtype=torch.int32, device=dev)
+        self.act = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.h = torch.empty((R, 2, c["I"]), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((R, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.n_batches = n_batches
+
+    def step(self, i, ev=None):
+        q, torch = self.q, self.torch
+        mw = self.layers[i % len(self.layers)]
+        b = (i // len(self.layers)) % self.n_batches
+        L = q.lib()
+        d = mw.desc(self.k)
+        import ctypes
+        dref = ctypes.byref(d)
+        st = q._stream()
+        P = q._ptr
+        T, E = self.T, self.c["E"]
+        q._check(L.moe_route_topk(P(self.logits[b]), T, E, self.k, P(self.ids), P(self.wts), st),
+                 "route")
+        q._check(L.moe_sort_tokens(P(self.ids), T, self.k, E, P(self.sp), P(self.off), P(self.inv),
+                                   P(self.act), st), "sort")
+        if ev is not None:
+            ev[0].record()
+        q._check(L.moe_expert_gate_up(dref, P(self.x[b]), T, P(self.sp), P(self.off), P(self.act),
+                                      P(mw.w_gate_up), P(mw.shared_gate_up), P(self.h), st),
+                 "gate_up")
+        if ev is not None:
+            ev[1].record()
+        q._check(L.moe_expert_down(dref, P(self.h), T, P(self.off), P(self.act), P(mw.w_down),
+                                   P(mw.shared_down), P(self.y), st), "down")
+        if ev is not None:
+            ev[2].record()
+        q._check(L.moe_combine(dref, P(self.y), P(self.wts), P(self.inv), T, P(self.out), st),
+                 "combine")
+
+    def touched(self, i):
+        """Routed experts touched by step i (read back outside any timed region)."""
+        self.step(i)
+        self.torch.cuda.synchronize()
+        return int(self.act[0].item())
+
+
+def q_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
+    import workloads
+    k = c["top_k"]
+    s = Stepper(q, torch, layers, T, k, n_batches, c)
+    period = len(layers) * n_batches
+    touched = [s.touched(i) for i in range(period)]
+    for i in range(warmup):
+        s.step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s.step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    H, I = c["H"], c["I"]
+    per_w = workloads.packed_weight_bytes(1)
+    gu_w, dn_w = 2 * I * H, H * I
+    # algorithmic bytes per step: weights of the touched experts + the shared one,
+    # activations in, outputs out, router logits in
+    gu_bytes, dn_bytes, step_bytes = [], [], []
+    for i in range(steps):
+        n_e = touched[i % period] + 1
+        gu_bytes.append(n_e * gu_w * per_w + T * H * 2 + T * (k + 1) * 2 * I * 2)
+        dn_bytes.append(n_e * dn_w * per_w + T * (k + 1) * 2 * I * 2 + T * (k + 1) * H * 4)
+        step_bytes.append(n_e * (gu_w + dn_w) * per_w + 2 * T * H * 2 + T * c["E"] * 4)
+    mean = lambda v: sum(v) / len(v)
+    ms_step = wall * 1e3 / steps
+    return {
+        "T": T, "ms_per_step": ms_step, "tokens_per_s": T * steps / wall,
+        "experts_touched_mean": mean([touched[i % period] for i in range(steps)]) + 1,
+        "step_GBps": mean(step_bytes) / (ms_step * 1e-3) / 1e9,
+        "gate_up_us": mean(gu_ms) * 1e3, "down_us": mean(dn_ms) * 1e3,
+        "gate_up_GBps": mean(gu_bytes) / (mean(gu_ms) * 1e-3) / 1e9,
+        "down_GBps": mean(dn_bytes) / (mean(dn_ms) * 1e-3) / 1e9,
+        "gate_up_bytes": mean(gu_bytes),
+    }
+
+
+def cpu_baseline(c, T, target_s):
+    """The oracle (fp64 C, OpenMP over output rows) on a bounded sample of the
+    same workload: n tokens of layer 0, n chosen for about target_s seconds."""
+    import numpy as np
+    import oracle
+    import workloads
+    oracle.lib()
+    ex = workloads.moe_experts(c["seed"], 0, c["E"], c["H"], c["I"], *c["scale"])
+    sh = workloads.moe_shared(c["seed"], 0, c["H"], c["I"], *c["scale"])
+    Tmax = 256
+    x = workloads.activations(c["seed"], 700, Tmax, c["H"], "bf16")
+    logits = workloads.logits_normal(c["seed"], 701, Tmax, c["E"])
+    ids, p = oracle.topk_softmax(logits, c["top_k"])
+    threads = oracle.default_threads()
+    x64 = oracle.widen(x, "bf16")
+    t0 = time.perf_counter()
+    oracle.moe(x64[:1], ids[:1], p[:1], ex, sh, c["H"], c["I"], c["E"], threads=threads)
+    one = time.perf_counter() - t0
+    n = int(max(1, min(Tmax, target_s // max(one, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.moe(x64[:n], ids[:n], p[:n], ex, sh, c["H"], c["I"], c["E"], threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} tokens through the full layer 0 (routing, 8 experts + shared each), "
+                      "one at a time as in decode",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
+              "multi-GPU path; see DESIGN.md for how the layer would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import ffn_int4_g128_amd as q
+    import workloads
+    c = dict(workloads.MOE_DECODE)
+    log(f"building {args.layers} layers of packed weights ...")
+    t0 = time.perf_counter()
+    layers = [build_layer(c, l, q, torch) for l in range(args.layers)]
+    log(f"  done in {time.perf_counter() - t0:.1f} s")
+
+    main_r = run_batch(q, torch, layers, c, args.T, args.steps, args.warmup)
+    log(f"T={args.T}: {json.dumps(main_r)}")
+    sweep = []
+    for t in [int(v) for v in args.sweep.split(",") if v.strip()]:
+        if t == args.T:
+            continue
+        r = run_batch(q, torch, layers, c, t, max(10, args.steps), args.warmup)
+        log(f"T={t}: {json.dumps(r)}")
+        sweep.append(r)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del layers
+        torch.cuda.empty_cache()
+        log("timing the oracle on a CPU sample ...")
+        cpu = cpu_baseline(c, args.T, args.cpu_seconds)
+        log(f"  {json.dumps(cpu)}")
+
+    gu_gbps = main_r["gate_up_GBps"]
+    out = {
+        "metric": "int4-g128 MoE FFN decode tokens/s (DeepSeek-V3-shaped layer)",
+        "value": main_r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded int4 weights, N(0,1) bf16 activations and router logits)",
+        "config": {"workload": "moe_ffn_decode_deepseekv3_shape", "T": args.T, "hidden": c["H"],
+                   "inter": c["I"], "experts": c["E"], "shared_experts": 1, "top_k": c["top_k"],
+                   "group": 128, "layers_alternated": args.layers},
+        "roofline": {"bound": "hbm", "kernel": "moe grouped gate/up + SiLU (qgemm_kernel)",
+                     "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gu_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "launch_us": main_r["gate_up_us"], "bytes_per_launch": main_r["gate_up_bytes"]},
+        "step_GBps": main_r["step_GBps"],
+        "experts_touched_mean": main_r["experts_touched_mean"],
+        "down_GBps": main_r["down_GBps"],
+        "sweep": [{k: r[k] for k in ("T", "tokens_per_s", "ms_per_step", "step_GBps", "gate_up_GBps",
+                                     "down_GBps", "experts_touched_mean")} for r in sweep],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

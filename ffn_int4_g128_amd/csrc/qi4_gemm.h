@@ -13,7 +13,7 @@ enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_SPLIT2 = 2 };
 // of A that use it).  blockIdx.y picks the problem, blockIdx.x a block of tiles.
 struct GemmArgs {
     // weights (packed)
-    const uint8_t *w;          // dense matrix, or routed expert 0
+    const uint8_t *w;          // dense matrix, or routed expert 0 (each matrix < 2^31 bytes)
     int64_t w_stride;          // bytes between routed experts
     const uint8_t *w_shared;   // shared expert (moe) or nullptr
     int64_t N, K;              // rows and reduction length of each matrix
@@ -21,6 +21,7 @@ struct GemmArgs {
     // activations
     const void *a;             // bf16 bits, or float32 when a_f32
     int64_t lda;               // elements per A source row
+    int64_t a_bytes;           // bytes of the whole A buffer (< 2^31)
     int a_f32;                 // float32 rows, split into 4 bf16 terms in registers
     int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
     // problems

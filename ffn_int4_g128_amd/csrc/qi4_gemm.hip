@@ -39,23 +39,43 @@ __device__ inline uint32_t split_part(float v, int part) {
     return part == 0 ? hi : part == 1 ? mid : part == 2 ? lo : 0u;
 }
 
-template <bool AF32>
-__device__ inline uint4 load_a_frag(const void *row, int64_t elem, int part) {
-    if constexpr (!AF32) {
-        return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(row) + elem);
-    } else {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(row) + elem);
-        const float4 u = p[0], v = p[1];
-        uint4 r;
-        r.x = split_part(u.x, part) | (split_part(u.y, part) << 16);
-        r.y = split_part(u.z, part) | (split_part(u.w, part) << 16);
-        r.z = split_part(v.x, part) | (split_part(v.y, part) << 16);
-        r.w = split_part(v.z, part) | (split_part(v.w, part) << 16);
-        return r;
-    }
+// bf16 fragment of part `part` of eight float32 activations.
+__device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
+    uint4 r;
+    r.x = split_part(__uint_as_float(u.x), part) | (split_part(__uint_as_float(u.y), part) << 16);
+    r.y = split_part(__uint_as_float(u.z), part) | (split_part(__uint_as_float(u.w), part) << 16);
+    r.z = split_part(__uint_as_float(v.x), part) | (split_part(__uint_as_float(v.y), part) << 16);
+    r.w = split_part(__uint_as_float(v.z), part) | (split_part(__uint_as_float(v.w), part) << 16);
+    return r;
 }
 
+// Loads of one 128-wide group: the codes, scale and zero byte of NB tiles and
+// the raw activation fragments of MT M tiles (bf16: one 16-byte load per k
+// step; float32: two).
 template <int NB, int MT, bool AF32>
+struct Stage {
+    uint4 cw[NB];
+    uint32_t sc[NB];
+    uint32_t zb[NB];
+    uint4 af[MT][4][AF32 ? 2 : 1];
+};
+
+// Buffer resource over [base, base + bytes): loads at offsets past the end
+// return zero, which lets every load of the K loop run unconditionally.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+// Out-of-range offsets.  Valid lane offsets stay below 2^31 (every buffer is
+// smaller than 2 GiB), so kOob (lane part) and kOobS (wave part) reach past
+// every resource and their sum, at most 2^32 - 1, never wraps around.
+constexpr uint32_t kOob = 0x80000000u;
+constexpr uint32_t kOobS = 0x7FFFFFFFu;
+
+__device__ inline uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <int NB, int MT, bool AF32, int S, int EPI>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 qgemm_kernel(const GemmArgs args) {
     __shared__ float red[kRedSlots * 256];
@@ -96,37 +116,31 @@ qgemm_kernel(const GemmArgs args) {
     const PackedLayout L(args.N, args.K, args.flags);
     const int64_t nt = L.nt, G = L.G;
     const int64_t tile0 = (int64_t)blockIdx.x * NB;
-    const uint4 *codes = reinterpret_cast<const uint4 *>(w);
-    const uint16_t *scl = reinterpret_cast<const uint16_t *>(w + L.scales_off);
-    const uint8_t *zrs = w + L.zeros_off;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)L.bytes);
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(args.a, (uint32_t)args.a_bytes);
+
+    // per-tile byte offsets of group 0 (or an out-of-range offset for padding tiles)
+    uint32_t cbase[NB], sbase[NB], zbase[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t tile = tile0 + nb;
+        const bool ok = tile < nt;
+        cbase[nb] = ok ? (uint32_t)((tile * G * 64 + lane) * 16) : kOob;
+        sbase[nb] = ok ? (uint32_t)(L.scales_off + (tile * G * 16 + r16) * 2) : kOob;
+        zbase[nb] = ok ? (uint32_t)(L.zeros_off + tile * G * 8 + (r16 >> 1)) : kOob;
+    }
+    const int zshift = 4 * (r16 & 1);
 
     const int gb = (int)((G * wave) / W), ge = (int)((G * (wave + 1)) / W);
     const int P = args.P;
     const int spt = 16 / P;                 // slots per M tile
     const int64_t chunk = (int64_t)MT * spt;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    constexpr int ES = AF32 ? 4 : 2;        // bytes per activation element
 
     for (int64_t c0 = 0; c0 < n; c0 += chunk) {
-        // ---- A rows of this lane (operand row r16 of each M tile)
-        const void *arow[MT];
-        bool avalid[MT];
-        int apart[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int64_t slot = c0 + (int64_t)m * spt + r16 / P;
-            const int part = r16 % P;
-            const bool ok = (r16 < spt * P) && slot < n;
-            avalid[m] = ok;
-            apart[m] = part;
-            arow[m] = nullptr;
-            if (ok) {
-                const int64_t src = gather ? (int64_t)(gather[row0 + slot] / args.top_k) : src0 + slot;
-                if constexpr (AF32)
-                    arow[m] = static_cast<const float *>(args.a) + src * args.lda;
-                else
-                    arow[m] = static_cast<const uint16_t *>(args.a) + (src * P + part) * args.lda;
-            }
-        }
+        // M tiles of this chunk that hold at least one slot (uniform per workgroup)
+        const int m_used = (int)((n - c0 + spt - 1) / spt < MT ? (n - c0 + spt - 1) / spt : MT);
 
         f32x4 res[MT][NB];
 #pragma unroll
@@ -134,52 +148,105 @@ qgemm_kernel(const GemmArgs args) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) res[m][nb] = zero4;
 
-        for (int g = gb; g < ge; ++g) {
-            uint4 cw[NB];
-            float sc[NB];
-            uint32_t zc[NB];
+        // S register stages: while one group is multiplied, the loads of the
+        // next S - 1 groups are in flight.  Every load is unconditional; a group
+        // past the end of this wave's range loads out-of-range offsets (zero
+        // codes, scale and activations), so computing it adds exactly 0.
+        Stage<NB, MT, AF32> st[S];
+        uint32_t abase[MT];
+        int apart[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            abase[m] = kOob;
+            apart[m] = 0;
+        }
+        // The lane offsets (cbase, sbase, zbase, abase) are loop-invariant; the
+        // group offset is the same for the whole wave and goes in soffset.
+        auto load_w = [&](Stage<NB, MT, AF32> &q, int g) {
+            const bool in = g < ge;
+            const uint32_t gg = (uint32_t)g;
+            const uint32_t oc = in ? gg * 1024u : kOobS, os = in ? gg * 32u : kOobS,
+                           oz = in ? gg * 8u : kOobS;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int64_t tile = tile0 + nb;
-                if (tile < nt) {
-                    const int64_t tg = tile * G + g;
-                    cw[nb] = codes[tg * 64 + lane];
-                    sc[nb] = f16_bits_to_f32(scl[tg * 16 + r16]);
-                    zc[nb] = (zrs[tg * 8 + (r16 >> 1)] >> (4 * (r16 & 1))) & 15u;
-                } else {
-                    cw[nb] = make_uint4(0, 0, 0, 0);
-                    sc[nb] = 0.f;
-                    zc[nb] = 0u;
-                }
+                q.cw[nb] = buf_b128(wr, cbase[nb], oc);
+                q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, sbase[nb], os, 0);
+                q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, zbase[nb], oz, 0);
             }
-            uint4 af[MT][4];
+        };
+        auto load_a = [&](Stage<NB, MT, AF32> &q, int g) {
+            const bool in = g < ge;
+            const uint32_t oa = in ? (uint32_t)g * 128u * ES : kOobS;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    af[m][s] = avalid[m] ? load_a_frag<AF32>(arow[m], (int64_t)g * 128 + 32 * s + 8 * j, apart[m])
-                                         : make_uint4(0, 0, 0, 0);
-
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    q.af[m][s4][0] = buf_b128(ar, abase[m] + 32u * s4 * ES, oa);
+                    if constexpr (AF32) q.af[m][s4][AF32 ? 1 : 0] = buf_b128(ar, abase[m] + 32u * s4 * ES + 16, oa);
+                }
+        };
+        auto compute = [&](const Stage<NB, MT, AF32> &q) {
+            bf16x8 a[MT][4];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    if constexpr (AF32)
+                        a[m][s4] = as_bf16x8(split_frag(q.af[m][s4][0], q.af[m][s4][AF32 ? 1 : 0], apart[m]));
+                    else
+                        a[m][s4] = as_bf16x8(q.af[m][s4][0]);
+                }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const bf16x8 b0 = as_bf16x8(unpack_codes_bf16(cw[nb].x));
-                const bf16x8 b1 = as_bf16x8(unpack_codes_bf16(cw[nb].y));
-                const bf16x8 b2 = as_bf16x8(unpack_codes_bf16(cw[nb].z));
-                const bf16x8 b3 = as_bf16x8(unpack_codes_bf16(cw[nb].w));
-                const uint32_t zz = (0x4300u | zc[nb]) * 0x00010001u;   // bf16 pair (128+z, 128+z)
+                const bf16x8 b0 = as_bf16x8(unpack_codes_bf16(q.cw[nb].x));
+                const bf16x8 b1 = as_bf16x8(unpack_codes_bf16(q.cw[nb].y));
+                const bf16x8 b2 = as_bf16x8(unpack_codes_bf16(q.cw[nb].z));
+                const bf16x8 b3 = as_bf16x8(unpack_codes_bf16(q.cw[nb].w));
+                const uint32_t z = (q.zb[nb] >> zshift) & 15u;
+                const uint32_t zz = (0x4300u | z) * 0x00010001u;   // bf16 pair (128+z, 128+z)
                 const bf16x8 bz = as_bf16x8(make_uint4(zz, zz, zz, zz));
+                const float sc = f16_bits_to_f32((uint16_t)q.sc[nb]);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    f32x4 acc = mfma16x16x32(as_bf16x8(af[m][0]), b0, zero4);
-                    f32x4 xz = mfma16x16x32(as_bf16x8(af[m][0]), bz, zero4);
-                    acc = mfma16x16x32(as_bf16x8(af[m][1]), b1, acc);
-                    xz = mfma16x16x32(as_bf16x8(af[m][1]), bz, xz);
-                    acc = mfma16x16x32(as_bf16x8(af[m][2]), b2, acc);
-                    xz = mfma16x16x32(as_bf16x8(af[m][2]), bz, xz);
-                    acc = mfma16x16x32(as_bf16x8(af[m][3]), b3, acc);
-                    xz = mfma16x16x32(as_bf16x8(af[m][3]), bz, xz);
+                    if (m >= m_used) break;
+                    f32x4 acc = mfma16x16x32(a[m][0], b0, zero4);
+                    f32x4 xz = mfma16x16x32(a[m][0], bz, zero4);
+                    acc = mfma16x16x32(a[m][1], b1, acc);
+                    xz = mfma16x16x32(a[m][1], bz, xz);
+                    acc = mfma16x16x32(a[m][2], b2, acc);
+                    xz = mfma16x16x32(a[m][2], bz, xz);
+                    acc = mfma16x16x32(a[m][3], b3, acc);
+                    xz = mfma16x16x32(a[m][3], bz, xz);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) res[m][nb][v] += sc[nb] * (acc[v] - xz[v]);
+                    for (int v = 0; v < 4; ++v) res[m][nb][v] += sc * (acc[v] - xz[v]);
+                }
+            }
+        };
+        if (gb < ge) {
+            // weights first: they come from HBM; the activation rows need the
+            // slot -> row lookups resolved above, and come from cache
+#pragma unroll
+            for (int q = 0; q < S; ++q) load_w(st[q], gb + q);
+            // ---- byte offset of this lane's activation row (operand row r16 of each M tile)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int64_t slot = c0 + (int64_t)m * spt + r16 / P;
+                const int part = r16 % P;
+                const bool ok = (r16 < spt * P) && slot < n;
+                const int64_t slot_c = ok ? slot : 0;
+                const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
+                const int64_t row = AF32 ? src : src * P + part;
+                apart[m] = part;
+                abase[m] = ok ? (uint32_t)((row * args.lda + 8 * j) * ES) : kOob;
+            }
+#pragma unroll
+            for (int q = 0; q < S; ++q) load_a(st[q], gb + q);
+            for (int g = gb; g < ge; g += S) {
+#pragma unroll
+                for (int q = 0; q < S; ++q) {
+                    compute(st[q]);
+                    load_w(st[q], g + S + q);
+                    load_a(st[q], g + S + q);
                 }
             }
         }
@@ -194,27 +261,27 @@ qgemm_kernel(const GemmArgs args) {
                     red[((wave * MT + m) * NB + nb) * 256 + v * 64 + lane] = res[m][nb][v];
         __syncthreads();
 
-        const int pairs = args.epi == QI4_EPI_SILU_MUL ? NB / 2 : NB;
+        const int pairs = EPI == QI4_EPI_SILU_MUL ? NB / 2 : NB;
         const int items = MT * pairs * 64;
         for (int it = threadIdx.x; it < items; it += blockDim.x) {
             const int l = it & 63;
             const int rest = it >> 6;
             const int pi = rest % pairs;
             const int m = rest / pairs;
-            const int nbA = args.epi == QI4_EPI_SILU_MUL ? 2 * pi : pi;
+            const int nbA = EPI == QI4_EPI_SILU_MUL ? 2 * pi : pi;
             float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
             for (int ww = 0; ww < W; ++ww) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     a4[v] += red[((ww * MT + m) * NB + nbA) * 256 + v * 64 + l];
-                    if (args.epi == QI4_EPI_SILU_MUL)
+                    if (EPI == QI4_EPI_SILU_MUL)
                         b4[v] += red[((ww * MT + m) * NB + nbA + 1) * 256 + v * 64 + l];
                 }
             }
             const int col = l & 15;
             const int64_t tile = tile0 + nbA;
             int64_t oc;
-            if (args.epi == QI4_EPI_SILU_MUL)
+            if (EPI == QI4_EPI_SILU_MUL)
                 oc = (tile >> 1) * 16 + col;
             else
                 oc = tile < nt ? tile_row(tile, col, args.N, args.flags) : -1;
@@ -230,7 +297,7 @@ qgemm_kernel(const GemmArgs args) {
                     val += a4[v0 + p];
                     uval += b4[v0 + p];
                 }
-                if (args.epi == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
+                if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
                 const int64_t dst = row0 + slot;
                 if (args.out_mode == OUT_F32) {
                     static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
@@ -249,40 +316,60 @@ qgemm_kernel(const GemmArgs args) {
     }
 }
 
-template <int NB, int MT>
-int launch_nb_mt(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
-    if (a.a_f32)
-        qgemm_kernel<NB, MT, true><<<grid, threads, 0, st>>>(a);
-    else
-        qgemm_kernel<NB, MT, false><<<grid, threads, 0, st>>>(a);
+template <int NB, int MT, int S>
+int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
+    if (a.epi == QI4_EPI_SILU_MUL) {
+        if constexpr (NB % 2 == 0) {
+            if (a.a_f32)
+                qgemm_kernel<NB, MT, true, 2, QI4_EPI_SILU_MUL><<<grid, threads, 0, st>>>(a);
+            else
+                qgemm_kernel<NB, MT, false, S, QI4_EPI_SILU_MUL><<<grid, threads, 0, st>>>(a);
+        } else {
+            return QI4_ERR_UNSUPPORTED;
+        }
+    } else if (a.a_f32) {
+        qgemm_kernel<NB, MT, true, 2, QI4_EPI_NONE><<<grid, threads, 0, st>>>(a);
+    } else {
+        qgemm_kernel<NB, MT, false, S, QI4_EPI_NONE><<<grid, threads, 0, st>>>(a);
+    }
     return launch_status();
 }
 
 }  // namespace
 
+// Launch shape, from sweeps on MI355X over the decode workloads (dense Llama-7B
+// and 5120/13824 shapes, DeepSeek-V3-shaped experts at T = 1, 8, 32):
+//  * W waves split K; about ten 128-wide groups per wave for a single matrix,
+//    and two waves per workgroup when many expert problems already fill the chip;
+//  * NB = 2 tiles per workgroup (the gate/up pair) unless a single small matrix
+//    needs more workgroups (NB = 1);
+//  * one M tile per pass (16 activation rows) unless a problem has more slots.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t st) {
     if (n_problems <= 0 || max_slots <= 0) return QI4_OK;
     const int64_t nt = num_tiles(args.N, args.flags);
     const int64_t G = args.K / kGroup;
     const int spt = 16 / args.P;
     const int MT = max_slots > spt ? 2 : 1;
-    const int nb_min = args.epi == QI4_EPI_SILU_MUL ? 2 : 1;
-    int NB = 4;
-    while (NB > nb_min && ceil_div(nt, NB) * n_problems < 2048) NB /= 2;
-    int W = kMaxWaves;
-    while (W > 1 && (G / W < 2 || W * MT * NB > kRedSlots)) W /= 2;
+    const bool silu = args.epi == QI4_EPI_SILU_MUL;
+    int NB = (silu || ceil_div(nt, 2) * n_problems >= 1024) ? 2 : 1;
+    int W;
+    if (n_problems > 1) {
+        W = 2;
+    } else {
+        W = 1;
+        while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
+    }
+    while (W > 1 && W * MT * NB > kRedSlots) W /= 2;
     const int64_t gx = ceil_div(nt, NB);
     if (gx > 0x7fffffff || n_problems > 65535) return QI4_ERR_SHAPE;
     dim3 grid((unsigned)gx, (unsigned)n_problems);
     const int threads = W * 64;
     if (MT == 1) {
-        if (NB == 4) return launch_nb_mt<4, 1>(args, grid, threads, st);
-        if (NB == 2) return launch_nb_mt<2, 1>(args, grid, threads, st);
-        return launch_nb_mt<1, 1>(args, grid, threads, st);
+        if (NB == 2) return launch_cfg<2, 1, 2>(args, grid, threads, st);
+        return launch_cfg<1, 1, 2>(args, grid, threads, st);
     }
-    if (NB == 4) return launch_nb_mt<4, 2>(args, grid, threads, st);
-    if (NB == 2) return launch_nb_mt<2, 2>(args, grid, threads, st);
-    return launch_nb_mt<1, 2>(args, grid, threads, st);
+    if (NB == 2) return launch_cfg<2, 2, 2>(args, grid, threads, st);
+    return launch_cfg<1, 2, 2>(args, grid, threads, st);
 }
 
 }  // namespace qi4
@@ -306,6 +393,7 @@ extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t 
     const int64_t xb = T * K * (x_dtype == QI4_F32 ? 4 : 2);
     const int64_t yb = T * n_out * (y_dtype == QI4_F32 ? 4 : 2);
     const int64_t wb = PackedLayout(N, K, flags).bytes;
+    if (wb >= (int64_t(1) << 31) || xb >= (int64_t(1) << 31)) return QI4_ERR_SHAPE;
     if (overlaps(y, yb, x, xb) || overlaps(y, yb, packed_w, wb)) return QI4_ERR_ALIAS;
     if ((rc = check_device())) return rc;
 
@@ -316,6 +404,7 @@ extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t 
     a.flags = flags;
     a.a = x;
     a.lda = K;
+    a.a_bytes = xb;
     a.a_f32 = x_dtype == QI4_F32;
     a.P = a.a_f32 ? 4 : 1;
     a.moe = 0;

@@ -298,6 +298,7 @@ GemmArgs gate_up_args(const qi4_moe_desc *d, const void *x, int64_t T, const int
     a.flags = QI4_PACK_GATEUP;
     a.a = x;
     a.lda = d->hidden;
+    a.a_bytes = T * d->hidden * 2;
     a.a_f32 = 0;
     a.P = 1;
     a.moe = 1;
@@ -327,6 +328,7 @@ GemmArgs down_args(const qi4_moe_desc *d, const void *h, int64_t T, const int32_
     a.flags = 0;
     a.a = h;
     a.lda = d->inter;
+    a.a_bytes = (T * d->top_k + (d->has_shared ? T : 0)) * 2 * d->inter * 2;
     a.a_f32 = 0;
     a.P = 2;
     a.moe = 1;
@@ -355,7 +357,12 @@ int launch_combine(const qi4_moe_desc *d, const float *y, const float *wts, cons
 
 int check_T(int64_t T, const qi4_moe_desc *d) {
     if (T < 0 || T > 65535) return QI4_ERR_SHAPE;
-    if (T * d->top_k > (int64_t(1) << 30)) return QI4_ERR_SHAPE;
+    const int64_t R = T * d->top_k + (d->has_shared ? T : 0);
+    if (R * 2 * d->inter * 2 >= (int64_t(1) << 31) || T * d->hidden * 2 >= (int64_t(1) << 31))
+        return QI4_ERR_SHAPE;
+    if (PackedLayout(2 * d->inter, d->hidden, QI4_PACK_GATEUP).bytes >= (int64_t(1) << 31) ||
+        PackedLayout(d->hidden, d->inter, 0).bytes >= (int64_t(1) << 31))
+        return QI4_ERR_SHAPE;
     return QI4_OK;
 }
 
