@@ -28,6 +28,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, decimal GB/s
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_decode_t32_hbm_traffic.md")
+GEMM_SOURCES = ["ffn_int4_g128_amd/csrc/qi4_dev.h", "ffn_int4_g128_amd/csrc/qi4_gemm.h",
+                "ffn_int4_g128_amd/csrc/qi4_gemm.hip"]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
+    or None when the GEMM sources changed since the counters were taken."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_SUMMARY).read().splitlines()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in lines if ": " in l and l.split(": ", 1)[0] in
+              ("kernel-source-sha256", "gate-up-traffic-bytes-per-launch"))
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("kernel-source-sha256") != h.hexdigest():
+        return None
+    return float(kv["gate-up-traffic-bytes-per-launch"])
 
 
 def parse():
@@ -250,7 +271,7 @@ def main():
                    "group": 128, "layers_alternated": args.layers},
         "roofline": {"bound": "hbm", "kernel": "moe grouped gate/up + SiLU (qgemm_kernel)",
                      "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gu_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": gu_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "launch_us": main_r["gate_up_us"], "bytes_per_launch": main_r["gate_up_bytes"]},
         "step_GBps": main_r["step_GBps"],
         "experts_touched_mean": main_r["experts_touched_mean"],

@@ -343,13 +343,17 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 //    and two waves per workgroup when many expert problems already fill the chip;
 //  * NB = 2 tiles per workgroup (the gate/up pair) unless a single small matrix
 //    needs more workgroups (NB = 1);
-//  * one M tile per pass (16 activation rows) unless a problem has more slots.
+//  * one M tile per pass (16 activation rows), two for a single matrix with
+//    more rows.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t st) {
     if (n_problems <= 0 || max_slots <= 0) return QI4_OK;
     const int64_t nt = num_tiles(args.N, args.flags);
     const int64_t G = args.K / kGroup;
     const int spt = 16 / args.P;
-    const int MT = max_slots > spt ? 2 : 1;
+    // Expert problems mostly hold a few slots each: one M tile per pass keeps
+    // registers low; a problem with more slots (the shared expert) takes more
+    // passes.  A single matrix with more than 16 rows uses two M tiles.
+    const int MT = (n_problems == 1 && max_slots > spt) ? 2 : 1;
     const bool silu = args.epi == QI4_EPI_SILU_MUL;
     int NB = (silu || ceil_div(nt, 2) * n_problems >= 1024) ? 2 : 1;
     int W;
