@@ -106,6 +106,7 @@ class Stepper:
         self.h = torch.empty((R, 2, c["I"]), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((R, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.ws = q.moe_workspace(layers[0], top_k, T, dev)
         self.n_batches = n_batches
 
     def step(self, i, ev=None):
@@ -126,12 +127,13 @@ class Stepper:
         if ev is not None:
             ev[0].record()
         q._check(L.moe_expert_gate_up(dref, P(self.x[b]), T, P(self.sp), P(self.off), P(self.act),
-                                      P(mw.w_gate_up), P(mw.shared_gate_up), P(self.h), st),
-                 "gate_up")
+                                      P(mw.w_gate_up), P(mw.shared_gate_up), P(self.h), P(self.ws),
+                                      self.ws.numel(), st), "gate_up")
         if ev is not None:
             ev[1].record()
         q._check(L.moe_expert_down(dref, P(self.h), T, P(self.off), P(self.act), P(mw.w_down),
-                                   P(mw.shared_down), P(self.y), st), "down")
+                                   P(mw.shared_down), P(self.y), P(self.ws), self.ws.numel(), st),
+                 "down")
         if ev is not None:
             ev[2].record()
         q._check(L.moe_combine(dref, P(self.y), P(self.wts), P(self.inv), T, P(self.out), st),

@@ -65,8 +65,8 @@ def lib():
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
             "moe_sort_tokens": (ci, [vp, i64, i32, i64, vp, vp, vp, vp, vp]),
             "moe_ffn_int4_workspace_bytes": (i64, [dp, i64]),
-            "moe_expert_gate_up": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
-            "moe_expert_down": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp]),
+            "moe_expert_gate_up": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+            "moe_expert_down": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
             "moe_combine": (ci, [dp, vp, vp, vp, i64, vp, vp]),
             "moe_ffn_int4": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         }
@@ -290,28 +290,35 @@ def moe_ffn(x, w: MoeWeights, top_k: int, logits=None, ids=None, weights=None, w
     return out
 
 
-def moe_gate_up(x, w: MoeWeights, top_k: int, sorted_pairs, offsets, active, h=None, stream=None):
+def moe_gate_up(x, w: MoeWeights, top_k: int, sorted_pairs, offsets, active, h=None,
+                workspace=None, stream=None):
     import torch
     T = x.shape[0]
     R = T * top_k + (T if w.shared_gate_up is not None else 0)
     if h is None:
         h = torch.empty((R, 2, w.I), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = moe_workspace(w, top_k, T, x.device)
     d = w.desc(top_k)
     _check(lib().moe_expert_gate_up(ctypes.byref(d), _ptr(x), T, _ptr(sorted_pairs), _ptr(offsets),
                                     _ptr(active), _ptr(w.w_gate_up), _ptr(w.shared_gate_up),
-                                    _ptr(h), _stream(stream)), "moe_expert_gate_up")
+                                    _ptr(h), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_expert_gate_up")
     return h
 
 
-def moe_down(h, T: int, w: MoeWeights, top_k: int, offsets, active, y=None, stream=None):
+def moe_down(h, T: int, w: MoeWeights, top_k: int, offsets, active, y=None, workspace=None,
+             stream=None):
     import torch
     R = T * top_k + (T if w.shared_down is not None else 0)
     if y is None:
         y = torch.empty((R, w.H), dtype=torch.float32, device=h.device)
+    if workspace is None:
+        workspace = moe_workspace(w, top_k, T, h.device)
     d = w.desc(top_k)
     _check(lib().moe_expert_down(ctypes.byref(d), _ptr(h), T, _ptr(offsets), _ptr(active),
-                                 _ptr(w.w_down), _ptr(w.shared_down), _ptr(y), _stream(stream)),
-           "moe_expert_down")
+                                 _ptr(w.w_down), _ptr(w.shared_down), _ptr(y), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)), "moe_expert_down")
     return y
 
 

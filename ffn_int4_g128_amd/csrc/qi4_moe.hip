@@ -13,6 +13,7 @@
 
 #include "qi4_gemm.h"
 #include "qi4_host.h"
+#include "qi4_prefill.h"
 
 namespace qi4 {
 namespace {
@@ -241,11 +242,16 @@ int check_desc(const qi4_moe_desc *d) {
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Batches of at least this many tokens run the prefill GEMM (fp16 MFMA on
+// LDS-staged activation tiles); smaller ones the weight-streaming decode GEMM.
+constexpr int64_t kPrefillMinT = 128;
+
 struct MoeWorkspace {
-    int64_t ids, wts, sorted, offsets, p2s, active, h, y, total;
+    int64_t ids, wts, sorted, offsets, p2s, active, h, y, x16, ex, h16, eh, tiles, ntiles, total;
     MoeWorkspace(const qi4_moe_desc *d, int64_t T) {
         const int64_t P = T * d->top_k;
         const int64_t R = P + (d->has_shared ? T : 0);
+        const bool pf = T >= kPrefillMinT;
         int64_t o = 0;
         ids = o;     o += align256(P * 4);
         wts = o;     o += align256(P * 4);
@@ -255,6 +261,13 @@ struct MoeWorkspace {
         active = o;  o += align256((d->num_experts + 1) * 4);
         h = o;       o += align256(R * 2 * d->inter * 2);
         y = o;       o += align256(R * d->hidden * 4);
+        // prefill only: fp16 rows with exponents and the tile list
+        x16 = o;     o += pf ? align256(T * d->hidden * 2) : 0;
+        ex = o;      o += pf ? align256(T * 4) : 0;
+        h16 = o;     o += pf ? align256(R * d->inter * 2) : 0;
+        eh = o;      o += pf ? align256(R * 4) : 0;
+        tiles = o;   o += pf ? align256(prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared) * 8) : 0;
+        ntiles = o;  o += pf ? 256 : 0;
         total = o;
     }
 };
@@ -346,6 +359,77 @@ GemmArgs down_args(const qi4_moe_desc *d, const void *h, int64_t T, const int32_
     return a;
 }
 
+PrefillArgs prefill_args(const qi4_moe_desc *d, int64_t T, bool gate_up, const int32_t *sorted,
+                         const int32_t *offsets, const int32_t *active, const void *w,
+                         const void *w_shared, const uint16_t *a16, const int32_t *aexp,
+                         const int2 *tiles, const int32_t *ntiles, void *out) {
+    PrefillArgs a = {};
+    const int64_t H = d->hidden, I = d->inter;
+    a.w = static_cast<const uint8_t *>(w);
+    a.w_shared = static_cast<const uint8_t *>(w_shared);
+    a.N = gate_up ? 2 * I : H;
+    a.K = gate_up ? H : I;
+    a.flags = gate_up ? QI4_PACK_GATEUP : 0;
+    a.w_stride = PackedLayout(a.N, a.K, a.flags).bytes;
+    a.a16 = a16;
+    a.a_rows = gate_up ? T : T * d->top_k + (d->has_shared ? T : 0);
+    a.a_exp = aexp;
+    a.gather_tokens = gate_up ? 1 : 0;
+    a.sorted_pairs = sorted;
+    a.offsets = offsets;
+    a.active = active;
+    a.top_k = d->top_k;
+    a.T = T;
+    a.tiles = tiles;
+    a.tile_count = ntiles;
+    a.out = out;
+    a.ldo = gate_up ? I : H;
+    a.epi = gate_up ? QI4_EPI_SILU_MUL : QI4_EPI_NONE;
+    a.n_out = gate_up ? I : H;
+    return a;
+}
+
+// The two projections of the expert FFN on either path.  `ws` is the moe_ffn_int4
+// workspace (only its prefill regions are used here).
+int run_gate_up(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *sorted,
+                const int32_t *offsets, const int32_t *active, const void *w_gu, const void *sh_gu,
+                void *h, uint8_t *ws, hipStream_t st) {
+    int rc;
+    if (T < kPrefillMinT) {
+        GemmArgs a = gate_up_args(d, x, T, sorted, offsets, active, w_gu, sh_gu, h);
+        return launch_qgemm(a, a.routed_slots + d->has_shared, T, st);
+    }
+    const MoeWorkspace L(d, T);
+    uint16_t *x16 = reinterpret_cast<uint16_t *>(ws + L.x16);
+    int32_t *ex = reinterpret_cast<int32_t *>(ws + L.ex);
+    int2 *tiles = reinterpret_cast<int2 *>(ws + L.tiles);
+    int32_t *nt = reinterpret_cast<int32_t *>(ws + L.ntiles);
+    if ((rc = launch_prep_rows(x, 0, T, d->hidden, x16, ex, st))) return rc;
+    if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, nt, st))) return rc;
+    PrefillArgs a = prefill_args(d, T, true, sorted, offsets, active, w_gu, sh_gu, x16, ex, tiles, nt, h);
+    return launch_prefill(a, prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared), st);
+}
+
+int run_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *offsets,
+             const int32_t *active, const void *w_dn, const void *sh_dn, float *y, uint8_t *ws,
+             hipStream_t st) {
+    int rc;
+    if (T < kPrefillMinT) {
+        GemmArgs a = down_args(d, h, T, offsets, active, w_dn, sh_dn, y);
+        return launch_qgemm(a, a.routed_slots + d->has_shared, T, st);
+    }
+    const MoeWorkspace L(d, T);
+    const int64_t R = T * d->top_k + (d->has_shared ? T : 0);
+    uint16_t *h16 = reinterpret_cast<uint16_t *>(ws + L.h16);
+    int32_t *eh = reinterpret_cast<int32_t *>(ws + L.eh);
+    int2 *tiles = reinterpret_cast<int2 *>(ws + L.tiles);
+    int32_t *nt = reinterpret_cast<int32_t *>(ws + L.ntiles);
+    if ((rc = launch_prep_rows(h, 1, R, d->inter, h16, eh, st))) return rc;
+    if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, nt, st))) return rc;
+    PrefillArgs a = prefill_args(d, T, false, nullptr, offsets, active, w_dn, sh_dn, h16, eh, tiles, nt, y);
+    return launch_prefill(a, prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared), st);
+}
+
 int launch_combine(const qi4_moe_desc *d, const float *y, const float *wts, const int32_t *p2s,
                    int64_t T, void *out, hipStream_t st) {
     if (T > 65535) return QI4_ERR_SHAPE;   // grid.y limit; check_T enforces it
@@ -416,37 +500,39 @@ int64_t moe_ffn_int4_workspace_bytes(const qi4_moe_desc *d, int64_t T) {
 int moe_expert_gate_up(const qi4_moe_desc *d, const void *x, int64_t T,
                        const int32_t *sorted_pairs, const int32_t *expert_offsets,
                        const int32_t *active, const void *w_gate_up, const void *shared_gate_up,
-                       void *h, void *stream) {
+                       void *h, void *workspace, int64_t ws_bytes, void *stream) {
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_T(T, d))) return rc;
     if (T == 0) return QI4_OK;
-    if (!x || !sorted_pairs || !expert_offsets || !active || !w_gate_up || !h) return QI4_ERR_NULL;
+    if (!x || !sorted_pairs || !expert_offsets || !active || !w_gate_up || !h || !workspace)
+        return QI4_ERR_NULL;
     if ((d->has_shared != 0) != (shared_gate_up != nullptr)) return QI4_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(h, 4) ||
+    if (!aligned(x, 16) || !aligned(w_gate_up, 16) || !aligned(h, 4) || !aligned(workspace, 256) ||
         (shared_gate_up && !aligned(shared_gate_up, 16)))
         return QI4_ERR_SHAPE;
+    if (ws_bytes < MoeWorkspace(d, T).total) return QI4_ERR_WORKSPACE;
     if ((rc = check_device())) return rc;
-    GemmArgs a = gate_up_args(d, x, T, sorted_pairs, expert_offsets, active, w_gate_up,
-                              shared_gate_up, h);
-    return launch_qgemm(a, a.routed_slots + d->has_shared, T, as_stream(stream));
+    return run_gate_up(d, x, T, sorted_pairs, expert_offsets, active, w_gate_up, shared_gate_up, h,
+                       static_cast<uint8_t *>(workspace), as_stream(stream));
 }
 
 int moe_expert_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *expert_offsets,
                     const int32_t *active, const void *w_down, const void *shared_down, float *y,
-                    void *stream) {
+                    void *workspace, int64_t ws_bytes, void *stream) {
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_T(T, d))) return rc;
     if (T == 0) return QI4_OK;
-    if (!h || !expert_offsets || !active || !w_down || !y) return QI4_ERR_NULL;
+    if (!h || !expert_offsets || !active || !w_down || !y || !workspace) return QI4_ERR_NULL;
     if ((d->has_shared != 0) != (shared_down != nullptr)) return QI4_ERR_NULL;
-    if (!aligned(h, 16) || !aligned(w_down, 16) || !aligned(y, 4) ||
+    if (!aligned(h, 16) || !aligned(w_down, 16) || !aligned(y, 4) || !aligned(workspace, 256) ||
         (shared_down && !aligned(shared_down, 16)))
         return QI4_ERR_SHAPE;
+    if (ws_bytes < MoeWorkspace(d, T).total) return QI4_ERR_WORKSPACE;
     if ((rc = check_device())) return rc;
-    GemmArgs a = down_args(d, h, T, expert_offsets, active, w_down, shared_down, y);
-    return launch_qgemm(a, a.routed_slots + d->has_shared, T, as_stream(stream));
+    return run_down(d, h, T, expert_offsets, active, w_down, shared_down, y,
+                    static_cast<uint8_t *>(workspace), as_stream(stream));
 }
 
 int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights,
@@ -502,10 +588,9 @@ int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
 
     if (router_logits && (rc = launch_route(router_logits, T, E, k, ids, wts, st))) return rc;
     if ((rc = launch_sort(ids, T * k, E, sorted, offsets, p2s, active, st))) return rc;
-    GemmArgs gu = gate_up_args(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h);
-    if ((rc = launch_qgemm(gu, gu.routed_slots + d->has_shared, T, st))) return rc;
-    GemmArgs dn = down_args(d, h, T, offsets, active, w_down, shared_down, y);
-    if ((rc = launch_qgemm(dn, dn.routed_slots + d->has_shared, T, st))) return rc;
+    if ((rc = run_gate_up(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h, ws, st)))
+        return rc;
+    if ((rc = run_down(d, h, T, offsets, active, w_down, shared_down, y, ws, st))) return rc;
     return launch_combine(d, y, wts, p2s, T, out, st);
 }
 

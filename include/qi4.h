@@ -171,14 +171,20 @@ int64_t moe_ffn_int4_workspace_bytes(const qi4_moe_desc *d, int64_t T);
  *   h  [R][2][I] bf16 bits: SiLU(gate)*up as an unevaluated sum hi + lo of two
  *      bf16 numbers (hi = bf16(h), lo = bf16(h - hi)), about 16 significant bits
  *   y  [R][H] float32: each expert's down-projection output, before weighting
- * `active` is the array moe_sort_tokens fills. */
+ * `active` is the array moe_sort_tokens fills.  `workspace` is a buffer of
+ * moe_ffn_int4_workspace_bytes(d, T) bytes (256-byte aligned); batches of 128 or
+ * more tokens use it for fp16 copies of the activations and the tile list of the
+ * prefill kernels (smaller batches do not touch it).  h and y may lie inside it
+ * only if they do not overlap those regions; passing separate buffers is simplest. */
 int moe_expert_gate_up(const qi4_moe_desc *d, const void *x, int64_t T,
                        const int32_t *sorted_pairs, const int32_t *expert_offsets,
                        const int32_t *active, const void *w_gate_up,
-                       const void *shared_gate_up, void *h, void *stream);
+                       const void *shared_gate_up, void *h, void *workspace, int64_t ws_bytes,
+                       void *stream);
 int moe_expert_down(const qi4_moe_desc *d, const void *h, int64_t T,
                     const int32_t *expert_offsets, const int32_t *active,
-                    const void *w_down, const void *shared_down, float *y, void *stream);
+                    const void *w_down, const void *shared_down, float *y,
+                    void *workspace, int64_t ws_bytes, void *stream);
 /* out[t] = sum_j topk_weights[t][j] * y[pair_to_sorted[t*top_k+j]] (+ y[P+t]),
    summed in that order in float32, rounded once to bf16. */
 int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights,

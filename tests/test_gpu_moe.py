@@ -71,7 +71,9 @@ def _small_layer(E, H, I, seed, shared=True):
 
 @pytest.mark.parametrize("T,E,H,I,k,shared", [(1, 8, 256, 128, 2, True), (5, 8, 256, 128, 2, True),
                                               (33, 16, 384, 256, 4, True), (17, 6, 128, 128, 6, False),
-                                              (64, 4, 256, 128, 1, True)])
+                                              (64, 4, 256, 128, 1, True), (127, 8, 256, 128, 2, True),
+                                              (128, 8, 256, 128, 2, True), (300, 16, 384, 256, 4, True),
+                                              (200, 6, 128, 384, 6, False), (513, 32, 512, 128, 8, True)])
 def test_moe_small_layers(T, E, H, I, k, shared):
     import torch
     import ffn_int4_g128_amd as q
@@ -87,12 +89,13 @@ def test_moe_small_layers(T, E, H, I, k, shared):
     assert_within(to_f64(out), ref, tol, f"moe T{T} E{E} H{H} I{I} k{k} shared={shared}")
 
 
-def test_moe_given_routing_and_stage_calls_agree():
+@pytest.mark.parametrize("T", [12, 150])
+def test_moe_given_routing_and_stage_calls_agree(T):
     """Passing ids/weights instead of logits, and running the five stages by hand,
-    give the same bits as the one-call path."""
+    give the same bits as the one-call path (decode and prefill sizes)."""
     import torch
     import ffn_int4_g128_amd as q
-    T, E, H, I, k = 12, 8, 256, 128, 3
+    E, H, I, k = 8, 256, 128, 3
     ex, sh = _small_layer(E, H, I, 80)
     x = bf16_dev(workloads.activations(81, 0, T, H, "bf16"))
     lg = to_dev(workloads.logits_normal(82, 0, T, E))
