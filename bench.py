@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, decimal GB/s
+BF16_MFMA_PEAK = 2.5166e15   # MI355X dense fp16/bf16 MFMA, flop/s
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_decode_t32_hbm_traffic.md")
 GEMM_SOURCES = ["ffn_int4_g128_amd/csrc/qi4_dev.h", "ffn_int4_g128_amd/csrc/qi4_gemm.h",
                 "ffn_int4_g128_amd/csrc/qi4_gemm.hip"]
@@ -59,6 +60,8 @@ def parse():
     ap.add_argument("--T", type=int, default=32, help="tokens of the main decode batch")
     ap.add_argument("--sweep", type=str, default="1,8", help="other decode batch sizes to report")
     ap.add_argument("--layers", type=int, default=2)
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="timed prefill steps (T=2048, Zipf-skewed routing); 0 to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -84,7 +87,7 @@ class Stepper:
     """Runs the five stages of one MoE forward through the C ABI, with events
     around the two grouped GEMMs."""
 
-    def __init__(self, q, torch, layers, T, top_k, n_batches, c):
+    def __init__(self, q, torch, layers, T, top_k, n_batches, c, zipf=None):
         import numpy as np
         import workloads
         self.q, self.torch, self.layers, self.T, self.k = q, torch, layers, T, top_k
@@ -92,8 +95,11 @@ class Stepper:
         E, H = c["E"], c["H"]
         self.x = [q_bf16(torch, workloads.activations(c["seed"], 500 + 10 * b + T, T, H, "bf16"))
                   for b in range(n_batches)]
-        self.logits = [torch.from_numpy(workloads.logits_normal(c["seed"], 600 + 10 * b + T, T, E)).cuda()
-                       for b in range(n_batches)]
+        if zipf is None:
+            lg = [workloads.logits_normal(c["seed"], 600 + 10 * b + T, T, E) for b in range(n_batches)]
+        else:
+            lg = [workloads.logits_zipf(c["seed"], 600 + 10 * b + T, T, E, zipf) for b in range(n_batches)]
+        self.logits = [torch.from_numpy(v).cuda() for v in lg]
         dev = "cuda"
         P = T * top_k
         R = P + T
@@ -193,6 +199,41 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     }
 
 
+def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
+    """Prefill: T=2048 tokens of one layer, top-8 routing with Zipf(1.1) skew."""
+    import workloads
+    p = dict(workloads.MOE_PREFILL)
+    c = dict(workloads.MOE_DECODE)
+    T, k, H, I = p["T"], p["top_k"], p["H"], p["I"]
+    s = Stepper(q, torch, layers, T, k, n_batches, c, zipf=p["zipf"])
+    period = len(layers) * n_batches
+    touched = [s.touched(i) for i in range(period)]
+    for i in range(warmup):
+        s.step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s.step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
+    dn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
+    per_w = workloads.packed_weight_bytes(1)
+    rows = T * k + T
+    flop_gu, flop_dn = 2.0 * rows * 2 * I * H, 2.0 * rows * H * I
+    n_e = sum(touched[i % period] for i in range(steps)) / steps + 1
+    bytes_step = n_e * 3 * I * H * per_w + 2 * T * H * 2
+    ms = wall * 1e3 / steps
+    return {"T": T, "workload": "moe_ffn_prefill_deepseekv3_shape_zipf1.1", "ms_per_step": ms,
+            "tokens_per_s": T * steps / wall, "experts_touched_mean": n_e,
+            "mfma_frac_step": (flop_gu + flop_dn) / (ms * 1e-3) / BF16_MFMA_PEAK,
+            "hbm_GBps_step": bytes_step / (ms * 1e-3) / 1e9,
+            "gate_up_ms": gu * 1e3, "down_ms": dn * 1e3,
+            "gate_up_mfma_frac": flop_gu / gu / BF16_MFMA_PEAK,
+            "down_mfma_frac": flop_dn / dn / BF16_MFMA_PEAK}
+
+
 def cpu_baseline(c, T, target_s):
     """The oracle (fp64 C, OpenMP over output rows) on a bounded sample of the
     same workload: n tokens of layer 0, n chosen for about target_s seconds."""
@@ -246,6 +287,11 @@ def main():
         log(f"T={t}: {json.dumps(r)}")
         sweep.append(r)
 
+    prefill = None
+    if args.prefill_steps > 0:
+        prefill = run_prefill(q, torch, layers, args.prefill_steps, 2)
+        log(f"prefill: {json.dumps(prefill)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         del layers
@@ -280,6 +326,7 @@ def main():
         "down_GBps": main_r["down_GBps"],
         "sweep": [{k: r[k] for k in ("T", "tokens_per_s", "ms_per_step", "step_GBps", "gate_up_GBps",
                                      "down_GBps", "experts_touched_mean")} for r in sweep],
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

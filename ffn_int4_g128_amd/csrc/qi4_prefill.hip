@@ -13,7 +13,8 @@
 //  * a workgroup is 4 waves x 64 weight rows and 128 activation rows; the
 //    activation tile of each group (32 KB) is copied from memory straight into
 //    LDS (buffer loads with the LDS bit) in the exact order the MFMA operand
-//    reads want, double-buffered, and shared by the 4 waves;
+//    reads want, double-buffered, and shared by the 4 waves; two workgroups
+//    share a CU so one computes while the other waits at its barrier;
 //  * a device-side tile list (expert, first row) built from the expert
 //    segments covers every routed expert plus the shared one, so load follows
 //    the routing skew without a host round trip.
@@ -123,10 +124,9 @@ constexpr int kABlock = 1024;                  // one MFMA operand fragment of a
 constexpr int kABytes = kMS * 4 * kABlock;     // activation tile of one group: 32 KB
 
 template <int EPI>
-__global__ void __launch_bounds__(kWaves * 64)
+__global__ void __launch_bounds__(kWaves * 64, 2)
 prefill_kernel(const PrefillArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kABytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a1[kABytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kABytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -159,15 +159,10 @@ prefill_kernel(const PrefillArgs args) {
     const __amdgpu_buffer_rsrc_t wr = rsrc(w, (uint32_t)L.bytes);
     const __amdgpu_buffer_rsrc_t ar = rsrc(args.a16, (uint32_t)(args.a_rows * args.K * 2));
 
-    uint32_t cbase[kNB], sbase[kNB], zbase[kNB];
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        const int64_t tile = tile0 + nb;
-        const bool ok = tile < nt;
-        cbase[nb] = ok ? (uint32_t)((tile * G * 64 + lane) * 16) : kOob;
-        sbase[nb] = ok ? (uint32_t)(L.scales_off + (tile * G * 16 + r16) * 2) : kOob;
-        zbase[nb] = ok ? (uint32_t)(L.zeros_off + tile * G * 8 + (r16 >> 1)) : kOob;
-    }
+    // Weight offsets: the lane part is the same for every tile and group; the
+    // tile and group part is wave-uniform and goes in soffset (scalar registers).
+    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 2u, vz = (uint32_t)(r16 >> 1);
+    const int nt_here = (int)(nt - tile0 < kNB ? (nt - tile0 > 0 ? nt - tile0 : 0) : kNB);
     const int zshift = 4 * (r16 & 1);
 
     // Activation rows this lane copies into LDS: wave w fills the operand
@@ -201,13 +196,16 @@ prefill_kernel(const PrefillArgs args) {
     };
     auto load_w = [&](WStage &q, int g) {
         const bool in = g < G;
-        const uint32_t oc = in ? (uint32_t)g * 1024u : kOobS, os = in ? (uint32_t)g * 32u : kOobS,
-                       oz = in ? (uint32_t)g * 8u : kOobS;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-            q.cw[nb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, cbase[nb], oc, 0));
-            q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, sbase[nb], os, 0);
-            q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, zbase[nb], oz, 0);
+            const bool ok = in && nb < nt_here;
+            const int64_t tg = (tile0 + nb) * G + g;
+            const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
+            const uint32_t os = ok ? (uint32_t)(L.scales_off + tg * 32) : kOobS;
+            const uint32_t oz = ok ? (uint32_t)(L.zeros_off + tg * 8) : kOobS;
+            q.cw[nb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, vc, oc, 0));
+            q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, vs, os, 0);
+            q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, vz, oz, 0);
         }
     };
 
@@ -216,6 +214,10 @@ prefill_kernel(const PrefillArgs args) {
     for (int m = 0; m < kMS; ++m)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // 16-row activation subtiles of this tile that hold rows (uniform): the
+    // MFMAs of empty subtiles are skipped, so a small expert costs only its rows.
+    const int m_used = (int)((n - m0 + 15) / 16 < kMS ? (n - m0 + 15) / 16 : kMS);
 
     auto compute = [&](const WStage &q, const uint8_t *buf) {
         uint32_t negz[kNB], s2[kNB];
@@ -227,41 +229,55 @@ prefill_kernel(const PrefillArgs args) {
             negz[nb] = nz * 0x00010001u;
             s2[nb] = (q.sc[nb] & 0xFFFFu) * 0x00010001u;
         }
+        // Operand fragments in (k step, subtile) order through a 2-deep ring, so
+        // each LDS read is issued one MFMA batch before it is needed.
+        auto rd = [&](int i) {
+            return *reinterpret_cast<const f16x8 *>(buf + ((i & 7) * 4 + (i >> 3)) * kABlock + lane * 16);
+        };
+        f16x8 a[2];
+        a[0] = rd(0);
+        f16x8 b[kNB];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            f16x8 b[kNB];
+        for (int i = 0; i < 4 * kMS; ++i) {
+            const int s = i >> 3, m = i & 7;
+            if (m == 0) {
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-                const uint32_t d = s == 0 ? q.cw[nb].x : s == 1 ? q.cw[nb].y : s == 2 ? q.cw[nb].z : q.cw[nb].w;
-                b[nb] = __builtin_bit_cast(f16x8, dequant_f16(d, negz[nb], s2[nb]));
+                for (int nb = 0; nb < kNB; ++nb) {
+                    const uint32_t d = s == 0 ? q.cw[nb].x : s == 1 ? q.cw[nb].y : s == 2 ? q.cw[nb].z : q.cw[nb].w;
+                    b[nb] = __builtin_bit_cast(f16x8, dequant_f16(d, negz[nb], s2[nb]));
+                }
             }
+            if (i + 1 < 4 * kMS) a[(i + 1) & 1] = rd(i + 1);
+            if (m < m_used) {
 #pragma unroll
-            for (int m = 0; m < kMS; ++m) {
-                const f16x8 a = *reinterpret_cast<const f16x8 *>(buf + (m * 4 + s) * kABlock + lane * 16);
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) acc[m][nb] = mfma16x16x32_f16(a, b[nb], acc[m][nb]);
+                for (int nb = 0; nb < kNB; ++nb) acc[m][nb] = mfma16x16x32_f16(a[i & 1], b[nb], acc[m][nb]);
             }
         }
     };
 
-    // Double-buffered: group g's activation tile and weights are requested one
-    // group ahead; at the top of each step this wave's copies of group g have
-    // landed (vmcnt 0) and the barrier makes every wave's copies visible.
-    WStage w0, w1;
-    fill(lds_a0, 0);
-    load_w(w0, 0);
+    // Pipeline: at step g the activation tile of group g + 1 is copied into the
+    // other LDS buffer and its weights are requested while group g is
+    // multiplied.  At the top of a step this wave waits for its requests (vmcnt
+    // 0) and the barrier makes every wave's LDS copies visible and frees the
+    // buffer the next copies refill.  The second workgroup on the CU computes
+    // while this one waits.
+    WStage wst[2];
+    fill(lds_a[0], 0);
+    load_w(wst[0], 0);
     for (int g = 0; g < G; g += 2) {
-        __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
-        __syncthreads();
-        fill(lds_a1, g + 1);
-        load_w(w1, g + 1);
-        compute(w0, lds_a0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        fill(lds_a0, g + 2);
-        load_w(w0, g + 2);
-        compute(w1, lds_a1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (g + u >= G) break;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            fill(lds_a[(u + 1) & 1], g + u + 1);
+            load_w(wst[(u + 1) & 1], g + u + 1);
+            compute(wst[u], lds_a[u]);
+        }
     }
+    // the copies requested past the last group (out of range, zero-filled)
+    // must land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue: row factor 2^e, SiLU(gate) * up or the plain output ----
 #pragma unroll
