@@ -136,19 +136,19 @@ def moe_shared(seed: int, layer: int, H: int, I: int, scale_lo: float, scale_hi:
 
 # ---- the five workloads --------------------------------------------------------
 
-#: c0: one GEMV, fp32 activations and output
+#: one small GEMV, fp32 activations and output
 GEMV_SMALL = dict(name="gemv_k256_n128_f32", T=1, K=256, N=128, scale=(0.005, 0.02), seed=0)
-#: c1: Llama-7B-shaped decode linear stack (T=1), bf16 in/out
+#: Llama-7B-shaped decode linear stack (T=1), bf16 in/out
 LLAMA7B_STACK = dict(name="llama7b_decode_stack_t1", T=1, seed=1, scale=(0.005, 0.02),
                      linears=[("qkv", 4096, 12288, None), ("o", 4096, 4096, None),
                               ("gate_up", 4096, 2 * 11008, "silu_mul"), ("down", 11008, 4096, None)])
-#: c2: skinny decode GEMM sweep
+#: skinny decode GEMM sweep
 SKINNY_SWEEP = dict(name="skinny_decode_sweep", seed=2, scale=(0.002, 0.01), x_scale=0.5,
                     shapes=[(5120, 13824), (13824, 5120)], T=[1, 4, 8, 16, 32])
-#: c3: DeepSeek-V3-shaped MoE expert FFN, decode
+#: DeepSeek-V3-shaped MoE expert FFN, decode
 MOE_DECODE = dict(name="moe_deepseekv3_shape_decode", seed=3, H=7168, I=2048, E=256, top_k=8,
                   shared=1, scale=(0.005, 0.02), T=[1, 8, 32])
-#: c4: same MoE layer at prefill size with Zipf(1.1)-skewed routing
+#: the same MoE layer at prefill size with Zipf(1.1)-skewed routing
 MOE_PREFILL = dict(name="moe_deepseekv3_shape_prefill", seed=4, H=7168, I=2048, E=256, top_k=8,
                    shared=1, scale=(0.005, 0.02), T=2048, zipf=1.1)
 
