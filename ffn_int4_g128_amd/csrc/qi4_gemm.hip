@@ -81,7 +81,7 @@ qgemm_kernel(const GemmArgs args) {
     __shared__ float red[kRedSlots * 256];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int W = blockDim.x >> 6;
     const int r16 = lane & 15;   // operand row / output column within the tile
     const int j = lane >> 4;     // k quarter of the operand, row block of the result
@@ -119,16 +119,10 @@ qgemm_kernel(const GemmArgs args) {
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)L.bytes);
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(args.a, (uint32_t)args.a_bytes);
 
-    // per-tile byte offsets of group 0 (or an out-of-range offset for padding tiles)
-    uint32_t cbase[NB], sbase[NB], zbase[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t tile = tile0 + nb;
-        const bool ok = tile < nt;
-        cbase[nb] = ok ? (uint32_t)((tile * G * 64 + lane) * 16) : kOob;
-        sbase[nb] = ok ? (uint32_t)(L.scales_off + (tile * G * 16 + r16) * 2) : kOob;
-        zbase[nb] = ok ? (uint32_t)(L.zeros_off + tile * G * 8 + (r16 >> 1)) : kOob;
-    }
+    // Weight offsets: the lane part is the same for every tile and group; the
+    // tile and group part is wave-uniform and goes in soffset.
+    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 2u, vz = (uint32_t)(r16 >> 1);
+    const int nt_here = (int)(nt - tile0 < NB ? (nt - tile0 > 0 ? nt - tile0 : 0) : NB);
     const int zshift = 4 * (r16 & 1);
 
     const int gb = (int)((G * wave) / W), ge = (int)((G * (wave + 1)) / W);
@@ -160,18 +154,20 @@ qgemm_kernel(const GemmArgs args) {
             abase[m] = kOob;
             apart[m] = 0;
         }
-        // The lane offsets (cbase, sbase, zbase, abase) are loop-invariant; the
-        // group offset is the same for the whole wave and goes in soffset.
+        // The activation lane offsets (abase) are loop-invariant; the group
+        // offset is the same for the whole wave and goes in soffset.
         auto load_w = [&](Stage<NB, MT, AF32> &q, int g) {
             const bool in = g < ge;
-            const uint32_t gg = (uint32_t)g;
-            const uint32_t oc = in ? gg * 1024u : kOobS, os = in ? gg * 32u : kOobS,
-                           oz = in ? gg * 8u : kOobS;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                q.cw[nb] = buf_b128(wr, cbase[nb], oc);
-                q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, sbase[nb], os, 0);
-                q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, zbase[nb], oz, 0);
+                const bool ok = in && nb < nt_here;
+                const int64_t tg = (tile0 + nb) * G + g;
+                const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
+                const uint32_t os = ok ? (uint32_t)(L.scales_off + tg * 32) : kOobS;
+                const uint32_t oz = ok ? (uint32_t)(L.zeros_off + tg * 8) : kOobS;
+                q.cw[nb] = buf_b128(wr, vc, oc);
+                q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, vs, os, 0);
+                q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, vz, oz, 0);
             }
         };
         auto load_a = [&](Stage<NB, MT, AF32> &q, int g) {
@@ -342,7 +338,8 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 //  * W waves split K; about ten 128-wide groups per wave for a single matrix,
 //    and two waves per workgroup when many expert problems already fill the chip;
 //  * NB = 2 tiles per workgroup (the gate/up pair) unless a single small matrix
-//    needs more workgroups (NB = 1);
+//    needs more workgroups (NB = 1); grouped gate/up GEMMs take NB = 4, with
+//    four waves when the grid is small;
 //  * one M tile per pass (16 activation rows), two for a single matrix with
 //    more rows.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t st) {
@@ -358,7 +355,10 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     int NB = (silu || ceil_div(nt, 2) * n_problems >= 1024) ? 2 : 1;
     int W;
     if (n_problems > 1) {
-        W = 2;
+        // grouped expert GEMMs: the gate/up pairs stream best four tiles per
+        // workgroup, split over more waves when the grid is small
+        if (silu) NB = 4;
+        W = (silu && ceil_div(nt, NB) * n_problems < 8192) ? 4 : 2;
     } else {
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
@@ -369,6 +369,7 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     dim3 grid((unsigned)gx, (unsigned)n_problems);
     const int threads = W * 64;
     if (MT == 1) {
+        if (NB == 4) return launch_cfg<4, 1, 2>(args, grid, threads, st);
         if (NB == 2) return launch_cfg<2, 1, 2>(args, grid, threads, st);
         return launch_cfg<1, 1, 2>(args, grid, threads, st);
     }
