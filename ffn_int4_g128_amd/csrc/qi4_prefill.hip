@@ -129,7 +129,7 @@ prefill_kernel(const PrefillArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kABytes];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r16 = lane & 15, j = lane >> 4;
 
     const int tix = blockIdx.y;
