@@ -246,8 +246,16 @@ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 // LDS-staged activation tiles); smaller ones the weight-streaming decode GEMM.
 constexpr int64_t kPrefillMinT = 128;
 
+// Capacity of the prefill deferred list: the larger of the two projections.
+int64_t prefill_deferred_capacity(const qi4_moe_desc *d, const PrefillTiles &mt) {
+    const int64_t a = prefill_max_deferred(2 * d->inter, QI4_PACK_GATEUP, mt);
+    const int64_t b = prefill_max_deferred(d->hidden, 0, mt);
+    return a > b ? a : b;
+}
+
 struct MoeWorkspace {
-    int64_t ids, wts, sorted, offsets, p2s, active, h, y, x16, ex, h16, eh, tiles, ntiles, total;
+    int64_t ids, wts, sorted, offsets, p2s, active, h, y, x16, ex, h16, eh, tiles, ntiles, deferred,
+        total;
     MoeWorkspace(const qi4_moe_desc *d, int64_t T) {
         const int64_t P = T * d->top_k;
         const int64_t R = P + (d->has_shared ? T : 0);
@@ -266,8 +274,10 @@ struct MoeWorkspace {
         ex = o;      o += pf ? align256(T * 4) : 0;
         h16 = o;     o += pf ? align256(R * d->inter * 2) : 0;
         eh = o;      o += pf ? align256(R * 4) : 0;
-        tiles = o;   o += pf ? align256(prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared) * 8) : 0;
+        const PrefillTiles mt = prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared);
+        tiles = o;   o += pf ? align256((mt.big + 3 * mt.small) * 8) : 0;
         ntiles = o;  o += pf ? 256 : 0;
+        deferred = o; o += pf ? align256(prefill_deferred_capacity(d, mt) * 16) : 0;
         total = o;
     }
 };
@@ -362,8 +372,14 @@ GemmArgs down_args(const qi4_moe_desc *d, const void *h, int64_t T, const int32_
 PrefillArgs prefill_args(const qi4_moe_desc *d, int64_t T, bool gate_up, const int32_t *sorted,
                          const int32_t *offsets, const int32_t *active, const void *w,
                          const void *w_shared, const uint16_t *a16, const int32_t *aexp,
-                         const int2 *tiles, const int32_t *ntiles, void *out) {
+                         const int2 *tiles, const int32_t *ntiles, int4 *deferred, void *out) {
     PrefillArgs a = {};
+    const PrefillTiles mt = prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared);
+    a.max_big = mt.big;
+    a.max_small = mt.small;
+    a.deferred = deferred;
+    a.deferred_count = const_cast<int32_t *>(ntiles) + 4;
+    a.max_deferred = prefill_deferred_capacity(d, mt);
     const int64_t H = d->hidden, I = d->inter;
     a.w = static_cast<const uint8_t *>(w);
     a.w_shared = static_cast<const uint8_t *>(w_shared);
@@ -405,9 +421,11 @@ int run_gate_up(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *
     int2 *tiles = reinterpret_cast<int2 *>(ws + L.tiles);
     int32_t *nt = reinterpret_cast<int32_t *>(ws + L.ntiles);
     if ((rc = launch_prep_rows(x, 0, T, d->hidden, x16, ex, st))) return rc;
-    if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, nt, st))) return rc;
-    PrefillArgs a = prefill_args(d, T, true, sorted, offsets, active, w_gu, sh_gu, x16, ex, tiles, nt, h);
-    return launch_prefill(a, prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared), st);
+    int4 *def = reinterpret_cast<int4 *>(ws + L.deferred);
+    PrefillArgs a = prefill_args(d, T, true, sorted, offsets, active, w_gu, sh_gu, x16, ex, tiles, nt, def, h);
+    if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, {a.max_big, a.max_small}, nt, st)))
+        return rc;
+    return launch_prefill(a, st);
 }
 
 int run_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *offsets,
@@ -425,9 +443,11 @@ int run_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *off
     int2 *tiles = reinterpret_cast<int2 *>(ws + L.tiles);
     int32_t *nt = reinterpret_cast<int32_t *>(ws + L.ntiles);
     if ((rc = launch_prep_rows(h, 1, R, d->inter, h16, eh, st))) return rc;
-    if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, nt, st))) return rc;
-    PrefillArgs a = prefill_args(d, T, false, nullptr, offsets, active, w_dn, sh_dn, h16, eh, tiles, nt, y);
-    return launch_prefill(a, prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared), st);
+    int4 *def = reinterpret_cast<int4 *>(ws + L.deferred);
+    PrefillArgs a = prefill_args(d, T, false, nullptr, offsets, active, w_dn, sh_dn, h16, eh, tiles, nt, def, y);
+    if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, {a.max_big, a.max_small}, nt, st)))
+        return rc;
+    return launch_prefill(a, st);
 }
 
 int launch_combine(const qi4_moe_desc *d, const float *y, const float *wts, const int32_t *p2s,

@@ -5,19 +5,28 @@
 // than a weight stream.  The design:
 //  * activations are converted once per row to fp16 with an exact power-of-two
 //    prescale (value = fp16 * 2^e, |fp16| < 2^14), so the contraction runs on
-//    fp16 MFMA and the row factor 2^e is applied once in the epilogue;
-//  * each wave dequantizes its own 64 weight rows per 128-wide group straight
-//    into fp16 MFMA operands: (1024 + q) - (1024 + zero) with packed fp16 adds
-//    (exact), times the binary16 scale (one rounding, relative error <= 2^-11),
-//    so no per-group epilogue remains;
-//  * a workgroup is 4 waves x 64 weight rows and 128 activation rows; the
-//    activation tile of each group (32 KB) is copied from memory straight into
-//    LDS (buffer loads with the LDS bit) in the exact order the MFMA operand
-//    reads want, double-buffered, and shared by the 4 waves; two workgroups
-//    share a CU so one computes while the other waits at its barrier;
-//  * a device-side tile list (expert, first row) built from the expert
-//    segments covers every routed expert plus the shared one, so load follows
-//    the routing skew without a host round trip.
+//    fp16 MFMA and the row factor 2^e is applied once in the epilogue; the
+//    columns k = 2, 3, 6, 7 (mod 8) carry a further exact 2^-4;
+//  * each wave dequantizes its own weight rows per 128-wide group straight
+//    into fp16 MFMA operands, 16 (q - zero) scale for the columns above and
+//    (q - zero) scale for the others (exact integer part, one rounding of the
+//    product, relative error <= 2^-11), so no per-group epilogue remains;
+//  * a device-side planner splits every expert's rows (and the shared
+//    expert's) into big tiles of up to 128 rows and at most one small tile of
+//    up to 16, 32 or 64 rows.  Big tiles run on MFMA-bound workgroups (4 waves
+//    x 64 weight rows, two-stage pipeline, two workgroups per CU); small tiles
+//    run on weight-stream-bound workgroups (8 waves x 32 weight rows,
+//    four-stage pipeline, 16 waves per CU), on a side stream so that the two
+//    kinds share the chip;
+//  * the activation tile of each group is copied from memory straight into LDS
+//    (buffer loads with the LDS bit), each 4-lane quad reading 64 contiguous
+//    bytes, in a rotated order that keeps the MFMA operand reads free of bank
+//    conflicts, and shared by all waves of the workgroup;
+//  * a workgroup whose weights hold a scale the 16x operands cannot represent
+//    (|scale| >= 256, inf, NaN) hands its tile to a pass with plain operands.
+#include <mutex>
+#include <type_traits>
+
 #include "qi4_gemm.h"
 #include "qi4_host.h"
 #include "qi4_prefill.h"
@@ -42,7 +51,8 @@ __device__ inline f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
 }
 
 // fp16 operands scale * (q - zero) of the 8 codes in one packed dword, in the
-// element order of the packed layout (see qi4_dev.h).
+// element order of the packed layout (see qi4_dev.h): (1024 + q) - (1024 + zero)
+// with packed fp16 adds (exact), times the binary16 scale (one rounding).
 __device__ inline uint4 dequant_f16(uint32_t d, uint32_t negz, uint32_t s2) {
     const uint32_t m = 0x000F000Fu, magic = 0x64006400u;   // fp16 1024 + q
     const f16x2 nz = __builtin_bit_cast(f16x2, negz), sc = __builtin_bit_cast(f16x2, s2);
@@ -51,6 +61,33 @@ __device__ inline uint4 dequant_f16(uint32_t d, uint32_t negz, uint32_t s2) {
     r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, ((d >> 4) & m) | magic) + nz) * sc);
     r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, ((d >> 8) & m) | magic) + nz) * sc);
     r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, ((d >> 12) & m) | magic) + nz) * sc);
+    return r;
+}
+
+// (a & m) | c in one VALU instruction (m in a scalar register, c in a vector
+// register: a three-operand VALU op takes no literal here).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
+
+// The same operands with elements 2, 3, 6 and 7 sixteen times larger: their
+// codes sit at bits 4..7 of each half, so masking them in place gives
+// 1024 + 16q and (1024 + 16q) - (1024 + 16 zero) = 16 (q - zero), exactly.
+// Activations at k = 2, 3, 6, 7 (mod 8) are stored divided by 16, so the
+// products are unchanged.  One shift, four and-or, four adds, four multiplies
+// per 8 codes.  magic holds fp16 1024 in both halves.
+__device__ inline uint4 dequant_f16_x16(uint32_t d, uint32_t negz, uint32_t negz16, uint32_t s2,
+                                        uint32_t magic) {
+    const f16x2 nz = __builtin_bit_cast(f16x2, negz), nz16 = __builtin_bit_cast(f16x2, negz16);
+    const f16x2 sc = __builtin_bit_cast(f16x2, s2);
+    const uint32_t t = d >> 8;
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, and_or(d, 0x000F000Fu, magic)) + nz) * sc);
+    r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, and_or(d, 0x00F000F0u, magic)) + nz16) * sc);
+    r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, and_or(t, 0x000F000Fu, magic)) + nz) * sc);
+    r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, and_or(t, 0x00F000F0u, magic)) + nz16) * sc);
     return r;
 }
 
@@ -77,7 +114,8 @@ prep_rows_kernel(const uint16_t *__restrict__ src, int src_kind, int64_t len,
     if (mx > 0.f) frexpf(mx, &E);          // mx in [2^(E-1), 2^E)
     const int sh = mx > 0.f ? 14 - E : 0;  // |v * 2^sh| < 2^14
     for (int64_t i = threadIdx.x; i < len; i += 256) {
-        const _Float16 h = (_Float16)ldexpf(value(i), sh);
+        // k = 2, 3, 6, 7 (mod 8) carry an extra 2^-4 (the weights there are 16x)
+        const _Float16 h = (_Float16)ldexpf(value(i), (i & 2) ? sh - 4 : sh);
         dst[row * len + i] = __builtin_bit_cast(uint16_t, h);
     }
     if (threadIdx.x == 0) exps[row] = -sh;
@@ -85,56 +123,358 @@ prep_rows_kernel(const uint16_t *__restrict__ src, int src_kind, int64_t len,
 
 // ---- tile planner ---------------------------------------------------------------
 
-// One entry (problem, first slot) per 128-row tile of every nonempty routed
-// expert (problem = index into the active list) and of the shared expert
-// (problem = -1).  Single workgroup.
+// Tiles of a problem (routed expert or the shared one) with n rows: n / 128 big
+// tiles of 128 rows, then the remaining n % 128 rows as one more big tile if
+// there are more than 64 of them, else as one small tile of at most 16, 32 or
+// 64 rows (classes 0, 1, 2).  Big tiles are bound by the MFMAs, small ones by
+// the weight stream; each list has its own kernel.  Entry: (problem, first
+// slot), problem -1 for the shared expert.  counts: [0] big, [1 + c] small of
+// class c, [4] deferred pairs (zeroed here).  Single workgroup; each thread
+// owns two problems.
+__device__ inline int small_class(int64_t rows) { return rows <= 16 ? 0 : rows <= 32 ? 1 : 2; }
+
 __global__ void __launch_bounds__(1024)
 plan_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ active, int64_t T,
-            int has_shared, int2 *__restrict__ tiles, int32_t *__restrict__ count) {
-    __shared__ int scan[1024];
+            int has_shared, int2 *__restrict__ big, int2 *__restrict__ small, int64_t small_cap,
+            int32_t *__restrict__ counts) {
+    __shared__ int sc[4][1024];   // [0] big, [1..3] small classes
     const int n_act = active[0];
+    const int n_prob = n_act + (has_shared ? 1 : 0);
     const int i = threadIdx.x;
-    int mt = 0;
-    if (i < n_act) {
-        const int e = active[1 + i];
-        mt = (offsets[e + 1] - offsets[e] + kPrefillBM - 1) / kPrefillBM;
+    auto rows = [&](int p) -> int64_t {
+        if (p < n_act) {
+            const int e = active[1 + p];
+            return offsets[e + 1] - offsets[e];
+        }
+        return T;
+    };
+    int mine[4] = {0, 0, 0, 0};
+    for (int q = 0; q < 2; ++q) {
+        const int p = 2 * i + q;
+        if (p >= n_prob) break;
+        const int64_t n = rows(p), rem = n % kPrefillBM;
+        mine[0] += (int)(n / kPrefillBM) + (rem > kPrefillBMSmall ? 1 : 0);
+        if (rem > 0 && rem <= kPrefillBMSmall) mine[1 + small_class(rem)] += 1;
     }
-    scan[i] = mt;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sc[c][i] = mine[c];
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
-        const int v = i >= d ? scan[i - d] : 0;
+        int v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = i >= d ? sc[c][i - d] : 0;
         __syncthreads();
-        scan[i] += v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sc[c][i] += v[c];
         __syncthreads();
     }
-    const int base = scan[i] - mt;
-    for (int k = 0; k < mt; ++k) tiles[base + k] = make_int2(i, k * kPrefillBM);
-    const int total = scan[1023];
-    const int sh_tiles = has_shared ? (int)((T + kPrefillBM - 1) / kPrefillBM) : 0;
-    for (int k = i; k < sh_tiles; k += 1024) tiles[total + k] = make_int2(-1, k * kPrefillBM);
-    if (i == 0) *count = total + sh_tiles;
+    int pos[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pos[c] = sc[c][i] - mine[c];
+    for (int q = 0; q < 2; ++q) {
+        const int p = 2 * i + q;
+        if (p >= n_prob) break;
+        const int64_t n = rows(p), full = n / kPrefillBM, rem = n % kPrefillBM;
+        const int pid = p < n_act ? p : -1;
+        for (int64_t k = 0; k < full; ++k) big[pos[0]++] = make_int2(pid, (int)(k * kPrefillBM));
+        if (rem > kPrefillBMSmall) {
+            big[pos[0]++] = make_int2(pid, (int)(full * kPrefillBM));
+        } else if (rem > 0) {
+            const int c = small_class(rem);
+            small[c * small_cap + pos[1 + c]++] = make_int2(pid, (int)(full * kPrefillBM));
+        }
+    }
+    if (i == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) counts[c] = sc[c][1023];
+        counts[4] = 0;
+    }
 }
 
 // ---- the grouped GEMM ----------------------------------------------------------------
 
-constexpr int kWaves = 4;
-constexpr int kNB = 4;                         // 16-row weight tiles per wave
-constexpr int kMS = kPrefillBM / 16;           // 16-row activation subtiles per workgroup
-constexpr int kABlock = 1024;                  // one MFMA operand fragment of a wave
-constexpr int kABytes = kMS * 4 * kABlock;     // activation tile of one group: 32 KB
+constexpr int kABlock = 1024;          // one MFMA operand fragment of a wave (16 rows x 32 k, fp16)
+constexpr int kRowsPerWG = 256;        // weight rows (16 tiles) of one workgroup
 
-template <int EPI>
-__global__ void __launch_bounds__(kWaves * 64, 2)
-prefill_kernel(const PrefillArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kABytes];
+// Shapes of the two kernels.  Big tiles: 128 activation rows, 4 waves of 64
+// weight rows, 2 pipeline stages, two workgroups per CU (256 registers a wave).
+// Small tiles: 64 activation rows, 8 waves of 32 weight rows, 4 stages (three
+// groups of requests in flight), 128 registers a wave so that 16 waves share a CU.
+template <int MS_, int NBW_, int W_, int S_, int OCC_>
+struct Shape {
+    static constexpr int MS = MS_;     // 16-row activation subtiles per tile
+    static constexpr int NBW = NBW_;   // 16-row weight tiles per wave
+    static constexpr int W = W_;       // waves per workgroup
+    static constexpr int S = S_;       // pipeline stages
+    static constexpr int OCC = OCC_;   // waves per SIMD the register budget allows
+    static constexpr int kStageBytes = MS * 4 * kABlock;
+    static constexpr int FPW = MS * 4 / W;   // operand fragments each wave copies per group
+    static constexpr int NH = FPW >= 4 ? FPW / 4 : 1;   // distinct subtiles each wave copies
+    static constexpr int kReqs = FPW + 3 * NBW;   // memory requests per group per wave
+    static_assert(W * NBW * 16 == kRowsPerWG, "workgroup rows");
+    static constexpr int kLds = S * kStageBytes;   // LDS of one workgroup
+    static_assert(kLds <= 160 * 1024, "LDS stages");
+    static_assert(FPW >= 1 && (FPW >= 4 ? FPW % 4 == 0 : 4 % FPW == 0), "copy split");
+};
+using BigShape = Shape<8, 4, 4, 2, 2>;
+using SmallShape = Shape<4, 2, 8, 4, 4>;
 
+// s_waitcnt operand that waits until at most `vm` vector memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// One tile: SH::MS 16-row activation subtiles times this workgroup's 256
+// weight rows, over the whole K.
+template <int EPI, class SH, int MU, bool WIDE>
+__device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLayout &L, uint8_t *lds,
+                                         int *wg_flag, int2 te, const uint8_t *w, int64_t row0,
+                                         int64_t n, int64_t src0, const int32_t *gather, int64_t bx,
+                                         int wave, int lane) {
+    const int64_t m0 = te.y;
+    constexpr int MS = SH::MS, NBW = SH::NBW, S = SH::S, FPW = SH::FPW, NH = SH::NH;
+    const int r16 = lane & 15, j = lane >> 4;
+    const int64_t nt = L.nt, G = L.G;
+    const int64_t tile0 = bx * (kRowsPerWG / 16) + wave * NBW;
+    const __amdgpu_buffer_rsrc_t wr = rsrc(w, (uint32_t)L.bytes);
+    const __amdgpu_buffer_rsrc_t ar = rsrc(args.a16, (uint32_t)(args.a_rows * args.K * 2));
+
+    // Weight offsets: the lane part is the same for every tile and group; the
+    // tile and group part is wave-uniform and goes in soffset (scalar registers).
+    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 2u, vz = (uint32_t)(r16 >> 1);
+    const int nt_here = (int)(nt - tile0 < NBW ? (nt - tile0 > 0 ? nt - tile0 : 0) : NBW);
+    const int zshift = 4 * (r16 & 1);
+
+    // 16-row subtiles of this tile that hold rows (uniform).
+    const int m_used = (int)((n - m0 + 15) / 16 < MS ? (n - m0 + 15) / 16 : MS);
+
+    // Operand fragments this wave copies into LDS each group: fragment
+    // f = FPW * wave + i is k step f % 4 of subtile f / 4 (16 rows x 64 bytes).
+    // A copy request moves 16 bytes per lane to LDS at 16 * lane.  Lane l
+    // copies row l / 4 of the fragment, so every 4 consecutive lanes read 64
+    // contiguous bytes (the address unit coalesces them); inside the quad the
+    // four 16-byte chunks are rotated by rot(row), which makes the MFMA operand
+    // reads below hit distinct LDS banks in every 8- or 16-lane phase.
+    auto rot = [](int r) { return ((r >> 1) + (r >> 3)) & 3; };
+    auto frag_sub = [&](int i) { return (FPW * wave + i) >> 2; };
+    auto frag_k = [&](int i) { return (FPW * wave + i) & 3; };
+    const int crow = lane >> 2, cchunk = ((lane & 3) - rot(lane >> 2)) & 3;
+    uint32_t aoff[NH];   // byte offset of this lane's activation chunk, per copied subtile
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const int64_t slot = m0 + 16 * frag_sub(4 * h) + crow;
+        const bool ok = slot < n;
+        const int64_t slot_c = ok ? slot : 0;
+        const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
+        aoff[h] = ok ? (uint32_t)((src * args.K + 8 * cchunk) * 2) : kOob;
+    }
+    // MFMA operand lane (row r16, chunk j) finds its chunk at this LDS offset
+    const uint32_t rdoff = 16u * (uint32_t)(4 * r16 + ((j + rot(r16)) & 3));
+
+    // Past the last group every lane loads from an out-of-range offset (a
+    // select, not a sum, so an invalid row's offset cannot wrap around), which
+    // fills zeros.  Big tiles skip the copies of empty subtiles (they wait for
+    // all requests); small tiles issue every copy (rows past the end are
+    // zero-filled, without a memory access) so that each group costs each
+    // wave exactly kReqs requests.
+    auto fill = [&](int stage, int g) {
+        const bool in = g < G;
+        const uint32_t so = in ? (uint32_t)g * 256u : 0u;
+        uint8_t *buf = lds + stage * SH::kStageBytes;
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) {
+            if (S == 2 && frag_sub(i) >= m_used) continue;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ar, (__attribute__((address_space(3))) void *)(buf + (FPW * wave + i) * kABlock), 16,
+                in ? aoff[i / 4 < NH ? i / 4 : 0] + 64u * (uint32_t)frag_k(i) : kOob, so, 0, 0);
+        }
+    };
+    struct WStage {
+        uint4 cw[NBW];
+        uint32_t sc[NBW], zb[NBW];
+    };
+    auto load_w = [&](WStage &q, int g) {
+        const bool in = g < G;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const bool ok = in && nb < nt_here;
+            const int64_t tg = (tile0 + nb) * G + g;
+            const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
+            const uint32_t os = ok ? (uint32_t)(L.scales_off + tg * 32) : kOobS;
+            const uint32_t oz = ok ? (uint32_t)(L.zeros_off + tg * 8) : kOobS;
+            q.cw[nb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, vc, oc, 0));
+            q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, vs, os, 0);
+            q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, vz, oz, 0);
+        }
+    };
+
+    f32x4 acc[MS][NBW];
+#pragma unroll
+    for (int m = 0; m < MS; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // 16 (q - zero) scale can exceed binary16 once |scale| >= 256.  On the fast
+    // pass each wave scans the scales of its tiles (contiguous: nt_here * G * 32
+    // bytes) while the prologue's requests are in flight; a workgroup that
+    // finds such a scale (or inf/NaN) records its tile in the deferred list and
+    // leaves it to the plain-operand pass.
+    bool big = false;
+    if constexpr (!WIDE) {
+        const uint32_t span = (uint32_t)(nt_here * G * kScaleBytes);
+        const uint32_t base = (uint32_t)(L.scales_off + tile0 * G * kScaleBytes);
+        for (uint32_t o = 0; o < span; o += 1024) {
+            const uint32_t lo = o + (uint32_t)lane * 16u;
+            const uint4 v = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, lo < span ? lo : kOob, base, 0));
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                big |= (u[c] & 0x7C00u) >= 0x5C00u || (u[c] & 0x7C000000u) >= 0x5C000000u;
+        }
+    }
+
+    // Prologue: the first S - 1 groups' activation tiles and weights.
+    WStage wst[S];
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) {
+        fill(q, q);
+        load_w(wst[q], q);
+    }
+
+    if constexpr (!WIDE) {
+        if (threadIdx.x == 0) *wg_flag = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(big) != 0 && lane == 0) *wg_flag = 1;
+        __syncthreads();
+        if (*wg_flag) {
+            if (threadIdx.x == 0) {
+                const int slot = atomicAdd(args.deferred_count, 1);
+                args.deferred[slot] = make_int4(te.x, te.y, (int)bx, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // the prologue's LDS copies land before exit
+            return;
+        }
+    }
+
+    // magic (fp16 1024 in both halves) is produced opaquely so that it stays in
+    // one vector register instead of being rematerialized at every use.
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+    // The main loop multiplies the first MU subtiles (MU * 16 >= the tile's
+    // rows; rows past its end only feed output rows that are never stored), so
+    // its body has no branches.
+    {
+        static_assert(MU >= 1 && MU <= MS, "subtiles");
+        auto compute = [&](const WStage &q, int stage) {
+            const uint8_t *buf = lds + stage * SH::kStageBytes;
+            uint32_t negz[NBW], negz16[NBW], s2[NBW];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const uint32_t z = (q.zb[nb] >> zshift) & 15u;
+                // fp16 -(1024 + z) and -(1024 + 16 z) in both halves; scale in both halves
+                negz[nb] = (0xE400u | z) * 0x00010001u;
+                negz16[nb] = (0xE400u | (z << 4)) * 0x00010001u;
+                s2[nb] = (q.sc[nb] & 0xFFFFu) * 0x00010001u;
+            }
+            auto deq = [&](int s, f16x8 (&b)[NBW]) {
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const uint32_t d = s == 0 ? q.cw[nb].x : s == 1 ? q.cw[nb].y : s == 2 ? q.cw[nb].z : q.cw[nb].w;
+                    if constexpr (WIDE)
+                        b[nb] = __builtin_bit_cast(f16x8, dequant_f16(d, negz[nb], s2[nb]));
+                    else
+                        b[nb] = __builtin_bit_cast(f16x8, dequant_f16_x16(d, negz[nb], negz16[nb], s2[nb], magic));
+                }
+            };
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                f16x8 b[NBW];
+                deq(s, b);
+#pragma unroll
+                for (int m = 0; m < MU; ++m) {
+                    f16x8 a = *reinterpret_cast<const f16x8 *>(buf + (m * 4 + s) * kABlock + rdoff);
+                    if constexpr (WIDE) {
+                        // the activations at k = 2, 3, 6, 7 (mod 8) are stored / 16
+                        const f16x8 x16 = {1, 1, 16, 16, 1, 1, 16, 16};
+                        a = a * x16;
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) acc[m][nb] = mfma16x16x32_f16(a, b[nb], acc[m][nb]);
+                }
+                // nothing moves across k steps: bounds the registers in flight
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // Pipeline: at step g the activation tile and the weights of group
+        // g + S - 1 are requested into the stage that group g - 1 used, while
+        // group g is multiplied.  At the top of a step this wave waits until
+        // group g's requests have landed (the requests issued after them are
+        // those of the S - 2 groups that follow, kReqs each; with two stages,
+        // none), then the barrier makes every wave's LDS copies of group g
+        // visible and frees the stage of group g - 1.
+        for (int g = 0; g < G; g += S) {
+#pragma unroll
+            for (int u = 0; u < S; ++u) {
+                if (g + u >= G) break;
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(SH::kReqs * (S - 2)));
+                __syncthreads();
+                const int nxt = (u + S - 1) % S;   // constant once unrolled
+                fill(nxt, g + u + S - 1);
+                load_w(wst[nxt], g + u + S - 1);
+                compute(wst[u], u);
+            }
+        }
+    }
+    // the copies requested past the last group (out of range, zero-filled)
+    // must land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- epilogue: row factor 2^e, SiLU(gate) * up or the plain output ----
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t slot = m0 + 16 * m + 4 * j + v;
+            if (slot >= n) continue;
+            const int64_t src = gather ? (int64_t)(gather[row0 + slot] / args.top_k) : src0 + slot;
+            const int e = args.a_exp[src];
+            const int64_t dst = row0 + slot;
+            if constexpr (EPI == QI4_EPI_SILU_MUL) {
+#pragma unroll
+                for (int p = 0; p < NBW / 2; ++p) {
+                    const int64_t tile = tile0 + 2 * p;
+                    const int64_t oc = (tile >> 1) * 16 + r16;
+                    if (tile >= nt || oc >= args.n_out) continue;
+                    const float gv = ldexpf(acc[m][2 * p][v], e), uv = ldexpf(acc[m][2 * p + 1][v], e);
+                    const float hv = gv / (1.0f + expf(-gv)) * uv;
+                    const uint32_t hi = f32_to_bf16_rne(hv);
+                    const uint32_t lo = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+                    uint16_t *o = static_cast<uint16_t *>(args.out);
+                    o[(dst * 2) * args.ldo + oc] = (uint16_t)hi;
+                    o[(dst * 2 + 1) * args.ldo + oc] = (uint16_t)lo;
+                }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const int64_t tile = tile0 + nb;
+                    if (tile >= nt) continue;
+                    const int64_t oc = tile_row(tile, r16, args.N, args.flags);
+                    if (oc < 0 || oc >= args.n_out) continue;
+                    static_cast<float *>(args.out)[dst * args.ldo + oc] = ldexpf(acc[m][nb][v], e);
+                }
+            }
+        }
+    }
+}
+
+// Tile list entry -> problem, then run_tile.
+template <int EPI, class SH, int MU, bool WIDE>
+__device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int64_t bx, uint8_t *lds,
+                                           int *wg_flag) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int r16 = lane & 15, j = lane >> 4;
-
-    const int tix = blockIdx.y;
-    if (tix >= *args.tile_count) return;
-    const int2 te = args.tiles[tix];
+    const PackedLayout L(args.N, args.K, args.flags);
     const uint8_t *w;
     int64_t row0, n, src0 = 0;
     const int32_t *gather = nullptr;
@@ -151,169 +491,49 @@ prefill_kernel(const PrefillArgs args) {
         n = args.T;
         src0 = args.gather_tokens ? 0 : row0;
     }
-    const int64_t m0 = te.y;
+    run_tile<EPI, SH, MU, WIDE>(args, L, lds, wg_flag, te, w, row0, n, src0, gather, bx, wave, lane);
+}
 
-    const PackedLayout L(args.N, args.K, args.flags);
-    const int64_t nt = L.nt, G = L.G;
-    const int64_t tile0 = (int64_t)blockIdx.x * (kWaves * kNB) + wave * kNB;
-    const __amdgpu_buffer_rsrc_t wr = rsrc(w, (uint32_t)L.bytes);
-    const __amdgpu_buffer_rsrc_t ar = rsrc(args.a16, (uint32_t)(args.a_rows * args.K * 2));
+// Workgroup ids are dealt to the 8 XCDs in turn (id mod 8): tile tix goes to
+// XCD tix mod 8 and all its column blocks run there back to back, so the
+// activation tile they share is fetched once into that XCD's L2.
+template <int EPI, class SH, int MU>
+__device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *tiles, int count) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SH::kLds];
+    __shared__ int wg_flag;
+    const int64_t nt = num_tiles(args.N, args.flags);
+    const uint32_t gx = (uint32_t)((nt * 16 + kRowsPerWG - 1) / kRowsPerWG);
+    const uint32_t kx = blockIdx.x >> 3;
+    const int tix = (int)((kx / gx) * 8 + (blockIdx.x & 7));
+    if (tix >= count) return;
+    tile_entry<EPI, SH, MU, false>(args, tiles[tix], kx % gx, lds, &wg_flag);
+}
 
-    // Weight offsets: the lane part is the same for every tile and group; the
-    // tile and group part is wave-uniform and goes in soffset (scalar registers).
-    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 2u, vz = (uint32_t)(r16 >> 1);
-    const int nt_here = (int)(nt - tile0 < kNB ? (nt - tile0 > 0 ? nt - tile0 : 0) : kNB);
-    const int zshift = 4 * (r16 & 1);
+template <int EPI>
+__global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
+prefill_big_kernel(const PrefillArgs args) {
+    fast_pass<EPI, BigShape, BigShape::MS>(args, args.tiles, args.tile_count[0]);
+}
 
-    // Activation rows this lane copies into LDS: wave w fills the operand
-    // fragments of 16-row subtiles 2w and 2w+1 (four 32-wide k steps each).
-    uint32_t aoff[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t slot = m0 + 16 * (2 * wave + h) + r16;
-        const bool ok = slot < n;
-        const int64_t slot_c = ok ? slot : 0;
-        const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
-        aoff[h] = ok ? (uint32_t)((src * args.K + 8 * j) * 2) : kOob;
-    }
+// Small tiles of class C: at most 16 << C rows, 1 << C subtiles multiplied.
+template <int EPI, int C>
+__global__ void __launch_bounds__(SmallShape::W * 64, SmallShape::OCC)
+prefill_small_kernel(const PrefillArgs args) {
+    fast_pass<EPI, SmallShape, 1 << C>(args, args.tiles + args.max_big + C * args.max_small,
+                                      args.tile_count[1 + C]);
+}
 
-    // Past the last group every lane loads from an out-of-range offset (a
-    // select, not a sum, so an invalid row's offset cannot wrap around).
-    auto fill = [&](uint8_t *buf, int g) {
-        const bool in = g < G;
-        const uint32_t so = in ? (uint32_t)g * 256u : 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int h = i >> 2, s = i & 3;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ar, (__attribute__((address_space(3))) void *)(buf + ((2 * wave + h) * 4 + s) * kABlock),
-                16, in ? aoff[h] + 64u * s : kOob, so, 0, 0);
-        }
-    };
-    struct WStage {
-        uint4 cw[kNB];
-        uint32_t sc[kNB], zb[kNB];
-    };
-    auto load_w = [&](WStage &q, int g) {
-        const bool in = g < G;
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-            const bool ok = in && nb < nt_here;
-            const int64_t tg = (tile0 + nb) * G + g;
-            const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
-            const uint32_t os = ok ? (uint32_t)(L.scales_off + tg * 32) : kOobS;
-            const uint32_t oz = ok ? (uint32_t)(L.zeros_off + tg * 8) : kOobS;
-            q.cw[nb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, vc, oc, 0));
-            q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, vs, os, 0);
-            q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, vz, oz, 0);
-        }
-    };
-
-    f32x4 acc[kMS][kNB];
-#pragma unroll
-    for (int m = 0; m < kMS; ++m)
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // 16-row activation subtiles of this tile that hold rows (uniform): the
-    // MFMAs of empty subtiles are skipped, so a small expert costs only its rows.
-    const int m_used = (int)((n - m0 + 15) / 16 < kMS ? (n - m0 + 15) / 16 : kMS);
-
-    auto compute = [&](const WStage &q, const uint8_t *buf) {
-        uint32_t negz[kNB], s2[kNB];
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-            const uint32_t z = (q.zb[nb] >> zshift) & 15u;
-            // fp16 -(1024 + z) in both halves; scale in both halves
-            const uint32_t nz = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + (float)z)));
-            negz[nb] = nz * 0x00010001u;
-            s2[nb] = (q.sc[nb] & 0xFFFFu) * 0x00010001u;
-        }
-        // Operand fragments in (k step, subtile) order through a 2-deep ring, so
-        // each LDS read is issued one MFMA batch before it is needed.
-        auto rd = [&](int i) {
-            return *reinterpret_cast<const f16x8 *>(buf + ((i & 7) * 4 + (i >> 3)) * kABlock + lane * 16);
-        };
-        f16x8 a[2];
-        a[0] = rd(0);
-        f16x8 b[kNB];
-#pragma unroll
-        for (int i = 0; i < 4 * kMS; ++i) {
-            const int s = i >> 3, m = i & 7;
-            if (m == 0) {
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
-                    const uint32_t d = s == 0 ? q.cw[nb].x : s == 1 ? q.cw[nb].y : s == 2 ? q.cw[nb].z : q.cw[nb].w;
-                    b[nb] = __builtin_bit_cast(f16x8, dequant_f16(d, negz[nb], s2[nb]));
-                }
-            }
-            if (i + 1 < 4 * kMS) a[(i + 1) & 1] = rd(i + 1);
-            if (m < m_used) {
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) acc[m][nb] = mfma16x16x32_f16(a[i & 1], b[nb], acc[m][nb]);
-            }
-        }
-    };
-
-    // Pipeline: at step g the activation tile of group g + 1 is copied into the
-    // other LDS buffer and its weights are requested while group g is
-    // multiplied.  At the top of a step this wave waits for its requests (vmcnt
-    // 0) and the barrier makes every wave's LDS copies visible and frees the
-    // buffer the next copies refill.  The second workgroup on the CU computes
-    // while this one waits.
-    WStage wst[2];
-    fill(lds_a[0], 0);
-    load_w(wst[0], 0);
-    for (int g = 0; g < G; g += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (g + u >= G) break;
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            fill(lds_a[(u + 1) & 1], g + u + 1);
-            load_w(wst[(u + 1) & 1], g + u + 1);
-            compute(wst[u], lds_a[u]);
-        }
-    }
-    // the copies requested past the last group (out of range, zero-filled)
-    // must land before the workgroup's LDS is released
-    __builtin_amdgcn_s_waitcnt(0);
-
-    // ---- epilogue: row factor 2^e, SiLU(gate) * up or the plain output ----
-#pragma unroll
-    for (int m = 0; m < kMS; ++m) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t slot = m0 + 16 * m + 4 * j + v;
-            if (slot >= n) continue;
-            const int64_t src = gather ? (int64_t)(gather[row0 + slot] / args.top_k) : src0 + slot;
-            const int e = args.a_exp[src];
-            const int64_t dst = row0 + slot;
-            if constexpr (EPI == QI4_EPI_SILU_MUL) {
-#pragma unroll
-                for (int p = 0; p < kNB / 2; ++p) {
-                    const int64_t tile = tile0 + 2 * p;
-                    const int64_t oc = (tile >> 1) * 16 + r16;
-                    if (tile >= nt || oc >= args.n_out) continue;
-                    const float gv = ldexpf(acc[m][2 * p][v], e), uv = ldexpf(acc[m][2 * p + 1][v], e);
-                    const float hv = gv / (1.0f + expf(-gv)) * uv;
-                    const uint32_t hi = f32_to_bf16_rne(hv);
-                    const uint32_t lo = f32_to_bf16_rne(hv - bf16_to_f32(hi));
-                    uint16_t *o = static_cast<uint16_t *>(args.out);
-                    o[(dst * 2) * args.ldo + oc] = (uint16_t)hi;
-                    o[(dst * 2 + 1) * args.ldo + oc] = (uint16_t)lo;
-                }
-            } else {
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
-                    const int64_t tile = tile0 + nb;
-                    if (tile >= nt) continue;
-                    const int64_t oc = tile_row(tile, r16, args.N, args.flags);
-                    if (oc < 0 || oc >= args.n_out) continue;
-                    static_cast<float *>(args.out)[dst * args.ldo + oc] = ldexpf(acc[m][nb][v], e);
-                }
-            }
-        }
+// Deferred (tile, column block) pairs, with the plain operands (big-tile shape
+// also for small tiles).  A grid-stride loop over the list.
+template <int EPI>
+__global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
+prefill_wide_kernel(const PrefillArgs args) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[BigShape::kLds];
+    const int count = *args.deferred_count;
+    for (int i = blockIdx.x; i < count; i += gridDim.x) {
+        const int4 d = args.deferred[i];
+        tile_entry<EPI, BigShape, BigShape::MS, true>(args, make_int2(d.x, d.y), d.z, lds, nullptr);
+        __syncthreads();   // LDS is reused by the next entry
     }
 }
 
@@ -329,27 +549,101 @@ int launch_prep_rows(const void *src, int src_kind, int64_t rows, int64_t len, u
 }
 
 int launch_plan(const int32_t *offsets, const int32_t *active, int64_t T, int has_shared,
-                int2 *tiles, int32_t *count, hipStream_t st) {
-    plan_kernel<<<1, 1024, 0, st>>>(offsets, active, T, has_shared, tiles, count);
+                int2 *tiles, const PrefillTiles &m, int32_t *counts, hipStream_t st) {
+    plan_kernel<<<1, 1024, 0, st>>>(offsets, active, T, has_shared, tiles, tiles + m.big, m.small,
+                                    counts);
     return launch_status();
 }
 
-int64_t prefill_max_tiles(int64_t T, int top_k, int64_t E, int has_shared) {
+PrefillTiles prefill_max_tiles(int64_t T, int top_k, int64_t E, int has_shared) {
+    // each problem of n rows has at most n / 128 + 1 tiles, at most one small
     const int64_t P = T * top_k;
     const int64_t act = P < E ? P : E;
-    return P / kPrefillBM + act + (has_shared ? (T + kPrefillBM - 1) / kPrefillBM : 0) + 1;
+    PrefillTiles m;
+    m.big = P / kPrefillBM + act + (has_shared ? T / kPrefillBM + 1 : 0);
+    m.small = act + (has_shared ? 1 : 0);
+    return m;
 }
 
-int launch_prefill(const PrefillArgs &a, int64_t max_tiles, hipStream_t st) {
-    const int64_t nt = num_tiles(a.N, a.flags);
-    const int64_t gx = ceil_div(nt, kWaves * kNB);
-    if (gx > 0x7fffffff || max_tiles > 65535) return QI4_ERR_SHAPE;
-    dim3 grid((unsigned)gx, (unsigned)max_tiles);
-    if (a.epi == QI4_EPI_SILU_MUL)
-        prefill_kernel<QI4_EPI_SILU_MUL><<<grid, kWaves * 64, 0, st>>>(a);
-    else
-        prefill_kernel<QI4_EPI_NONE><<<grid, kWaves * 64, 0, st>>>(a);
+int64_t prefill_max_deferred(int64_t N, int flags, const PrefillTiles &m) {
+    const int64_t gx = ceil_div(num_tiles(N, flags) * 16, kRowsPerWG);
+    return gx * (ceil_div(m.big, 8) + 3 * ceil_div(m.small, 8)) * 8;
+}
+
+// The small-tile kernels run on a side stream of the device, forked from and
+// joined back to the caller's stream with events, so that they share the chip
+// with the big-tile kernel (one streams weights, the other keeps the MFMAs
+// busy).  One side stream and event pair per device, created on first use and
+// kept for the life of the process; a mutex makes each fork/join sequence of
+// enqueues atomic, so calls on different streams cannot pick up each other's
+// events.
+namespace {
+struct SideStream {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+int side_stream(SideStream **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QI4_ERR_HIP;
+    SideStream &ss = g_side[dev];
+    std::lock_guard<std::mutex> lk(g_side_init);
+    if (!ss.s) {
+        hipStream_t s = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return QI4_ERR_HIP;
+        if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+            if (f) (void)hipEventDestroy(f);
+            (void)hipStreamDestroy(s);
+            return QI4_ERR_HIP;
+        }
+        ss.fork = f;
+        ss.join = j;
+        ss.s = s;
+    }
+    *out = &ss;
+    return QI4_OK;
+}
+
+template <int EPI>
+int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsigned gs) {
+    const unsigned tb = BigShape::W * 64, ts = SmallShape::W * 64;
+    SideStream *ss = nullptr;
+    int rc;
+    if ((rc = side_stream(&ss))) return rc;
+    {
+        std::lock_guard<std::mutex> lk(ss->mu);
+        if (hipEventRecord(ss->fork, st) != hipSuccess) return QI4_ERR_HIP;
+        if (hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) return QI4_ERR_HIP;
+        prefill_small_kernel<EPI, 0><<<gs, ts, 0, ss->s>>>(a);
+        prefill_small_kernel<EPI, 1><<<gs, ts, 0, ss->s>>>(a);
+        prefill_small_kernel<EPI, 2><<<gs, ts, 0, ss->s>>>(a);
+        if ((rc = launch_status())) return rc;
+        prefill_big_kernel<EPI><<<gb, tb, 0, st>>>(a);
+        if ((rc = launch_status())) return rc;
+        if (hipEventRecord(ss->join, ss->s) != hipSuccess) return QI4_ERR_HIP;
+        if (hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) return QI4_ERR_HIP;
+    }
+    // tiles deferred by either kind, after both
+    prefill_wide_kernel<EPI><<<512, tb, 0, st>>>(a);   // two workgroups per CU
     return launch_status();
+}
+}  // namespace
+
+int launch_prefill(const PrefillArgs &a, hipStream_t st) {
+    const int64_t nt = num_tiles(a.N, a.flags);
+    const int64_t gx = ceil_div(nt * 16, kRowsPerWG);
+    const int64_t gb = gx * ceil_div(a.max_big, 8) * 8, gs = gx * ceil_div(a.max_small, 8) * 8;
+    if (gb > 0x7fffffff || gs > 0x7fffffff) return QI4_ERR_SHAPE;
+    if (gb + 3 * gs > a.max_deferred) return QI4_ERR_SHAPE;
+    if (a.epi == QI4_EPI_SILU_MUL)
+        return launch_prefill_epi<QI4_EPI_SILU_MUL>(a, st, (unsigned)gb, (unsigned)gs);
+    return launch_prefill_epi<QI4_EPI_NONE>(a, st, (unsigned)gb, (unsigned)gs);
 }
 
 }  // namespace qi4

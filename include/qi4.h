@@ -31,8 +31,12 @@
  *  - Only group_size == 128 is built (QI4_ERR_GROUP otherwise); K must be a
  *    multiple of 128 (QI4_ERR_SHAPE).  The device must be gfx950
  *    (QI4_ERR_UNSUPPORTED otherwise).
- *  - Calls are reentrant; the only global state is a cached per-device
- *    architecture check.
+ *  - Calls are reentrant.  The global state is a cached per-device
+ *    architecture check and, for MoE batches of 128 tokens or more, one
+ *    internal side stream per device (with an event pair), created on first
+ *    use and kept for the life of the process: part of such a call runs there,
+ *    ordered after the work already enqueued on `stream` and before anything
+ *    enqueued on `stream` after the call, so the caller sees one stream.
  *
  * Canonical (interchange) format of a quantized matrix W [N][K] (out x in):
  *    qweight uint8  [N][K/2]    code of (n, k) in byte k/2, even k in the low nibble
@@ -173,7 +177,7 @@ int64_t moe_ffn_int4_workspace_bytes(const qi4_moe_desc *d, int64_t T);
  *   y  [R][H] float32: each expert's down-projection output, before weighting
  * `active` is the array moe_sort_tokens fills.  `workspace` is a buffer of
  * moe_ffn_int4_workspace_bytes(d, T) bytes (256-byte aligned); batches of 128 or
- * more tokens use it for fp16 copies of the activations and the tile list of the
+ * more tokens use it for fp16 copies of the activations and the tile lists of the
  * prefill kernels (smaller batches do not touch it).  h and y may lie inside it
  * only if they do not overlap those regions; passing separate buffers is simplest. */
 int moe_expert_gate_up(const qi4_moe_desc *d, const void *x, int64_t T,

@@ -135,6 +135,34 @@ def test_moe_top1_equals_single_expert_linear_path():
     assert_within(to_f64(y), ref, tol, "qlinear chain vs oracle")
 
 
+@pytest.mark.parametrize("T", [12, 300])
+def test_moe_large_scales(T):
+    """Scales at and above 256 (where 16 (q - zero) scale leaves binary16) in a
+    gate/up row block of one expert and a down row block of another, plus one
+    scale just below: the prefill path hands the affected tiles to its
+    plain-operand pass; decode sizes take the f32-scale path.  Checked against
+    the oracle like any other layer."""
+    import torch
+    import ffn_int4_g128_amd as q
+    E, H, I, k = 8, 384, 256, 4
+    ex, sh = _small_layer(E, H, I, 95)
+    f16 = lambda v: np.array([v], np.float16).view(np.uint16)[0]
+    ex["gu_s"][2, 40:48, 1] = f16(300.0)     # gate rows of expert 2
+    ex["gu_s"][2, 300, 2] = f16(256.0)       # up row of expert 2
+    ex["dn_s"][5, 100:116, 0] = f16(1000.0)  # down rows of expert 5
+    ex["dn_s"][6, 7, 1] = f16(255.9)         # just below: stays on the fast operands
+    x = workloads.activations(96, T, T, H, "bf16")
+    logits = workloads.logits_normal(97, T, T, E)
+    mw = q.pack_moe(ex, sh, E, H, I)
+    out = q.moe_ffn(bf16_dev(x), mw, k, logits=to_dev(logits))
+    torch.cuda.synchronize()
+    oids, op = oracle.topk_softmax(logits, k)
+    assert {2, 5, 6} <= set(np.unique(oids).tolist())
+    ref, tol = oracle.moe(oracle.widen(x, "bf16"), oids, op, ex, sh, H, I, E)
+    assert np.isfinite(ref).all()
+    assert_within(to_f64(out), ref, tol, f"moe large scales T{T}")
+
+
 # ---- the DeepSeek-V3-shaped layer ----------------------------------------------------
 
 @pytest.fixture(scope="module")
