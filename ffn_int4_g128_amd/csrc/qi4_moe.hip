@@ -19,7 +19,6 @@ namespace qi4 {
 namespace {
 
 constexpr int kRouteWaves = 4;
-constexpr int kSortWaves = 8;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 
@@ -96,22 +95,24 @@ __device__ inline uint64_t match_expert(int e, bool valid, int nbits) {
     return m;
 }
 
-__global__ void __launch_bounds__(kSortWaves * 64)
+// One workgroup of W waves; wave w takes the w-th chunk of the pairs.
+template <int W>
+__global__ void __launch_bounds__(W * 64)
 sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
             int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ offsets,
             int32_t *__restrict__ pair_to_sorted, int32_t *__restrict__ active) {
-    __shared__ int cnt[kSortWaves][kMaxExperts];
+    __shared__ int cnt[W][kMaxExperts];
     __shared__ int off_s[kMaxExperts + 1];
     __shared__ int tot_s[kMaxExperts];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    int64_t chunk = (npairs + kSortWaves - 1) / kSortWaves;
+    int64_t chunk = (npairs + W - 1) / W;
     chunk = (chunk + 63) & ~int64_t(63);
     const int64_t pb = wave * chunk;
     const int64_t pe = pb + chunk < npairs ? pb + chunk : npairs;
 
-    for (int i = threadIdx.x; i < kSortWaves * E; i += blockDim.x) cnt[i / E][i % E] = 0;
+    for (int i = threadIdx.x; i < W * E; i += blockDim.x) cnt[i / E][i % E] = 0;
     __syncthreads();
 
     // histogram of this wave's chunk (ids outside [0, E) are left out)
@@ -128,7 +129,7 @@ sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
     // per expert: exclusive prefix over the waves, and the total
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = 0;
-        for (int w = 0; w < kSortWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             const int c = cnt[w][e];
             cnt[w][e] = run;
             run += c;
@@ -304,7 +305,12 @@ int launch_route(const float *logits, int64_t T, int E, int k, int32_t *ids, flo
 
 int launch_sort(const int32_t *ids, int64_t npairs, int E, int32_t *sorted, int32_t *offsets,
                 int32_t *p2s, int32_t *active, hipStream_t st) {
-    sort_kernel<<<1, kSortWaves * 64, 0, st>>>(ids, npairs, E, bits_for(E), sorted, offsets, p2s,
+    // 16 waves once there are enough pairs to keep them busy
+    if (npairs >= 4096)
+        sort_kernel<16><<<1, 16 * 64, 0, st>>>(ids, npairs, E, bits_for(E), sorted, offsets, p2s,
+                                              active);
+    else
+        sort_kernel<8><<<1, 8 * 64, 0, st>>>(ids, npairs, E, bits_for(E), sorted, offsets, p2s,
                                                active);
     return launch_status();
 }

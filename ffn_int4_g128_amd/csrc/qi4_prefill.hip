@@ -93,32 +93,64 @@ __device__ inline uint4 dequant_f16_x16(uint32_t d, uint32_t negz, uint32_t negz
 
 // ---- row preparation: fp16 with a per-row power-of-two prescale ----------------
 
-// src_kind 0: bf16 rows [rows][len]; 1: hi/lo bf16 pairs [rows][2][len].
-__global__ void __launch_bounds__(256)
-prep_rows_kernel(const uint16_t *__restrict__ src, int src_kind, int64_t len,
+// src_kind 0: bf16 rows [rows][len]; 1: hi/lo bf16 pairs [rows][2][len].  One
+// wave per row; each lane takes 8 consecutive elements (16-byte loads and
+// stores) of every 512-wide chunk: one pass for the row maximum, one for the
+// conversion (the row is then in cache).  len is a multiple of 128 and the rows
+// are 16-byte aligned.
+constexpr int kPrepWaves = 4;
+
+__global__ void __launch_bounds__(kPrepWaves * 64)
+prep_rows_kernel(const uint16_t *__restrict__ src, int src_kind, int64_t rows, int64_t len,
                  uint16_t *__restrict__ dst, int32_t *__restrict__ exps) {
-    __shared__ float red[4];
-    const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
     const uint16_t *s = src + row * len * (src_kind ? 2 : 1);
-    auto value = [&](int64_t i) -> float {
-        if (src_kind == 0) return bf16_to_f32(s[i]);
-        return bf16_to_f32(s[i]) + bf16_to_f32(s[len + i]);
+    auto load8 = [&](int64_t i, float (&v)[8]) {   // elements i .. i + 7
+        const uint4 a = *reinterpret_cast<const uint4 *>(s + i);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v[2 * c] = bf16_to_f32(w[c] & 0xFFFFu);
+            v[2 * c + 1] = bf16_to_f32(w[c] >> 16);
+        }
+        if (src_kind) {
+            const uint4 b = *reinterpret_cast<const uint4 *>(s + len + i);
+            const uint32_t u[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                v[2 * c] += bf16_to_f32(u[c] & 0xFFFFu);
+                v[2 * c + 1] += bf16_to_f32(u[c] >> 16);
+            }
+        }
     };
     float mx = 0.f;
-    for (int64_t i = threadIdx.x; i < len; i += 256) mx = fmaxf(mx, fabsf(value(i)));
+    for (int64_t i = 8 * lane; i < len; i += 512) {
+        float v[8];
+        load8(i, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    }
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     int E = 0;
     if (mx > 0.f) frexpf(mx, &E);          // mx in [2^(E-1), 2^E)
     const int sh = mx > 0.f ? 14 - E : 0;  // |v * 2^sh| < 2^14
-    for (int64_t i = threadIdx.x; i < len; i += 256) {
-        // k = 2, 3, 6, 7 (mod 8) carry an extra 2^-4 (the weights there are 16x)
-        const _Float16 h = (_Float16)ldexpf(value(i), (i & 2) ? sh - 4 : sh);
-        dst[row * len + i] = __builtin_bit_cast(uint16_t, h);
+    for (int64_t i = 8 * lane; i < len; i += 512) {
+        float v[8];
+        load8(i, v);
+        uint32_t o[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // k = 2, 3, 6, 7 (mod 8) carry an extra 2^-4 (the weights there are 16x)
+            const int se = (c & 1) ? sh - 4 : sh;
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[2 * c], se));
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[2 * c + 1], se));
+            o[c] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(dst + row * len + i) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    if (threadIdx.x == 0) exps[row] = -sh;
+    if (lane == 0) exps[row] = -sh;
 }
 
 // ---- tile planner ---------------------------------------------------------------
@@ -543,8 +575,8 @@ int launch_prep_rows(const void *src, int src_kind, int64_t rows, int64_t len, u
                      int32_t *exps, hipStream_t st) {
     if (rows <= 0) return QI4_OK;
     if (rows > 0x7fffffff) return QI4_ERR_SHAPE;
-    prep_rows_kernel<<<(unsigned)rows, 256, 0, st>>>(static_cast<const uint16_t *>(src), src_kind,
-                                                     len, dst, exps);
+    prep_rows_kernel<<<(unsigned)ceil_div(rows, kPrepWaves), kPrepWaves * 64, 0, st>>>(
+        static_cast<const uint16_t *>(src), src_kind, rows, len, dst, exps);
     return launch_status();
 }
 
