@@ -14,7 +14,10 @@ The step runs the five stages through the C ABI (route, sort, grouped
 gate/up + SiLU, grouped down, combine); HIP events on the launch stream time
 each grouped GEMM inside the timed region.  The JSON line reports tokens/s of
 the main batch size, the roofline of the dominant kernel (grouped gate/up),
-and the oracle's CPU time on a bounded sample as a baseline.
+and the oracle's CPU time on a bounded sample as a baseline.  Extra fields
+report the other decode batch sizes, the T=2048 prefill step (Zipf-skewed
+routing) and, with a cold last-level cache, the dense linears: the
+Llama-7B-shaped decode stack at T=1 and the skinny sweep.
 """
 from __future__ import annotations
 
@@ -63,6 +66,7 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed prefill steps (T=2048, Zipf-skewed routing); 0 to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-linear measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     return ap.parse_args()
@@ -234,6 +238,98 @@ def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
             "down_mfma_frac": flop_dn / dn / BF16_MFMA_PEAK}
 
 
+def _dense_pack(q, torch, w, flags=0):
+    dev = lambda a: torch.from_numpy(a.view("int16") if a.dtype.name == "uint16" else a).cuda()
+    return q.pack(dev(w["qweight"]), dev(w["scales"]), dev(w["zeros"]), w["N"], w["K"], flags)
+
+
+def run_dense(q, torch, reps=20):
+    """Dense int4-g128 linears, cold cache: before each timed rep 1 GiB is read
+    (outside the event pair), so no weight is served from the 256 MB last-level
+    cache.  A read, not a write: a 1 GiB write would leave that cache full of
+    dirty lines whose write-back the next kernel's reads would pay for.  The
+    events are enqueued while the flush runs, so the host adds no gaps.  Median
+    over reps.  Workloads: the Llama-7B-shaped decode stack at T=1 (QKV, O,
+    gate/up with SiLU*up, down: four launches back to back, and the same four
+    replayed from a captured HIP graph) and the skinny sweep (5120->13824 and
+    13824->5120 at T = 1..32, one launch per event pair).  An event pair around a
+    launch adds about 5-8 us here, a large part of a 10-20 us linear."""
+    import statistics
+    import workloads
+    per_w = workloads.packed_weight_bytes(1)
+    rd = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 3):
+            torch.sum(rd, dim=0, out=acc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return statistics.median(ts)
+
+    c1 = workloads.LLAMA7B_STACK
+    lin = []
+    for i, (name, K, N, epi) in enumerate(c1["linears"]):
+        w = workloads.weights(c1["seed"], 10 + i, N, K, *c1["scale"])
+        flags = q.QI4_PACK_GATEUP if epi == "silu_mul" else 0
+        e = q.QI4_EPI_SILU_MUL if epi == "silu_mul" else q.QI4_EPI_NONE
+        x = q_bf16(torch, workloads.activations(c1["seed"], 20 + i, 1, K, "bf16"))
+        n_out = N // 2 if epi == "silu_mul" else N
+        y = torch.empty((1, n_out), dtype=torch.bfloat16, device="cuda")
+        lin.append((name, N, K, n_out, _dense_pack(q, torch, w, flags), flags, e, x, y))
+    calls = [lambda l=l: q.qlinear(l[7], l[4], l[1], flags=l[5], epilogue=l[6], out=l[8]) for l in lin]
+
+    def stack():
+        for f in calls:
+            f()
+    stack()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack()
+    t_eager, t_graph = timed(stack), timed(graph.replay)
+    stack_bytes, per = 0.0, []
+    for (name, N, K, n_out, *_), f in zip(lin, calls):
+        b = N * K * per_w + K * 2 + n_out * 2
+        stack_bytes += b
+        t = timed(f)
+        per.append({"linear": name, "N": N, "K": K, "us_with_event_overhead": t * 1e6,
+                    "GBps": b / t / 1e9})
+    del graph, lin, calls
+    stack = {"workload": "llama7b_decode_stack_t1", "bytes": stack_bytes,
+             "eager_us": t_eager * 1e6, "eager_tokens_per_s": 1.0 / t_eager,
+             "eager_GBps": stack_bytes / t_eager / 1e9,
+             "graph_us": t_graph * 1e6, "graph_tokens_per_s": 1.0 / t_graph,
+             "graph_GBps": stack_bytes / t_graph / 1e9,
+             "graph_hbm_frac": stack_bytes / t_graph / 1e9 / HBM_PEAK_GBPS, "linears": per}
+
+    c2 = workloads.SKINNY_SWEEP
+    sweep = []
+    for i, (K, N) in enumerate(c2["shapes"]):
+        w = workloads.weights(c2["seed"], 10 + i, N, K, *c2["scale"])
+        pw = _dense_pack(q, torch, w)
+        for T in c2["T"]:
+            x = q_bf16(torch, workloads.activations(c2["seed"], 20 + 10 * i + T, T, K, "bf16",
+                                                    c2["x_scale"]))
+            y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+            t = timed(lambda: q.qlinear(x, pw, N, out=y))
+            b = N * K * per_w + T * K * 2 + T * N * 2
+            sweep.append({"K": K, "N": N, "T": T, "us_with_event_overhead": t * 1e6,
+                          "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
+                          "tokens_per_s": T / t})
+        del pw
+    del rd
+    torch.cuda.empty_cache()
+    return {"protocol": "1 GiB read before each rep (outside the events); median of "
+                        f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep}
+
+
 def cpu_baseline(c, T, target_s):
     """The oracle (fp64 C, OpenMP over output rows) on a bounded sample of the
     same workload: n tokens of layer 0, n chosen for about target_s seconds."""
@@ -292,6 +388,11 @@ def main():
         prefill = run_prefill(q, torch, layers, args.prefill_steps, 2)
         log(f"prefill: {json.dumps(prefill)}")
 
+    dense = None
+    if not args.no_dense:
+        dense = run_dense(q, torch)
+        log(f"dense: {json.dumps(dense)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         del layers
@@ -327,6 +428,7 @@ def main():
         "sweep": [{k: r[k] for k in ("T", "tokens_per_s", "ms_per_step", "step_GBps", "gate_up_GBps",
                                      "down_GBps", "experts_touched_mean")} for r in sweep],
         "prefill": prefill,
+        "dense": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

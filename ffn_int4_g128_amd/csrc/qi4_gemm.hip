@@ -337,9 +337,9 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 // and 5120/13824 shapes, DeepSeek-V3-shaped experts at T = 1, 8, 32):
 //  * W waves split K; about ten 128-wide groups per wave for a single matrix,
 //    and two waves per workgroup when many expert problems already fill the chip;
-//  * NB = 2 tiles per workgroup (the gate/up pair) unless a single small matrix
-//    needs more workgroups (NB = 1); grouped gate/up GEMMs take NB = 4, with
-//    four waves when the grid is small;
+//  * NB = 2 tiles per workgroup (the gate/up pair) unless a single matrix of
+//    fewer than 320 tiles needs more workgroups (NB = 1); grouped gate/up GEMMs
+//    take NB = 4, with four waves when the grid is small;
 //  * one M tile per pass (16 activation rows), two for a single matrix with
 //    more rows.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t st) {
@@ -352,7 +352,9 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     // passes.  A single matrix with more than 16 rows uses two M tiles.
     const int MT = (n_problems == 1 && max_slots > spt) ? 2 : 1;
     const bool silu = args.epi == QI4_EPI_SILU_MUL;
-    int NB = (silu || ceil_div(nt, 2) * n_problems >= 1024) ? 2 : 1;
+    // (a single matrix takes two tiles per workgroup from 320 tiles up: cold-cache
+    // sweeps of 4096..22016-row matrices put the crossover between 256 and 320)
+    int NB = (silu || ceil_div(nt, 2) * n_problems >= 160) ? 2 : 1;
     int W;
     if (n_problems > 1) {
         // grouped expert GEMMs: the gate/up pairs stream best four tiles per
