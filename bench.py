@@ -16,8 +16,9 @@ each grouped GEMM inside the timed region.  The JSON line reports tokens/s of
 the main batch size, the roofline of the dominant kernel (grouped gate/up),
 and the oracle's CPU time on a bounded sample as a baseline.  Extra fields
 report the other decode batch sizes, the T=2048 prefill step (Zipf-skewed
-routing) and, with a cold last-level cache, the dense linears: the
-Llama-7B-shaped decode stack at T=1 and the skinny sweep.
+routing) and, with a cold last-level cache, the dense linears (the
+Llama-7B-shaped decode stack at T=1 and the skinny sweep) and the load-time
+quantizer.
 """
 from __future__ import annotations
 
@@ -330,6 +331,37 @@ def run_dense(q, torch, reps=20):
                         f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep}
 
 
+def run_quantize(q, torch, reps=10):
+    """Load-time quantizer throughput: bf16 weights [16384][7168] (four experts'
+    gate/up rows of the MoE layer), N(0, 0.02), cold cache (1 GiB read before each
+    rep, outside the events); median of reps."""
+    import statistics
+    import workloads
+    N, K = 16384, 7168
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    w = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    rd = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    q.quantize(w)
+    ts = []
+    for r in range(reps + 2):
+        torch.sum(rd, dim=0, out=acc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        q.quantize(w)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = statistics.median(ts)
+    b = N * K * (2 + workloads.packed_weight_bytes(1))
+    del w, rd
+    torch.cuda.empty_cache()
+    return {"workload": "quantize_bf16_16384x7168_g128", "us": t * 1e6,
+            "weights_per_s": N * K / t, "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS}
+
+
 def cpu_baseline(c, T, target_s):
     """The oracle (fp64 C, OpenMP over output rows) on a bounded sample of the
     same workload: n tokens of layer 0, n chosen for about target_s seconds."""
@@ -393,6 +425,9 @@ def main():
         dense = run_dense(q, torch)
         log(f"dense: {json.dumps(dense)}")
 
+    quant = run_quantize(q, torch)
+    log(f"quantize: {json.dumps(quant)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         del layers
@@ -429,6 +464,7 @@ def main():
                                      "down_GBps", "experts_touched_mean")} for r in sweep],
         "prefill": prefill,
         "dense": dense,
+        "quantize": quant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -61,6 +61,7 @@ def lib():
             "qi4_pack": (ci, [vp, vp, vp, i64, i64, ci, ci, vp, vp]),
             "qi4_unpack": (ci, [vp, i64, i64, ci, ci, vp, vp, vp, vp]),
             "qi4_dequant_f32": (ci, [vp, i64, i64, ci, ci, vp, vp]),
+            "qi4_quantize": (ci, [vp, ci, i64, i64, ci, vp, vp, vp, vp]),
             "qlinear_int4_g128": (ci, [vp, ci, i64, i64, vp, i64, ci, vp, ci, ci, vp]),
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
             "moe_sort_tokens": (ci, [vp, i64, i32, i64, vp, vp, vp, vp, vp]),
@@ -79,7 +80,7 @@ def lib():
 
 # declared in include/qi4.h, in header order
 EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pack", "qi4_unpack",
-            "qi4_dequant_f32", "qlinear_int4_g128", "moe_route_topk", "moe_sort_tokens",
+            "qi4_dequant_f32", "qi4_quantize", "qlinear_int4_g128", "moe_route_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4"]
 
@@ -150,6 +151,27 @@ def dequant_f32(packed, N: int, K: int, flags: int = 0, stream=None):
     _check(lib().qi4_dequant_f32(_ptr(packed), N, K, GROUP, flags, _ptr(w), _stream(stream)),
            "qi4_dequant_f32")
     return w
+
+
+def quantize(w, stream=None):
+    """float32 or bfloat16 device weights [N][K] -> canonical (qweight uint8 [N][K/2],
+    scales int16 binary16 bits [N][K/128], zeros uint8 [N][K/128]) device tensors."""
+    import torch
+    if w.dtype == torch.float32:
+        wd = QI4_F32
+    elif w.dtype == torch.bfloat16:
+        wd = QI4_BF16
+    else:
+        raise ValueError(f"w must be float32 or bfloat16, got {w.dtype}")
+    if not (w.is_cuda and w.is_contiguous() and w.dim() == 2):
+        raise ValueError("w must be a contiguous 2-D device tensor")
+    N, K = w.shape
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((N, K // GROUP), dtype=torch.int16, device=w.device)
+    zr = torch.empty((N, K // GROUP), dtype=torch.uint8, device=w.device)
+    _check(lib().qi4_quantize(_ptr(w), wd, N, K, GROUP, _ptr(qw), _ptr(sc), _ptr(zr),
+                              _stream(stream)), "qi4_quantize")
+    return qw, sc, zr
 
 
 # ---- linear ----------------------------------------------------------------------

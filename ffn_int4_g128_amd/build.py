@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqi4.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["qi4_api.cpp", "qi4_pack.hip", "qi4_gemm.hip", "qi4_moe.hip", "qi4_prefill.hip"]
+SOURCES = ["qi4_api.cpp", "qi4_pack.hip", "qi4_gemm.hip", "qi4_moe.hip", "qi4_prefill.hip",
+           "qi4_quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are kept out of the generated code on purpose.

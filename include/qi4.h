@@ -112,6 +112,21 @@ int qi4_unpack(const void *packed, int64_t N, int64_t K, int group_size, int fla
 int qi4_dequant_f32(const void *packed, int64_t N, int64_t K, int group_size, int flags,
                     float *w, void *stream);
 
+/* Load-time quantizer: w [N][K] (float32 or bf16 per w_dtype, 16-byte aligned;
+ * qweight 4-byte aligned) -> canonical qweight, scales, zeros (the format above), groups
+ * of 128.  The fastllm README (gittoolsai.com), section "model export": loading
+ * with an int4 dtype quantizes online at every load, which is slow; this is that
+ * step on the GPU.  Per group (asymmetric min/max, 0 always inside the range):
+ *   lo = min(0, min w), hi = max(0, max w)
+ *   scale = binary16 nearest (ties to even) of (hi - lo) / 15; 1.0 if that is 0
+ *   zero  = clamp(rint(-lo / scale), 0, 15)
+ *   q     = clamp(rint(w / scale) + zero, 0, 15)     rint: half to even
+ * evaluated in binary64 (inputs widen exactly, divisions correctly rounded).
+ * Weights must be finite (NaN is skipped by the min/max, its code unspecified).
+ * Outputs must not overlap w or each other (QI4_ERR_ALIAS). */
+int qi4_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
+                 uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream);
+
 /* The linear layer: y[t][n'] = epilogue( sum_k x[t][k] * dequant(W)[n][k] ).
  *   x        [T][K] of x_dtype (QI4_BF16 or QI4_F32), row-major, contiguous
  *   packed_w packed N x K matrix (flags as given to qi4_pack)

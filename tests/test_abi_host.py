@@ -81,6 +81,14 @@ def test_argument_errors_return_before_any_launch(q):
     assert L.moe_route_topk(p, 4, 8, 9, p, p, None) == -2
     assert L.moe_route_topk(p, 4, 2000, 8, p, p, None) == -2
     assert L.moe_sort_tokens(None, 4, 8, 256, p, p, p, None, None) == -1
+    # quantizer: NULL, dtype, group size, K, alignment, overlapping outputs
+    assert L.qi4_quantize(None, 1, 16, 128, 128, p, p, p, None) == -1
+    assert L.qi4_quantize(p, 5, 16, 128, 128, p, p, p, None) == -3
+    assert L.qi4_quantize(p, 1, 16, 128, 64, p, p, p, None) == -4
+    assert L.qi4_quantize(p, 1, 16, 100, 128, p, p, p, None) == -2
+    assert L.qi4_quantize(ctypes.c_void_p(0x1008), 1, 16, 128, 128, p, p, p, None) == -2
+    w = ctypes.c_void_p(0x100000)
+    assert L.qi4_quantize(w, 1, 16, 128, 128, ctypes.c_void_p(0x100000 + 256), p, p, None) == -6
 
 
 def test_moe_descriptor_errors(q):
