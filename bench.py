@@ -12,7 +12,9 @@ data already resident in HBM when timing starts.
 
 The step runs the five stages through the C ABI (route, sort, grouped
 gate/up + SiLU, grouped down, combine); HIP events on the launch stream time
-each grouped GEMM inside the timed region.  The JSON line reports tokens/s of
+each grouped GEMM inside the timed region.  The events are created without a
+system-scope fence (TimingEvent): a fenced event writes back and invalidates the
+caches at every record, a 5-6 us gap that no real forward pays.  The JSON line reports tokens/s of
 the main batch size, the roofline of the dominant kernel (grouped gate/up),
 and the oracle's CPU time on a bounded sample as a baseline.  Extra fields
 report the other decode batch sizes, the T=2048 prefill step (Zipf-skewed
@@ -54,6 +56,58 @@ def measured_traffic():
     if kv.get("kernel-source-sha256") != h.hexdigest():
         return None
     return float(kv["gate-up-traffic-bytes-per-launch"])
+
+
+class TimingEvent:
+    """A HIP event created with hipEventDisableSystemFence, recorded on the
+    launch stream.  torch.cuda.Event records with a system-scope release: the
+    whole last-level cache hierarchy is written back and invalidated at every
+    record, which costs about 5-6 us and shows up as a gap before the next
+    kernel.  An event used only for timing needs no such fence, so these
+    events add no gap between the kernels they bracket."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            import torch
+            path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._h = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self._h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        rc = self._lib().hipEventRecord(self._h, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._h, end._h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._hip is not None:
+            self._hip.hipEventDestroy(self._h)
 
 
 def parse():
@@ -171,7 +225,7 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     for i in range(warmup):
         s.step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -215,7 +269,7 @@ def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
     touched = [s.touched(i) for i in range(period)]
     for i in range(warmup):
         s.step(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -253,8 +307,8 @@ def run_dense(q, torch, reps=20):
     over reps.  Workloads: the Llama-7B-shaped decode stack at T=1 (QKV, O,
     gate/up with SiLU*up, down: four launches back to back, and the same four
     replayed from a captured HIP graph) and the skinny sweep (5120->13824 and
-    13824->5120 at T = 1..32, one launch per event pair).  An event pair around a
-    launch adds about 5-8 us here, a large part of a 10-20 us linear."""
+    13824->5120 at T = 1..32, one launch per event pair).  The event pair is a
+    fence-free TimingEvent pair, so it adds no cache write-back to the time."""
     import statistics
     import workloads
     per_w = workloads.packed_weight_bytes(1)
@@ -265,7 +319,7 @@ def run_dense(q, torch, reps=20):
         ts = []
         for r in range(reps + 3):
             torch.sum(rd, dim=0, out=acc)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             e0.record()
             fn()
             e1.record()
@@ -300,7 +354,7 @@ def run_dense(q, torch, reps=20):
         b = N * K * per_w + K * 2 + n_out * 2
         stack_bytes += b
         t = timed(f)
-        per.append({"linear": name, "N": N, "K": K, "us_with_event_overhead": t * 1e6,
+        per.append({"linear": name, "N": N, "K": K, "us": t * 1e6,
                     "GBps": b / t / 1e9})
     del graph, lin, calls
     stack = {"workload": "llama7b_decode_stack_t1", "bytes": stack_bytes,
@@ -321,7 +375,7 @@ def run_dense(q, torch, reps=20):
             y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
             t = timed(lambda: q.qlinear(x, pw, N, out=y))
             b = N * K * per_w + T * K * 2 + T * N * 2
-            sweep.append({"K": K, "N": N, "T": T, "us_with_event_overhead": t * 1e6,
+            sweep.append({"K": K, "N": N, "T": T, "us": t * 1e6,
                           "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
                           "tokens_per_s": T / t})
         del pw
@@ -347,7 +401,7 @@ def run_quantize(q, torch, reps=10):
     ts = []
     for r in range(reps + 2):
         torch.sum(rd, dim=0, out=acc)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record()
         q.quantize(w)
         e1.record()

@@ -22,15 +22,98 @@ constexpr int kRouteWaves = 4;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 
+// ---- cross-lane helpers ----------------------------------------------------------------
+
+// Cross-lane moves without the LDS crossbar: DPP inside rows of 16 lanes, and
+// the permlane swaps between rows and between the wave's halves.
+// Lanes without a source, and lanes of rows left out by ROWS, read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15 - i within 16
+constexpr int kDppShr1 = 0x111;       // lane i <- lane i - 1 within 16 (row_shr:1)
+constexpr int kDppBcast15 = 0x142;    // row r <- lane 15 of row r - 1
+constexpr int kDppBcast31 = 0x143;    // rows 2, 3 <- lane 31
+
+// Inclusive prefix sum over the wave's lanes (every lane active).
+__device__ inline int wave_incl_scan(int x) {
+    x += (int)dpp_u32<kDppShr1>((uint32_t)x);
+    x += (int)dpp_u32<kDppShr1 + 1>((uint32_t)x);
+    x += (int)dpp_u32<kDppShr1 + 3>((uint32_t)x);
+    x += (int)dpp_u32<kDppShr1 + 7>((uint32_t)x);   // rows of 16 scanned
+    x += (int)dpp_u32<kDppBcast15, 0xA>((uint32_t)x);   // rows 1, 3 add their left row
+    x += (int)dpp_u32<kDppBcast31, 0xC>((uint32_t)x);   // rows 2, 3 add rows 0-1
+    return x;
+}
+
+// (value, index) pairs: the larger value wins, equal values go to the lower index.
+__device__ inline bool beats(float av, int ai, float bv, int bi) {
+    return (av > bv) | ((av == bv) & (ai < bi));   // no short-circuit: no branches
+}
+template <int CTRL>
+__device__ inline void argmax_step(float &v, int &i) {
+    const float ov = __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+    const int oi = (int)dpp_u32<CTRL>((uint32_t)i);
+    if (beats(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+// Both results of a swap hold, lane by lane, the two partners of a pairing
+// (lane with the other row / half); keep the better one.
+__device__ inline void argmax_swap(float &v, int &i, bool rows16) {
+    const uint32_t uv = __float_as_uint(v), ui = (uint32_t)i;
+    uint32_t av, bv, ai, bi;
+    if (rows16) {
+        const auto sv = __builtin_amdgcn_permlane16_swap(uv, uv, false, false);
+        const auto si = __builtin_amdgcn_permlane16_swap(ui, ui, false, false);
+        av = sv[0]; bv = sv[1]; ai = si[0]; bi = si[1];
+    } else {
+        const auto sv = __builtin_amdgcn_permlane32_swap(uv, uv, false, false);
+        const auto si = __builtin_amdgcn_permlane32_swap(ui, ui, false, false);
+        av = sv[0]; bv = sv[1]; ai = si[0]; bi = si[1];
+    }
+    const bool a_wins = beats(__uint_as_float(av), (int)ai, __uint_as_float(bv), (int)bi);
+    v = __uint_as_float(a_wins ? av : bv);
+    i = (int)(a_wins ? ai : bi);
+}
+// Argmax over the whole wave; every lane ends with the winner.  The wave must
+// be fully active.
+__device__ inline void wave_argmax(float &v, int &i) {
+    argmax_step<kDppXor1>(v, i);
+    argmax_step<kDppXor2>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    argmax_swap(v, i, true);
+    argmax_swap(v, i, false);
+}
+// Sum over the whole wave in a fixed pattern; every lane ends with the same bits.
+__device__ inline float wave_sum(float x) {
+    x += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(x)));
+    x += __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(x)));
+    x += __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(x)));
+    x += __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(x)));
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
 // ---- router: one wave per token --------------------------------------------------
 
+// k rounds of a wave argmax over the logits not taken yet; lane j keeps the
+// j-th pick.  Then the softmax over the k picks.
 template <int VPL>
 __global__ void __launch_bounds__(kRouteWaves * 64)
 route_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
              int32_t *__restrict__ ids, float *__restrict__ wts) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
-    if (t >= T) return;
+    if (t >= T) return;   // whole waves leave: the rest stay fully active
     float v[VPL];
     bool taken[VPL];
 #pragma unroll
@@ -49,20 +132,12 @@ route_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int e = i * 64 + lane;
-            if (!taken[i] && (v[i] > bv || (v[i] == bv && e < bi))) {
+            if ((!taken[i]) & beats(v[i], e, bv, bi)) {
                 bv = v[i];
                 bi = e;
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        wave_argmax(bv, bi);
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
             if (bi == i * 64 + lane) taken[i] = true;
@@ -71,11 +146,9 @@ route_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
             myi = bi;
         }
     }
-    const float l0 = __shfl(myv, 0);
-    float ex = lane < k ? expf(myv - l0) : 0.f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__float_as_uint(myv)));
+    const float ex = lane < k ? expf(myv - l0) : 0.f;
+    const float sum = wave_sum(ex);
     if (lane < k) {
         ids[t * k + lane] = myi;
         wts[t * k + lane] = ex / sum;
@@ -147,14 +220,7 @@ sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
             s += tot_s[e];
             a += tot_s[e] > 0;
         }
-        int ps = s, pa = a;   // inclusive scans across lanes
-        for (int d = 1; d < 64; d <<= 1) {
-            const int ys = __shfl_up(ps, d), ya = __shfl_up(pa, d);
-            if (lane >= d) {
-                ps += ys;
-                pa += ya;
-            }
-        }
+        const int ps = wave_incl_scan(s), pa = wave_incl_scan(a);   // across lanes
         int run = ps - s, arun = pa - a;
         for (int e = e0; e < e0 + per && e < E; ++e) {
             off_s[e] = run;
@@ -197,23 +263,39 @@ sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
 
 // ---- combine: fixed order, slots then the shared expert -------------------------------
 
+// The slot rows of a token are loaded eight at a time before any is added, so
+// their latencies overlap; the additions keep the order j = 0 .. k-1, then the
+// shared expert.
 __global__ void __launch_bounds__(256)
 combine_kernel(const float *__restrict__ y, const float *__restrict__ wts,
                const int32_t *__restrict__ p2s, int64_t T, int k, int64_t H, int has_shared,
                uint16_t *__restrict__ out) {
+    constexpr int kBatch = 8;
     const int64_t t = blockIdx.y;
     const int64_t n4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (n4 >= H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float p = wts[t * k + j];
-        const int64_t r = p2s[t * k + j];
-        if (r < 0) continue;
-        const float4 v = *reinterpret_cast<const float4 *>(y + r * H + n4);
-        acc.x += p * v.x;
-        acc.y += p * v.y;
-        acc.z += p * v.z;
-        acc.w += p * v.w;
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+        float p[kBatch];
+        float4 v[kBatch];
+        bool use[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int j = j0 + b;
+            const int64_t r = j < k ? p2s[t * k + j] : -1;   // -1: dropped slot
+            use[b] = r >= 0;
+            p[b] = use[b] ? wts[t * k + j] : 0.f;
+            v[b] = use[b] ? *reinterpret_cast<const float4 *>(y + r * H + n4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            if (!use[b]) continue;
+            acc.x += p[b] * v[b].x;
+            acc.y += p[b] * v[b].y;
+            acc.z += p[b] * v[b].z;
+            acc.w += p[b] * v[b].w;
+        }
     }
     if (has_shared) {
         const float4 v = *reinterpret_cast<const float4 *>(y + (T * k + t) * H + n4);
