@@ -14,8 +14,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kGroup = 128;        // weights per quantization group along K
 constexpr int kTileRows = 16;      // rows per packed tile (one MFMA 16x16 column block)
 constexpr int kTileGroupBytes = 1024;  // codes of one (tile, group) block: 64 lanes x 16 B
-constexpr int kScaleBytes = 32;    // 16 binary16 scales per (tile, group)
-constexpr int kZeroBytes = 8;      // 16 zero points, two per byte, per (tile, group)
+// Scales and zero points of four consecutive tiles (a "quad") are stored
+// together per group, so a wave serving 1, 2 or 4 aligned tiles fetches them
+// with one scale load and one zero load per lane.
+constexpr int kQuadTiles = 4;
+constexpr int kQuadScaleBytes = 128;   // [row 0..15][tile slot 0..3] binary16
+constexpr int kQuadZeroBytes = 32;     // [row 0..15][2 bytes]: tile slot s in nibble s
 
 // Number of 16-row tiles of an N-row matrix.  With the gate/up pairing the
 // gate half and the up half are each padded to whole tiles.
@@ -38,17 +42,48 @@ __host__ __device__ inline int64_t tile_row(int64_t t, int r, int64_t N, int fla
 
 // Byte offsets of the three regions of a packed matrix.
 struct PackedLayout {
-    int64_t nt, G;
+    int64_t nt, nq, G;
     int64_t scales_off, zeros_off, bytes;
     __host__ __device__ PackedLayout(int64_t N, int64_t K, int flags) {
         nt = num_tiles(N, flags);
+        nq = (nt + kQuadTiles - 1) / kQuadTiles;
         G = K / kGroup;
         scales_off = nt * G * kTileGroupBytes;
-        zeros_off = scales_off + nt * G * kScaleBytes;
-        int64_t end = zeros_off + nt * G * kZeroBytes;
+        zeros_off = scales_off + nq * G * kQuadScaleBytes;
+        int64_t end = zeros_off + nq * G * kQuadZeroBytes;
         bytes = (end + 255) & ~int64_t(255);
     }
+    // Start of the (quad of tile t, group g) scale and zero records.  Row r's
+    // scale of tile t is at scale_rec + 8 r + 2 (t & 3); its zero is nibble
+    // 4 (t & 1) of byte zero_rec + 2 r + ((t & 3) >> 1).
+    __host__ __device__ int64_t scale_rec(int64_t t, int64_t g) const {
+        return scales_off + ((t / kQuadTiles) * G + g) * kQuadScaleBytes;
+    }
+    __host__ __device__ int64_t zero_rec(int64_t t, int64_t g) const {
+        return zeros_off + ((t / kQuadTiles) * G + g) * kQuadZeroBytes;
+    }
 };
+
+// Scale and zero records of NB (1, 2 or 4) aligned tiles of one quad for one
+// row, one load each: lane offsets vs = 8 r + 2 slot0 and vz = 2 r + slot0 / 2
+// (slot0 = first tile's slot in its quad), record starts os and oz in soffset.
+// Afterwards the scale of tile nb is half (nb & 1) of sc[nb >> 1] and its zero
+// is nibble nb of zb (NB = 1: nibble slot0 & 1).
+template <int NB>
+__device__ inline void load_meta(__amdgpu_buffer_rsrc_t r, uint32_t vs, uint32_t vz, uint32_t os,
+                                 uint32_t oz, uint32_t *sc, uint32_t &zb) {
+    static_assert(NB == 1 || NB == 2 || NB == 4, "tiles per quad load");
+    if constexpr (NB == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, vs, os, 0);
+        sc[0] = v[0];
+        sc[1] = v[1];
+        zb = __builtin_amdgcn_raw_buffer_load_b16(r, vz, oz, 0);
+    } else {
+        sc[0] = NB == 2 ? __builtin_amdgcn_raw_buffer_load_b32(r, vs, os, 0)
+                        : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, vs, os, 0);
+        zb = __builtin_amdgcn_raw_buffer_load_b8(r, vz, oz, 0);
+    }
+}
 
 // Within one lane's dword, the code of k-offset e (0..7) sits at nibble
 // position (e >> 1) + 4 * (e & 1).  Unpacking then needs only a mask, a shift

@@ -39,6 +39,8 @@ struct GemmArgs {
     int out_mode;              // OutMode
     int epi;                   // QI4_EPI_NONE or QI4_EPI_SILU_MUL
     int64_t n_out;             // valid output columns
+    // set by launch_qgemm
+    int blocks_per_wg;         // consecutive tile blocks one workgroup streams
 };
 
 // Launch the GEMM for `n_problems` problems (grid.y); `max_slots` bounds the

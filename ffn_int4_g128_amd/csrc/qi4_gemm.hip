@@ -17,7 +17,12 @@
 //    equals scale * sum_k x * (q - zero).  Both chains see identical operands
 //    where q == zero, so an all-zero group contributes exactly 0;
 //  * the K range is split across the waves of a workgroup and reduced in LDS in
-//    a fixed order, so results are deterministic.
+//    a fixed order, so results are deterministic;
+//  * a workgroup may stream several consecutive tile blocks through one
+//    register pipeline: the next block's first loads are in flight while the
+//    previous block is reduced and stored;
+//  * the scales and zero points of a quad of four tiles arrive with one load
+//    each per group.
 // Activations in float32 are split exactly into three bf16 terms (hi + mid +
 // lo), each an MFMA row; the epilogue adds the rows of one token back together.
 #include "qi4_gemm.h"
@@ -55,10 +60,11 @@ __device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
 template <int NB, int MT, bool AF32>
 struct Stage {
     uint4 cw[NB];
-    uint32_t sc[NB];
-    uint32_t zb[NB];
+    uint32_t sc[(NB + 1) / 2];   // binary16 scales of tiles 2i, 2i+1 in dword i
+    uint32_t zb;                 // zero of tile nb in nibble nb (+ the slot offset)
     uint4 af[MT][4][AF32 ? 2 : 1];
 };
+
 
 // Buffer resource over [base, base + bytes): loads at offsets past the end
 // return zero, which lets every load of the K loop run unconditionally.
@@ -75,8 +81,14 @@ __device__ inline uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Waves per SIMD the register allocation must allow: the grouped gate/up GEMM
+// sits one register above the four-wave limit without this.
+template <int NB, int MT, bool AF32, int EPI>
+constexpr int kMinWaves = (!AF32 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL) ? 4 : 1;
+
 template <int NB, int MT, bool AF32, int S, int EPI>
 __global__ void __launch_bounds__(kMaxWaves * 64)
+__attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AF32, EPI>)))
 qgemm_kernel(const GemmArgs args) {
     __shared__ float red[kRedSlots * 256];
 
@@ -115,17 +127,29 @@ qgemm_kernel(const GemmArgs args) {
 
     const PackedLayout L(args.N, args.K, args.flags);
     const int64_t nt = L.nt, G = L.G;
-    const int64_t tile0 = (int64_t)blockIdx.x * NB;
+    // Tile blocks of this workgroup: R consecutive blocks of NB tiles, streamed
+    // back to back through one register pipeline, so a block's first loads are
+    // in flight while the previous block is reduced and stored, and the
+    // problem lookup above is paid once per R blocks.
+    const int R = args.blocks_per_wg;
+    const int64_t tile0 = (int64_t)blockIdx.x * R * NB;
+    const int64_t nblk_all = (nt + NB - 1) / NB;
+    const int64_t blk0 = (int64_t)blockIdx.x * R;
+    const int nblk = (int)(nblk_all - blk0 < R ? nblk_all - blk0 : R);
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)L.bytes);
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(args.a, (uint32_t)args.a_bytes);
 
     // Weight offsets: the lane part is the same for every tile and group; the
     // tile and group part is wave-uniform and goes in soffset.
-    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 2u, vz = (uint32_t)(r16 >> 1);
-    const int nt_here = (int)(nt - tile0 < NB ? (nt - tile0 > 0 ? nt - tile0 : 0) : NB);
-    const int zshift = 4 * (r16 & 1);
+    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 8u, vz = (uint32_t)r16 * 2u;
 
+    // The waves split the groups; every wave runs the same number of steps per
+    // block (ngp, a multiple of S) so that all reach each block's reduction
+    // together.  Steps past a wave's range load out-of-range offsets (zero
+    // codes, scales and activations), so computing them adds exactly 0.
     const int gb = (int)((G * wave) / W), ge = (int)((G * (wave + 1)) / W);
+    const int ngp = (((int)((G + W - 1) / W) + S - 1) / S) * S;
+    const int steps = nblk * ngp;
     const int P = args.P;
     const int spt = 16 / P;                 // slots per M tile
     const int64_t chunk = (int64_t)MT * spt;
@@ -142,37 +166,38 @@ qgemm_kernel(const GemmArgs args) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) res[m][nb] = zero4;
 
-        // S register stages: while one group is multiplied, the loads of the
-        // next S - 1 groups are in flight.  Every load is unconditional; a group
-        // past the end of this wave's range loads out-of-range offsets (zero
-        // codes, scale and activations), so computing it adds exactly 0.
+        // S register stages: while one step is multiplied, the loads of the
+        // next S - 1 steps are in flight.
         Stage<NB, MT, AF32> st[S];
         uint32_t abase[MT];
         int apart[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            abase[m] = kOob;
-            apart[m] = 0;
-        }
-        // The activation lane offsets (abase) are loop-invariant; the group
-        // offset is the same for the whole wave and goes in soffset.
-        auto load_w = [&](Stage<NB, MT, AF32> &q, int g) {
-            const bool in = g < ge;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const bool ok = in && nb < nt_here;
-                const int64_t tg = (tile0 + nb) * G + g;
-                const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
-                const uint32_t os = ok ? (uint32_t)(L.scales_off + tg * 32) : kOobS;
-                const uint32_t oz = ok ? (uint32_t)(L.zeros_off + tg * 8) : kOobS;
-                q.cw[nb] = buf_b128(wr, vc, oc);
-                q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, vs, os, 0);
-                q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, vz, oz, 0);
-            }
+        // Load cursor (wave-uniform): block lr, step li of that block, and the
+        // byte offsets of that step's codes (first tile of the block), scale and
+        // zero records, and activation group.  Offsets advance by a constant
+        // per step and are re-based once per block.
+        const uint32_t tstride = (uint32_t)G * kTileGroupBytes;   // next tile, same group
+        int lr = 0, li = 0;
+        uint32_t loc = 0, los = 0, loz = 0, loa = 0;
+        int lnt = 0;   // tiles of block lr inside the matrix (0..NB)
+        auto rebase = [&]() {
+            const int64_t tile = tile0 + (int64_t)lr * NB;
+            const uint32_t slot = (uint32_t)(tile & (kQuadTiles - 1));
+            loc = (uint32_t)((tile * G + gb) * kTileGroupBytes);
+            los = (uint32_t)L.scale_rec(tile, gb) + 2u * slot;
+            loz = (uint32_t)L.zero_rec(tile, gb) + (slot >> 1);
+            loa = (uint32_t)gb * 128u * ES;
+            lnt = lr < nblk ? (int)(nt - tile < NB ? nt - tile : NB) : 0;
         };
-        auto load_a = [&](Stage<NB, MT, AF32> &q, int g) {
-            const bool in = g < ge;
-            const uint32_t oa = in ? (uint32_t)g * 128u * ES : kOobS;
+        auto load_w = [&](Stage<NB, MT, AF32> &q) {
+            const bool in = lnt > 0 && gb + li < ge;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                q.cw[nb] = buf_b128(wr, vc, in && nb < lnt ? loc + nb * tstride : kOobS);
+            load_meta<NB>(wr, vs, vz, in ? los : kOobS, in ? loz : kOobS, q.sc, q.zb);
+        };
+        auto load_a = [&](Stage<NB, MT, AF32> &q) {
+            const bool in = lnt > 0 && gb + li < ge;
+            const uint32_t oa = in ? loa : kOobS;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -181,7 +206,18 @@ qgemm_kernel(const GemmArgs args) {
                     if constexpr (AF32) q.af[m][s4][AF32 ? 1 : 0] = buf_b128(ar, abase[m] + 32u * s4 * ES + 16, oa);
                 }
         };
-        auto compute = [&](const Stage<NB, MT, AF32> &q) {
+        auto advance = [&]() {
+            loc += kTileGroupBytes;
+            los += kQuadScaleBytes;
+            loz += kQuadZeroBytes;
+            loa += 128u * ES;
+            if (++li == ngp) {
+                li = 0;
+                ++lr;
+                rebase();
+            }
+        };
+        auto compute = [&](const Stage<NB, MT, AF32> &q, int zshift) {
             bf16x8 a[MT][4];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -198,10 +234,10 @@ qgemm_kernel(const GemmArgs args) {
                 const bf16x8 b1 = as_bf16x8(unpack_codes_bf16(q.cw[nb].y));
                 const bf16x8 b2 = as_bf16x8(unpack_codes_bf16(q.cw[nb].z));
                 const bf16x8 b3 = as_bf16x8(unpack_codes_bf16(q.cw[nb].w));
-                const uint32_t z = (q.zb[nb] >> zshift) & 15u;
+                const uint32_t z = (q.zb >> (zshift + 4 * nb)) & 15u;
                 const uint32_t zz = (0x4300u | z) * 0x00010001u;   // bf16 pair (128+z, 128+z)
                 const bf16x8 bz = as_bf16x8(make_uint4(zz, zz, zz, zz));
-                const float sc = f16_bits_to_f32((uint16_t)q.sc[nb]);
+                const float sc = f16_bits_to_f32((uint16_t)(q.sc[nb >> 1] >> (16 * (nb & 1))));
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m >= m_used) break;
@@ -218,97 +254,130 @@ qgemm_kernel(const GemmArgs args) {
                 }
             }
         };
-        if (gb < ge) {
-            // weights first: they come from HBM; the activation rows need the
-            // slot -> row lookups resolved above, and come from cache
+
+        // ---- reduction of the waves' partial sums of block r in a fixed
+        // order, epilogue and store
+        auto finish_block = [&](int r) {
 #pragma unroll
-            for (int q = 0; q < S; ++q) load_w(st[q], gb + q);
-            // ---- byte offset of this lane's activation row (operand row r16 of each M tile)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int64_t slot = c0 + (int64_t)m * spt + r16 / P;
-                const int part = r16 % P;
-                const bool ok = (r16 < spt * P) && slot < n;
-                const int64_t slot_c = ok ? slot : 0;
-                const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
-                const int64_t row = AF32 ? src : src * P + part;
-                apart[m] = part;
-                abase[m] = ok ? (uint32_t)((row * args.lda + 8 * j) * ES) : kOob;
-            }
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int q = 0; q < S; ++q) load_a(st[q], gb + q);
-            for (int g = gb; g < ge; g += S) {
+                    for (int v = 0; v < 4; ++v)
+                        red[((wave * MT + m) * NB + nb) * 256 + v * 64 + lane] = res[m][nb][v];
+            __syncthreads();
+
+            const int64_t tile_b = tile0 + (int64_t)r * NB;
+            const int pairs = EPI == QI4_EPI_SILU_MUL ? NB / 2 : NB;
+            const int items = MT * pairs * 64;
+            for (int it = threadIdx.x; it < items; it += blockDim.x) {
+                const int l = it & 63;
+                const int rest = it >> 6;
+                const int pi = rest % pairs;
+                const int m = rest / pairs;
+                const int nbA = EPI == QI4_EPI_SILU_MUL ? 2 * pi : pi;
+                float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int ww = 0; ww < W; ++ww) {
 #pragma unroll
-                for (int q = 0; q < S; ++q) {
-                    compute(st[q]);
-                    load_w(st[q], g + S + q);
-                    load_a(st[q], g + S + q);
+                    for (int v = 0; v < 4; ++v) {
+                        a4[v] += red[((ww * MT + m) * NB + nbA) * 256 + v * 64 + l];
+                        if (EPI == QI4_EPI_SILU_MUL)
+                            b4[v] += red[((ww * MT + m) * NB + nbA + 1) * 256 + v * 64 + l];
+                    }
                 }
+                const int col = l & 15;
+                const int64_t tile = tile_b + nbA;
+                int64_t oc;
+                if (EPI == QI4_EPI_SILU_MUL)
+                    oc = (tile >> 1) * 16 + col;
+                else
+                    oc = tile < nt ? tile_row(tile, col, args.N, args.flags) : -1;
+                if (oc < 0 || oc >= args.n_out) continue;
+                const int rbase = 4 * (l >> 4);
+                // (static register indices: v0 and p are unrolled, P is 1, 2 or 4)
+#pragma unroll
+                for (int v0 = 0; v0 < 4; ++v0) {
+                    if (v0 % P != 0) continue;
+                    const int rr = rbase + v0;
+                    if (rr / P >= spt) continue;
+                    const int64_t slot = c0 + (int64_t)m * spt + rr / P;
+                    if (slot >= n) continue;
+                    float val = 0.f, uval = 0.f;
+#pragma unroll
+                    for (int p = 0; v0 + p < 4; ++p) {
+                        if (p >= P) break;
+                        val += a4[v0 + p];
+                        uval += b4[v0 + p];
+                    }
+                    if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
+                    const int64_t dst = row0 + slot;
+                    if (args.out_mode == OUT_F32) {
+                        static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
+                    } else if (args.out_mode == OUT_BF16) {
+                        static_cast<uint16_t *>(args.out)[dst * args.ldo + oc] = (uint16_t)f32_to_bf16_rne(val);
+                    } else {
+                        const uint32_t hi = f32_to_bf16_rne(val);
+                        const uint32_t lo = f32_to_bf16_rne(val - bf16_to_f32(hi));
+                        uint16_t *o = static_cast<uint16_t *>(args.out);
+                        o[(dst * 2) * args.ldo + oc] = (uint16_t)hi;
+                        o[(dst * 2 + 1) * args.ldo + oc] = (uint16_t)lo;
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) res[m][nb] = zero4;
+        };
+
+        // weights first: they come from HBM; the activation rows need the
+        // slot -> row lookups, and come from cache
+        rebase();
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            load_w(st[q]);
+            advance();
+        }
+        // ---- byte offset of this lane's activation row (operand row r16 of each M tile)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int64_t slot = c0 + (int64_t)m * spt + r16 / P;
+            const int part = r16 % P;
+            const bool ok = (r16 < spt * P) && slot < n;
+            const int64_t slot_c = ok ? slot : 0;
+            const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
+            const int64_t row = AF32 ? src : src * P + part;
+            apart[m] = part;
+            abase[m] = ok ? (uint32_t)((row * args.lda + 8 * j) * ES) : kOob;
+        }
+        lr = 0;
+        li = 0;
+        rebase();
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            load_a(st[q]);
+            advance();
+        }
+        // (lr, li) now points S steps ahead of the step being computed, which
+        // is step ci of block cr
+        int cr = 0, ci = 0;
+        for (int s0 = 0; s0 < steps; s0 += S) {
+            const int zshift = NB == 1 ? 4 * (int)((tile0 + (int64_t)cr * NB) & 1) : 0;
+#pragma unroll
+            for (int q = 0; q < S; ++q) {
+                compute(st[q], zshift);
+                load_w(st[q]);
+                load_a(st[q]);
+                advance();
+            }
+            ci += S;   // S divides ngp: a block ends at an iteration boundary
+            if (ci == ngp) {
+                finish_block(cr);
+                ci = 0;
+                ++cr;
             }
         }
-
-        // ---- fixed-order reduction of the waves' partial sums
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    red[((wave * MT + m) * NB + nb) * 256 + v * 64 + lane] = res[m][nb][v];
-        __syncthreads();
-
-        const int pairs = EPI == QI4_EPI_SILU_MUL ? NB / 2 : NB;
-        const int items = MT * pairs * 64;
-        for (int it = threadIdx.x; it < items; it += blockDim.x) {
-            const int l = it & 63;
-            const int rest = it >> 6;
-            const int pi = rest % pairs;
-            const int m = rest / pairs;
-            const int nbA = EPI == QI4_EPI_SILU_MUL ? 2 * pi : pi;
-            float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int ww = 0; ww < W; ++ww) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    a4[v] += red[((ww * MT + m) * NB + nbA) * 256 + v * 64 + l];
-                    if (EPI == QI4_EPI_SILU_MUL)
-                        b4[v] += red[((ww * MT + m) * NB + nbA + 1) * 256 + v * 64 + l];
-                }
-            }
-            const int col = l & 15;
-            const int64_t tile = tile0 + nbA;
-            int64_t oc;
-            if (EPI == QI4_EPI_SILU_MUL)
-                oc = (tile >> 1) * 16 + col;
-            else
-                oc = tile < nt ? tile_row(tile, col, args.N, args.flags) : -1;
-            if (oc < 0 || oc >= args.n_out) continue;
-            const int rbase = 4 * (l >> 4);
-            for (int v0 = 0; v0 < 4; v0 += P) {
-                const int r = rbase + v0;
-                if (r / P >= spt) continue;
-                const int64_t slot = c0 + (int64_t)m * spt + r / P;
-                if (slot >= n) continue;
-                float val = 0.f, uval = 0.f;
-                for (int p = 0; p < P; ++p) {
-                    val += a4[v0 + p];
-                    uval += b4[v0 + p];
-                }
-                if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
-                const int64_t dst = row0 + slot;
-                if (args.out_mode == OUT_F32) {
-                    static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
-                } else if (args.out_mode == OUT_BF16) {
-                    static_cast<uint16_t *>(args.out)[dst * args.ldo + oc] = (uint16_t)f32_to_bf16_rne(val);
-                } else {
-                    const uint32_t hi = f32_to_bf16_rne(val);
-                    const uint32_t lo = f32_to_bf16_rne(val - bf16_to_f32(hi));
-                    uint16_t *o = static_cast<uint16_t *>(args.out);
-                    o[(dst * 2) * args.ldo + oc] = (uint16_t)hi;
-                    o[(dst * 2 + 1) * args.ldo + oc] = (uint16_t)lo;
-                }
-            }
-        }
-        __syncthreads();
     }
 }
 
@@ -335,11 +404,11 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 
 // Launch shape, from sweeps on MI355X over the decode workloads (dense Llama-7B
 // and 5120/13824 shapes, DeepSeek-V3-shaped experts at T = 1, 8, 32):
-//  * W waves split K; about ten 128-wide groups per wave for a single matrix,
-//    and two waves per workgroup when many expert problems already fill the chip;
-//  * NB = 2 tiles per workgroup (the gate/up pair) unless a single matrix of
-//    fewer than 320 tiles needs more workgroups (NB = 1); grouped gate/up GEMMs
-//    take NB = 4, with four waves when the grid is small;
+//  * W waves split K; about ten 128-wide groups per wave for a single matrix;
+//  * a single matrix takes NB = 2 tiles per workgroup (the gate/up pair)
+//    unless it has fewer than 320 tiles and needs more workgroups (NB = 1);
+//    the grouped expert GEMMs take a whole quad (NB = 4), and the down
+//    projection two quads per workgroup (R = 2) once the grid is large;
 //  * one M tile per pass (16 activation rows), two for a single matrix with
 //    more rows.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t st) {
@@ -355,28 +424,38 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     // (a single matrix takes two tiles per workgroup from 320 tiles up: cold-cache
     // sweeps of 4096..22016-row matrices put the crossover between 256 and 320)
     int NB = (silu || ceil_div(nt, 2) * n_problems >= 160) ? 2 : 1;
-    int W;
+    int W, R = 1;   // R: tile blocks streamed back to back by one workgroup
     if (n_problems > 1) {
-        // grouped expert GEMMs: the gate/up pairs stream best four tiles per
-        // workgroup, split over more waves when the grid is small
-        if (silu) NB = 4;
-        W = (silu && ceil_div(nt, NB) * n_problems < 8192) ? 4 : 2;
+        // grouped expert GEMMs: four tiles (one quad) per block; gate/up over
+        // four waves; down over four waves and two blocks per workgroup when
+        // the grid is large, else two waves
+        NB = 4;
+        if (silu) {
+            W = 4;
+        } else if (ceil_div(nt, NB) * n_problems >= 12000) {
+            W = 4;
+            R = 2;
+        } else {
+            W = 2;
+        }
     } else {
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
     }
     while (W > 1 && W * MT * NB > kRedSlots) W /= 2;
-    const int64_t gx = ceil_div(nt, NB);
+    GemmArgs a = args;
+    a.blocks_per_wg = R;
+    const int64_t gx = ceil_div(ceil_div(nt, NB), R);
     if (gx > 0x7fffffff || n_problems > 65535) return QI4_ERR_SHAPE;
     dim3 grid((unsigned)gx, (unsigned)n_problems);
     const int threads = W * 64;
     if (MT == 1) {
-        if (NB == 4) return launch_cfg<4, 1, 2>(args, grid, threads, st);
-        if (NB == 2) return launch_cfg<2, 1, 2>(args, grid, threads, st);
-        return launch_cfg<1, 1, 2>(args, grid, threads, st);
+        if (NB == 4) return launch_cfg<4, 1, 2>(a, grid, threads, st);
+        if (NB == 2) return launch_cfg<2, 1, 2>(a, grid, threads, st);
+        return launch_cfg<1, 1, 2>(a, grid, threads, st);
     }
-    if (NB == 2) return launch_cfg<2, 2, 2>(args, grid, threads, st);
-    return launch_cfg<1, 2, 2>(args, grid, threads, st);
+    if (NB == 2) return launch_cfg<2, 2, 2>(a, grid, threads, st);
+    return launch_cfg<1, 2, 2>(a, grid, threads, st);
 }
 
 }  // namespace qi4

@@ -40,24 +40,30 @@ pack_codes_kernel(const uint8_t *__restrict__ qweight, int64_t N, int64_t K, int
     }
 }
 
+// One thread per (quad, group, row): the scales and zeros of that row in the
+// quad's four tiles (missing tiles and rows hold 0).
 __global__ void __launch_bounds__(kThreads)
 pack_meta_kernel(const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-                 int64_t N, int64_t K, int flags, uint16_t *__restrict__ sc_out,
-                 uint8_t *__restrict__ zr_out, int64_t n_tg) {
+                 int64_t N, int64_t K, int flags, int64_t nt, uint64_t *__restrict__ sc_out,
+                 uint16_t *__restrict__ zr_out, int64_t n_qg) {
     const int64_t G = K / kGroup;
-    for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < n_tg * 16;
+    for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < n_qg * 16;
          idx += (int64_t)gridDim.x * kThreads) {
         const int r = idx & 15;
-        const int64_t tg = idx >> 4;
-        const int64_t t = tg / G, g = tg % G;
-        const int64_t row = tile_row(t, r, N, flags);
-        sc_out[idx] = row >= 0 ? scales[row * G + g] : (uint16_t)0;
-        if ((r & 1) == 0) {
-            const int64_t row1 = tile_row(t, r + 1, N, flags);
-            const uint32_t z0 = row >= 0 ? (zeros[row * G + g] & 15u) : 0u;
-            const uint32_t z1 = row1 >= 0 ? (zeros[row1 * G + g] & 15u) : 0u;
-            zr_out[tg * 8 + (r >> 1)] = (uint8_t)(z0 | (z1 << 4));
+        const int64_t qg = idx >> 4;
+        const int64_t q = qg / G, g = qg % G;
+        uint64_t sv = 0;
+        uint32_t zv = 0;
+#pragma unroll
+        for (int s = 0; s < kQuadTiles; ++s) {
+            const int64_t t = q * kQuadTiles + s;
+            const int64_t row = t < nt ? tile_row(t, r, N, flags) : -1;
+            if (row < 0) continue;
+            sv |= (uint64_t)scales[row * G + g] << (16 * s);
+            zv |= (zeros[row * G + g] & 15u) << (4 * s);
         }
+        sc_out[idx] = sv;
+        zr_out[idx] = (uint16_t)zv;
     }
 }
 
@@ -84,30 +90,35 @@ unpack_codes_kernel(const uint32_t *__restrict__ in, int64_t N, int64_t K, int f
 }
 
 __global__ void __launch_bounds__(kThreads)
-unpack_meta_kernel(const uint16_t *__restrict__ sc_in, const uint8_t *__restrict__ zr_in,
-                   int64_t N, int64_t K, int flags, uint16_t *__restrict__ scales,
-                   uint8_t *__restrict__ zeros, int64_t n_tg) {
+unpack_meta_kernel(const uint64_t *__restrict__ sc_in, const uint16_t *__restrict__ zr_in,
+                   int64_t N, int64_t K, int flags, int64_t nt, uint16_t *__restrict__ scales,
+                   uint8_t *__restrict__ zeros, int64_t n_qg) {
     const int64_t G = K / kGroup;
-    for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < n_tg * 16;
+    for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < n_qg * 16;
          idx += (int64_t)gridDim.x * kThreads) {
         const int r = idx & 15;
-        const int64_t tg = idx >> 4;
-        const int64_t t = tg / G, g = tg % G;
-        const int64_t row = tile_row(t, r, N, flags);
-        if (row < 0) continue;
-        scales[row * G + g] = sc_in[idx];
-        zeros[row * G + g] = (zr_in[tg * 8 + (r >> 1)] >> (4 * (r & 1))) & 15;
+        const int64_t qg = idx >> 4;
+        const int64_t q = qg / G, g = qg % G;
+        const uint64_t sv = sc_in[idx];
+        const uint32_t zv = zr_in[idx];
+#pragma unroll
+        for (int s = 0; s < kQuadTiles; ++s) {
+            const int64_t t = q * kQuadTiles + s;
+            const int64_t row = t < nt ? tile_row(t, r, N, flags) : -1;
+            if (row < 0) continue;
+            scales[row * G + g] = (uint16_t)(sv >> (16 * s));
+            zeros[row * G + g] = (uint8_t)((zv >> (4 * s)) & 15u);
+        }
     }
 }
 
 // One thread per packed dword: 8 consecutive weights of one row in float32.
 __global__ void __launch_bounds__(kThreads)
 dequant_kernel(const uint8_t *__restrict__ packed, int64_t N, int64_t K, int flags,
-               float *__restrict__ w, int64_t n_dwords, int64_t scales_off, int64_t zeros_off) {
+               float *__restrict__ w, int64_t n_dwords) {
     const int64_t G = K / kGroup;
+    const PackedLayout L(N, K, flags);
     const uint32_t *codes = reinterpret_cast<const uint32_t *>(packed);
-    const uint16_t *sc = reinterpret_cast<const uint16_t *>(packed + scales_off);
-    const uint8_t *zr = packed + zeros_off;
     for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < n_dwords;
          idx += (int64_t)gridDim.x * kThreads) {
         const int s = idx & 3;
@@ -119,8 +130,9 @@ dequant_kernel(const uint8_t *__restrict__ packed, int64_t N, int64_t K, int fla
         if (row < 0) continue;
         const int64_t k0 = g * kGroup + 32 * s + 8 * j;
         const uint32_t d = codes[idx];
-        const float scale = f16_bits_to_f32(sc[tg * 16 + r]);
-        const int z = (zr[tg * 8 + (r >> 1)] >> (4 * (r & 1))) & 15;
+        const float scale = f16_bits_to_f32(
+            *reinterpret_cast<const uint16_t *>(packed + L.scale_rec(t, g) + 8 * r + 2 * (t & 3)));
+        const int z = (packed[L.zero_rec(t, g) + 2 * r + ((t & 3) >> 1)] >> (4 * (t & 1))) & 15;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -165,9 +177,9 @@ int qi4_pack(const uint8_t *qweight, const uint16_t *scales, const uint8_t *zero
     pack_codes_kernel<<<grid_for(n_dwords), kThreads, 0, st>>>(
         qweight, N, K, flags, reinterpret_cast<uint32_t *>(p), n_dwords);
     if ((rc = launch_status())) return rc;
-    pack_meta_kernel<<<grid_for(L.nt * L.G * 16), kThreads, 0, st>>>(
-        scales, zeros, N, K, flags, reinterpret_cast<uint16_t *>(p + L.scales_off),
-        p + L.zeros_off, L.nt * L.G);
+    pack_meta_kernel<<<grid_for(L.nq * L.G * 16), kThreads, 0, st>>>(
+        scales, zeros, N, K, flags, L.nt, reinterpret_cast<uint64_t *>(p + L.scales_off),
+        reinterpret_cast<uint16_t *>(p + L.zeros_off), L.nq * L.G);
     return launch_status();
 }
 
@@ -189,9 +201,10 @@ int qi4_unpack(const void *packed, int64_t N, int64_t K, int group_size, int fla
     unpack_codes_kernel<<<grid_for(n_dwords), kThreads, 0, st>>>(
         reinterpret_cast<const uint32_t *>(p), N, K, flags, qweight, n_dwords);
     if ((rc = launch_status())) return rc;
-    unpack_meta_kernel<<<grid_for(L.nt * L.G * 16), kThreads, 0, st>>>(
-        reinterpret_cast<const uint16_t *>(p + L.scales_off), p + L.zeros_off, N, K, flags,
-        scales, zeros, L.nt * L.G);
+    unpack_meta_kernel<<<grid_for(L.nq * L.G * 16), kThreads, 0, st>>>(
+        reinterpret_cast<const uint64_t *>(p + L.scales_off),
+        reinterpret_cast<const uint16_t *>(p + L.zeros_off), N, K, flags, L.nt, scales, zeros,
+        L.nq * L.G);
     return launch_status();
 }
 
@@ -206,8 +219,7 @@ int qi4_dequant_f32(const void *packed, int64_t N, int64_t K, int group_size, in
     if ((rc = check_device())) return rc;
     const int64_t n_dwords = L.nt * L.G * 256;
     dequant_kernel<<<grid_for(n_dwords), kThreads, 0, as_stream(stream)>>>(
-        static_cast<const uint8_t *>(packed), N, K, flags, w, n_dwords, L.scales_off,
-        L.zeros_off);
+        static_cast<const uint8_t *>(packed), N, K, flags, w, n_dwords);
     return launch_status();
 }
 

@@ -272,9 +272,11 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
 
     // Weight offsets: the lane part is the same for every tile and group; the
     // tile and group part is wave-uniform and goes in soffset (scalar registers).
-    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 2u, vz = (uint32_t)(r16 >> 1);
+    // A wave's NBW tiles are aligned inside one quad (tile0 % NBW == 0).
+    const uint32_t slot0 = (uint32_t)(tile0 & (kQuadTiles - 1));
+    const uint32_t vc = (uint32_t)lane * 16u, vs = (uint32_t)r16 * 8u + 2u * slot0,
+                   vz = (uint32_t)r16 * 2u + (slot0 >> 1);
     const int nt_here = (int)(nt - tile0 < NBW ? (nt - tile0 > 0 ? nt - tile0 : 0) : NBW);
-    const int zshift = 4 * (r16 & 1);
 
     // 16-row subtiles of this tile that hold rows (uniform).
     const int m_used = (int)((n - m0 + 15) / 16 < MS ? (n - m0 + 15) / 16 : MS);
@@ -322,21 +324,19 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     };
     struct WStage {
         uint4 cw[NBW];
-        uint32_t sc[NBW], zb[NBW];
+        uint32_t sc[(NBW + 1) / 2], zb;
     };
     auto load_w = [&](WStage &q, int g) {
-        const bool in = g < G;
+        const bool in = g < G && nt_here > 0;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
             const bool ok = in && nb < nt_here;
             const int64_t tg = (tile0 + nb) * G + g;
             const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
-            const uint32_t os = ok ? (uint32_t)(L.scales_off + tg * 32) : kOobS;
-            const uint32_t oz = ok ? (uint32_t)(L.zeros_off + tg * 8) : kOobS;
             q.cw[nb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, vc, oc, 0));
-            q.sc[nb] = __builtin_amdgcn_raw_buffer_load_b16(wr, vs, os, 0);
-            q.zb[nb] = __builtin_amdgcn_raw_buffer_load_b8(wr, vz, oz, 0);
         }
+        load_meta<NBW>(wr, vs, vz, in ? (uint32_t)L.scale_rec(tile0, g) : kOobS,
+                       in ? (uint32_t)L.zero_rec(tile0, g) : kOobS, q.sc, q.zb);
     };
 
     f32x4 acc[MS][NBW];
@@ -346,14 +346,16 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
         for (int nb = 0; nb < NBW; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // 16 (q - zero) scale can exceed binary16 once |scale| >= 256.  On the fast
-    // pass each wave scans the scales of its tiles (contiguous: nt_here * G * 32
-    // bytes) while the prologue's requests are in flight; a workgroup that
-    // finds such a scale (or inf/NaN) records its tile in the deferred list and
-    // leaves it to the plain-operand pass.
+    // pass the waves scan the scale records of their tiles' quads (contiguous:
+    // G * 128 bytes per quad; of two waves sharing a quad, the first scans it)
+    // while the prologue's requests are in flight; a workgroup that finds such
+    // a scale (or inf/NaN) records its tile in the deferred list and leaves it
+    // to the plain-operand pass.
     bool big = false;
     if constexpr (!WIDE) {
-        const uint32_t span = (uint32_t)(nt_here * G * kScaleBytes);
-        const uint32_t base = (uint32_t)(L.scales_off + tile0 * G * kScaleBytes);
+        const bool scans = nt_here > 0 && (tile0 & (kQuadTiles - 1)) == 0;
+        const uint32_t span = scans ? (uint32_t)(G * kQuadScaleBytes) : 0u;
+        const uint32_t base = (uint32_t)L.scale_rec(tile0, 0);
         for (uint32_t o = 0; o < span; o += 1024) {
             const uint32_t lo = o + (uint32_t)lane * 16u;
             const uint4 v = __builtin_bit_cast(
@@ -403,11 +405,11 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
             uint32_t negz[NBW], negz16[NBW], s2[NBW];
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
-                const uint32_t z = (q.zb[nb] >> zshift) & 15u;
+                const uint32_t z = (q.zb >> (4 * nb)) & 15u;
                 // fp16 -(1024 + z) and -(1024 + 16 z) in both halves; scale in both halves
                 negz[nb] = (0xE400u | z) * 0x00010001u;
                 negz16[nb] = (0xE400u | (z << 4)) * 0x00010001u;
-                s2[nb] = (q.sc[nb] & 0xFFFFu) * 0x00010001u;
+                s2[nb] = ((q.sc[nb >> 1] >> (16 * (nb & 1))) & 0xFFFFu) * 0x00010001u;
             }
             auto deq = [&](int s, f16x8 (&b)[NBW]) {
 #pragma unroll

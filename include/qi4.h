@@ -47,10 +47,13 @@
  * Packed (device) format, produced by qi4_pack: rows are cut into 16-row tiles
  * (with QI4_PACK_GATEUP, tile 2m holds gate rows 16m.. and tile 2m+1 the up rows
  * with the same index, so a tile pair yields 16 outputs of SiLU(gate)*up).
- * Let nt = number of tiles and G = K/128.  Three regions follow each other:
+ * Let nt = number of tiles, G = K/128, and nq = ceil(nt/4) "quads" of four
+ * consecutive tiles (tile t is slot t%4 of quad t/4).  Three regions follow
+ * each other:
  *    codes  nt*G*1024 bytes  [tile][group][lane 0..63][16 bytes]
- *    scales nt*G*32 bytes    [tile][group][row 0..15] binary16
- *    zeros  nt*G*8 bytes     [tile][group][8 bytes] row r in nibble r&1 of byte r/2
+ *    scales nq*G*128 bytes   [quad][group][row 0..15][slot 0..3] binary16
+ *    zeros  nq*G*32 bytes    [quad][group][row 0..15][2 bytes], slot s in nibble s
+ * and the total is rounded up to a multiple of 256 bytes.
  * Lane 16*j + r of a tile/group block holds row r's codes for k in
  * 128*g + 32*s + 8*j + [0, 8) in its dword s (s = 0..3), so one 16-byte load per
  * lane brings a wave exactly one group of 16 rows.  Missing rows (N not a multiple

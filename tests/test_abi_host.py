@@ -47,12 +47,16 @@ def test_version_and_status_strings(q):
 
 def test_packed_bytes(q):
     L = q.lib()
-    # 16-row tiles x 128-wide groups: 1024 B codes + 32 B scales + 8 B zeros each
-    assert L.qi4_packed_bytes(16, 128, 128, 0) == 1280  # 1064 rounded up to 256
-    assert L.qi4_packed_bytes(4096, 4096, 128, 0) == 256 * 32 * 1064
-    assert L.qi4_packed_bytes(17, 256, 128, 0) == ((2 * 2 * 1064 + 255) // 256) * 256
+    # 16-row tiles x 128-wide groups: 1024 B of codes each; per group, the
+    # scales (128 B) and zeros (32 B) of each quad of 4 tiles (the last quad
+    # padded); the total rounded up to 256 B
+    def size(nt, G):
+        return ((nt * G * 1024 + -(-nt // 4) * G * 160 + 255) // 256) * 256
+    assert L.qi4_packed_bytes(16, 128, 128, 0) == 1280 == size(1, 1)  # 1184 rounded up
+    assert L.qi4_packed_bytes(4096, 4096, 128, 0) == 256 * 32 * 1064 == size(256, 32)
+    assert L.qi4_packed_bytes(17, 256, 128, 0) == 4608 == size(2, 2)
     # gate/up: each half padded to whole tiles
-    assert L.qi4_packed_bytes(48, 128, 128, 1) == ((4 * 1064 + 255) // 256) * 256
+    assert L.qi4_packed_bytes(48, 128, 128, 1) == size(4, 1)
     assert L.qi4_packed_bytes(16, 100, 128, 0) == -2
     assert L.qi4_packed_bytes(16, 128, 64, 0) == -4
     assert L.qi4_packed_bytes(17, 128, 128, 1) == -2
