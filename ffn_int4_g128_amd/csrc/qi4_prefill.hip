@@ -16,8 +16,8 @@
 //    up to 16, 32 or 64 rows.  Big tiles run on MFMA-bound workgroups (4 waves
 //    x 64 weight rows, two-stage pipeline, two workgroups per CU); small tiles
 //    run on weight-stream-bound workgroups (8 waves x 32 weight rows,
-//    four-stage pipeline, 16 waves per CU), on a side stream so that the two
-//    kinds share the chip;
+//    four-stage pipeline, 16 waves per CU), on side streams so that all of
+//    them share the chip;
 //  * the activation tile of each group is copied from memory straight into LDS
 //    (buffer loads with the LDS bit), each 4-lane quad reading 64 contiguous
 //    bytes, in a rotated order that keeps the MFMA operand reads free of bank
@@ -604,18 +604,20 @@ int64_t prefill_max_deferred(int64_t N, int flags, const PrefillTiles &m) {
     return gx * (ceil_div(m.big, 8) + 3 * ceil_div(m.small, 8)) * 8;
 }
 
-// The small-tile kernels run on a side stream of the device, forked from and
-// joined back to the caller's stream with events, so that they share the chip
-// with the big-tile kernel (one streams weights, the other keeps the MFMAs
-// busy).  One side stream and event pair per device, created on first use and
-// kept for the life of the process; a mutex makes each fork/join sequence of
-// enqueues atomic, so calls on different streams cannot pick up each other's
-// events.
+// The small-tile kernels run on side streams of the device, one per height
+// class, forked from and joined back to the caller's stream with events, so
+// that all of them share the chip with the big-tile kernel (one kind streams
+// weights, the other keeps the MFMAs busy; a class run after the big tiles
+// would leave most of the chip idle).  Three side streams and their events per
+// device, created on first use and kept for the life of the process; a mutex
+// makes each fork/join sequence of enqueues atomic, so calls on different
+// streams cannot pick up each other's events.
 namespace {
+constexpr int kSideStreams = 3;
 struct SideStream {
     std::mutex mu;
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipStream_t s[kSideStreams] = {};
+    hipEvent_t fork = nullptr, join[kSideStreams] = {};
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
@@ -626,19 +628,26 @@ int side_stream(SideStream **out) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QI4_ERR_HIP;
     SideStream &ss = g_side[dev];
     std::lock_guard<std::mutex> lk(g_side_init);
-    if (!ss.s) {
-        hipStream_t s = nullptr;
-        hipEvent_t f = nullptr, j = nullptr;
-        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return QI4_ERR_HIP;
-        if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    if (!ss.fork) {
+        hipStream_t s[kSideStreams] = {};
+        hipEvent_t f = nullptr, j[kSideStreams] = {};
+        bool ok = hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess;
+        for (int i = 0; ok && i < kSideStreams; ++i)
+            ok = hipStreamCreateWithFlags(&s[i], hipStreamNonBlocking) == hipSuccess &&
+                 hipEventCreateWithFlags(&j[i], hipEventDisableTiming) == hipSuccess;
+        if (!ok) {
+            for (int i = 0; i < kSideStreams; ++i) {
+                if (j[i]) (void)hipEventDestroy(j[i]);
+                if (s[i]) (void)hipStreamDestroy(s[i]);
+            }
             if (f) (void)hipEventDestroy(f);
-            (void)hipStreamDestroy(s);
             return QI4_ERR_HIP;
         }
+        for (int i = 0; i < kSideStreams; ++i) {
+            ss.s[i] = s[i];
+            ss.join[i] = j[i];
+        }
         ss.fork = f;
-        ss.join = j;
-        ss.s = s;
     }
     *out = &ss;
     return QI4_OK;
@@ -653,15 +662,18 @@ int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsign
     {
         std::lock_guard<std::mutex> lk(ss->mu);
         if (hipEventRecord(ss->fork, st) != hipSuccess) return QI4_ERR_HIP;
-        if (hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) return QI4_ERR_HIP;
-        prefill_small_kernel<EPI, 0><<<gs, ts, 0, ss->s>>>(a);
-        prefill_small_kernel<EPI, 1><<<gs, ts, 0, ss->s>>>(a);
-        prefill_small_kernel<EPI, 2><<<gs, ts, 0, ss->s>>>(a);
+        for (int i = 0; i < kSideStreams; ++i)
+            if (hipStreamWaitEvent(ss->s[i], ss->fork, 0) != hipSuccess) return QI4_ERR_HIP;
+        prefill_small_kernel<EPI, 0><<<gs, ts, 0, ss->s[0]>>>(a);
+        prefill_small_kernel<EPI, 1><<<gs, ts, 0, ss->s[1]>>>(a);
+        prefill_small_kernel<EPI, 2><<<gs, ts, 0, ss->s[2]>>>(a);
         if ((rc = launch_status())) return rc;
         prefill_big_kernel<EPI><<<gb, tb, 0, st>>>(a);
         if ((rc = launch_status())) return rc;
-        if (hipEventRecord(ss->join, ss->s) != hipSuccess) return QI4_ERR_HIP;
-        if (hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) return QI4_ERR_HIP;
+        for (int i = 0; i < kSideStreams; ++i) {
+            if (hipEventRecord(ss->join[i], ss->s[i]) != hipSuccess) return QI4_ERR_HIP;
+            if (hipStreamWaitEvent(st, ss->join[i], 0) != hipSuccess) return QI4_ERR_HIP;
+        }
     }
     // tiles deferred by either kind, after both
     prefill_wide_kernel<EPI><<<512, tb, 0, st>>>(a);   // two workgroups per CU

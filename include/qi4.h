@@ -32,8 +32,8 @@
  *    multiple of 128 (QI4_ERR_SHAPE).  The device must be gfx950
  *    (QI4_ERR_UNSUPPORTED otherwise).
  *  - Calls are reentrant.  The global state is a cached per-device
- *    architecture check and, for MoE batches of 128 tokens or more, one
- *    internal side stream per device (with an event pair), created on first
+ *    architecture check and, for MoE batches of 128 tokens or more, three
+ *    internal side streams per device (with their events), created on first
  *    use and kept for the life of the process: part of such a call runs there,
  *    ordered after the work already enqueued on `stream` and before anything
  *    enqueued on `stream` after the call, so the caller sees one stream.
