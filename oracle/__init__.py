@@ -213,6 +213,7 @@ def moe(x64: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: dict, shared: 
     ``experts`` holds canonical arrays for all E routed experts:
     gu_q [E][2I][H/2], gu_s/gu_z [E][2I][H/G], dn_q [E][H][I/2], dn_s/dn_z [E][H][I/G].
     ``shared`` holds the same keys for one expert (no leading E), or None.
+    ``group`` 0 means one group per row of each matrix (H for gate/up, I for down).
     """
     x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(-1, H)
     T = x64.shape[0]

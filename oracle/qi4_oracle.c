@@ -278,18 +278,18 @@ int qi4o_sort(const int32_t *ids, int64_t T, int k, int64_t E,
 /* One expert on one token: h = SiLU(W_g x) * (W_u x), y = W_d h, in double.
    A (may be NULL) receives the first-order tolerance of y:
    A[n] = sum_i |W_d[n][i]| * (c*|h_i| + tol_h[i]). */
-static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t G, double c,
-                      const uint8_t *gq, const uint16_t *gs, const uint8_t *gz,
+static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t Ggu, int64_t Gdn,
+                      double c, const uint8_t *gq, const uint16_t *gs, const uint8_t *gz,
                       const uint8_t *dq, const uint16_t *ds, const uint8_t *dz,
                       double *y, double *A, double *h, double *tol_h, int threads)
 {
-    int rc = qi4o_gate_up_silu(xt, 1, H, gq, gs, gz, I, G, c, h, tol_h, threads);
+    int rc = qi4o_gate_up_silu(xt, 1, H, gq, gs, gz, I, Ggu, c, h, tol_h, threads);
     if (rc) return rc;
 #pragma omp parallel for num_threads(threads) schedule(static)
     for (int64_t n = 0; n < H; n++) {
         double acc = 0.0, a = 0.0;
         for (int64_t i = 0; i < I; i++) {
-            double w = w_at(dq, ds, dz, I, G, n, i);
+            double w = w_at(dq, ds, dz, I, Gdn, n, i);
             acc += w * h[i];
             a += fabs(w) * (c * fabs(h[i]) + tol_h[i]);
         }
@@ -302,7 +302,9 @@ static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t G, double 
 /* out[t] = sum_{j<k} p[t][j] * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t)   (R10, R11)
  *
  * Routed expert e uses gate/up block gu_*[e] (2I x H, groups along H) and down
- * block dn_*[e] (H x I, groups along I).  The shared expert (sh_*) is skipped
+ * block dn_*[e] (H x I, groups along I); G = 0 means one group per row of each
+ * matrix (H for gate/up, I for down: the plain, per-channel int4 that the
+ * fastllm README names beside the grouped int4g).  The shared expert (sh_*) is skipped
  * when sh_gu_q is NULL.  tol (may be NULL) is the first-order tolerance
  * sum_j p_j*A_{e_j} + A_shared + eps_p * sum_j |y_{e_j}| with c the per-linear
  * relative factor and eps_p a bound on the error of the combine weights.
@@ -315,10 +317,11 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
              const uint8_t *sh_dn_q, const uint16_t *sh_dn_s, const uint8_t *sh_dn_z,
              int64_t G, double c, double eps_p, double *out, double *tol, int threads)
 {
-    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || G <= 0 || H % G || I % G) return -2;
+    const int64_t Ggu = G ? G : H, Gdn = G ? G : I;
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || G < 0 || H % Ggu || I % Gdn) return -2;
     if (threads < 1) threads = 1;
-    const int64_t gu_qb = 2 * I * (H / 2), gu_mb = 2 * I * (H / G);
-    const int64_t dn_qb = H * (I / 2), dn_mb = H * (I / G);
+    const int64_t gu_qb = 2 * I * (H / 2), gu_mb = 2 * I * (H / Ggu);
+    const int64_t dn_qb = H * (I / 2), dn_mb = H * (I / Gdn);
     double *y = (double *)malloc(sizeof(double) * (size_t)H);
     double *A = (double *)malloc(sizeof(double) * (size_t)H);
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
@@ -334,7 +337,7 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
             int64_t e = ids[t * k + j];
             if (e < 0 || e >= E) { rc = -3; break; }
             double pj = p[t * k + j];
-            rc = expert_ffn(xt, H, I, G, c,
+            rc = expert_ffn(xt, H, I, Ggu, Gdn, c,
                             gu_q + e * gu_qb, gu_s + e * gu_mb, gu_z + e * gu_mb,
                             dn_q + e * dn_qb, dn_s + e * dn_mb, dn_z + e * dn_mb,
                             y, A, h, th, threads);
@@ -344,7 +347,7 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
             }
         }
         if (rc == 0 && sh_gu_q) {
-            rc = expert_ffn(xt, H, I, G, c, sh_gu_q, sh_gu_s, sh_gu_z,
+            rc = expert_ffn(xt, H, I, Ggu, Gdn, c, sh_gu_q, sh_gu_s, sh_gu_z,
                             sh_dn_q, sh_dn_s, sh_dn_z, y, A, h, th, threads);
             for (int64_t n = 0; n < H; n++) {
                 ot[n] += y[n];

@@ -101,6 +101,32 @@ def test_dequant_group_boundary_and_row_indexing():
     assert np.all(w[1, :128] == 12.0) and np.all(w[1, 128:] == 16.0)
 
 
+def test_dequant_group_sizes_relate():
+    # a matrix quantized with 64-wide groups whose neighbours share scale and zero
+    # is the 128-wide matrix with those values; 256-wide and per-row (one group
+    # per row, G = K) groups are 128-wide ones with repeated values
+    N, K = 3, 512
+    g = np.random.default_rng(5)
+    qw = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s128 = g.uniform(0.01, 0.02, size=(N, K // 128)).astype(np.float16).view(np.uint16)
+    z128 = g.integers(0, 16, size=(N, K // 128), dtype=np.uint8)
+    w128 = oracle.dequant(qw, s128, z128, N, K)
+    assert np.array_equal(oracle.dequant(qw, np.repeat(s128, 2, axis=1), np.repeat(z128, 2, axis=1),
+                                         N, K, group=64), w128)
+    s256, z256 = s128[:, ::2], z128[:, ::2]
+    assert np.array_equal(oracle.dequant(qw, s256, z256, N, K, group=256),
+                          oracle.dequant(qw, np.repeat(s256, 2, axis=1), np.repeat(z256, 2, axis=1),
+                                         N, K))
+    sr, zr = s128[:, :1], z128[:, :1]
+    assert np.array_equal(oracle.dequant(qw, sr, zr, N, K, group=K),
+                          oracle.dequant(qw, np.repeat(sr, 4, axis=1), np.repeat(zr, 4, axis=1), N, K))
+    # and a 64-wide group boundary really splits a 128-wide block
+    s64 = np.array([[0x3C00, 0x4000]], dtype=np.uint16)      # 1, 2
+    z64 = np.array([[0, 1]], dtype=np.uint8)
+    w = oracle.dequant(np.full((1, 64), 0x33, dtype=np.uint8), s64, z64, 1, 128, group=64)
+    assert np.all(w[0, :64] == 3.0) and np.all(w[0, 64:] == 4.0)
+
+
 def test_dequant_exact_in_fp32_for_workload_scales():
     # s*(q-z) for every binary16 scale of the workload range and every q-z is exact in
     # binary32: the product of an 11-bit and a 5-bit integer significand has <= 16 bits

@@ -55,6 +55,21 @@ def test_small_shapes_against_exact_rationals(T, N, K):
             assert err <= Fraction(2 * K * U53) * Fraction(float(S[t, n]))
 
 
+@pytest.mark.parametrize("T,N,K,G", [(2, 5, 256, 64), (3, 4, 512, 256), (2, 3, 384, 384),
+                                     (1, 6, 640, 640)])
+def test_other_group_sizes_against_exact_rationals(T, N, K, G):
+    # group sizes 64 and 256 (the FastLLM page's section 4.2 allows them beside
+    # 128) and one group per row (G = K)
+    w = workloads.weights(13, T * 100 + N + G, N, K, 0.002, 0.02, group=G)
+    x64 = oracle.widen(workloads.activations(13, N + G, T, K, "bf16"), "bf16")
+    y, S = oracle.linear(x64, w["qweight"], w["scales"], w["zeros"], N, K, group=G)
+    ex = _exact_linear(x64, w["qweight"], w["scales"], w["zeros"], N, K, G)
+    for t in range(T):
+        for n in range(N):
+            err = abs(Fraction(float(y[t, n])) - ex[t][n])
+            assert err <= Fraction(2 * K * U53) * Fraction(float(S[t, n]))
+
+
 def test_closed_form_ramp():
     # q_k = k mod 16, zero 8, scale 0.5, x_k = k+1 over one group of 128:
     # sum_k 0.5*(k mod 16 - 8)*(k+1) = 0.5 * sum_b (272 - 128 b), b = 0..7 = -704

@@ -171,20 +171,34 @@ def test_moe_is_linear_in_combine_weights(small_moe):
     assert np.allclose(c, 0.25 * a + 0.75 * b, rtol=1e-13, atol=1e-13 * np.abs(c).max())
 
 
+def test_moe_per_row_groups_match_whole_row_groups_when_hidden_equals_inter():
+    # group 0 means one group per row of each matrix; with H == I that is G = H
+    Hs = Is = 256
+    ex = workloads.moe_experts(41, 0, 4, Hs, Is, 0.005, 0.02, group=0)
+    sh = workloads.moe_shared(41, 0, Hs, Is, 0.005, 0.02, group=0)
+    x = oracle.widen(workloads.activations(41, 1, 3, Hs, "bf16"), "bf16")
+    ids = np.array([[0, 2], [1, 3], [3, 0]], dtype=np.int32)
+    p = np.array([[0.6, 0.4], [0.5, 0.5], [0.9, 0.1]])
+    a, ta = oracle.moe(x, ids, p, ex, sh, Hs, Is, 4, group=0)
+    b, tb = oracle.moe(x, ids, p, ex, sh, Hs, Is, 4, group=Hs)
+    assert np.array_equal(a, b) and np.array_equal(ta, tb)
+
+
 # ---- reference quantizer -----------------------------------------------------------
 
-def test_quantizer_error_bound_and_dequant_round_trip():
+@pytest.mark.parametrize("G", [128, 64, 256, 512])
+def test_quantizer_error_bound_and_dequant_round_trip(G):
     g = np.random.default_rng(9)
     w = g.standard_normal((8, 512)) * 0.05
-    w[0, :128] = 0.0          # an all-zero group
-    w[1, :128] = 0.37         # a constant positive group (0 joins the range)
-    w[2, :128] = -np.abs(w[2, :128])  # an all-negative group
-    qw, s, z = oracle.quantize(w)
-    wd = oracle.dequant(qw, s, z, 8, 512)
-    sc = np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    w[0, :G] = 0.0          # an all-zero group
+    w[1, :G] = 0.37         # a constant positive group (0 joins the range)
+    w[2, :G] = -np.abs(w[2, :G])  # an all-negative group
+    qw, s, z = oracle.quantize(w, G)
+    wd = oracle.dequant(qw, s, z, 8, 512, G)
+    sc = np.repeat(s.view(np.float16).astype(np.float64), G, axis=1)
     assert np.all(np.abs(w - wd) <= sc * (0.5 + 1e-3) + 1e-12)
-    assert np.all(wd[0, :128] == 0.0)
+    assert np.all(wd[0, :G] == 0.0)
     # re-quantizing the dequantized grid with its own scale and zero reproduces the codes
     q = oracle.unpack(qw, 8, 512).astype(np.int64)
-    zz = np.repeat(z.astype(np.int64), 128, axis=1)
+    zz = np.repeat(z.astype(np.int64), G, axis=1)
     assert np.array_equal(np.clip(np.rint(wd / sc) + zz, 0, 15), q)

@@ -45,7 +45,9 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 def weights(seed: int, tag: int, N: int, K: int, scale_lo: float, scale_hi: float,
             group: int = GROUP) -> dict:
     """q uniform in 0..15 (so a packed byte is uniform in 0..255), zero uniform in
-    0..15, scale uniform in [scale_lo, scale_hi] rounded to binary16."""
+    0..15, scale uniform in [scale_lo, scale_hi] rounded to binary16.  group 0 means
+    one group per row."""
+    group = group or K
     assert K % group == 0 and K % 2 == 0
     G = K // group
     qw = rng(seed, tag, _T_QW).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
