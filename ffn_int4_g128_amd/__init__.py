@@ -1,5 +1,6 @@
-"""Python binding of libqi4: int4 group-quantized (g128) linear layer and routed
-MoE expert FFN for AMD MI355X (gfx950).
+"""Python binding of libqi4: int4 group-quantized linear layer (groups of 128 by
+default; 64, multiples of 128, or one group per row) and routed MoE expert FFN
+for AMD MI355X (gfx950).
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``libqi4.so`` (sources in ``csrc/``, C ABI in ``include/qi4.h``);
@@ -19,7 +20,11 @@ QI4_OK = 0
 QI4_F32, QI4_BF16 = 0, 1
 QI4_EPI_NONE, QI4_EPI_SILU_MUL = 0, 1
 QI4_PACK_GATEUP = 1
-GROUP = 128
+GROUP = 128          # default group size; 0 means one group per row
+
+
+def _ngroups(K: int, group: int) -> int:
+    return 1 if group == 0 else K // group
 
 _lib = None
 
@@ -63,6 +68,7 @@ def lib():
             "qi4_dequant_f32": (ci, [vp, i64, i64, ci, ci, vp, vp]),
             "qi4_quantize": (ci, [vp, ci, i64, i64, ci, vp, vp, vp, vp]),
             "qlinear_int4_g128": (ci, [vp, ci, i64, i64, vp, i64, ci, vp, ci, ci, vp]),
+            "qlinear_int4": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
             "moe_sort_tokens": (ci, [vp, i64, i32, i64, vp, vp, vp, vp, vp]),
             "moe_ffn_int4_workspace_bytes": (i64, [dp, i64]),
@@ -80,7 +86,8 @@ def lib():
 
 # declared in include/qi4.h, in header order
 EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pack", "qi4_unpack",
-            "qi4_dequant_f32", "qi4_quantize", "qlinear_int4_g128", "moe_route_topk", "moe_sort_tokens",
+            "qi4_dequant_f32", "qi4_quantize", "qlinear_int4_g128", "qlinear_int4", "moe_route_topk",
+            "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4"]
 
@@ -115,47 +122,50 @@ def _need(t, dtype, what):
 
 # ---- format -------------------------------------------------------------------
 
-def packed_bytes(N: int, K: int, flags: int = 0) -> int:
-    n = lib().qi4_packed_bytes(N, K, GROUP, flags)
+def packed_bytes(N: int, K: int, flags: int = 0, group: int = GROUP) -> int:
+    n = lib().qi4_packed_bytes(N, K, group, flags)
     _check(int(n) if n < 0 else 0, "qi4_packed_bytes")
     return int(n)
 
 
-def pack(qweight, scales, zeros, N: int, K: int, flags: int = 0, out=None, stream=None):
-    """Canonical (uint8 [N][K/2], int16/uint16 binary16 bits [N][K/128], uint8 [N][K/128])
-    device tensors -> packed uint8 device tensor."""
+def pack(qweight, scales, zeros, N: int, K: int, flags: int = 0, out=None, stream=None,
+         group: int = GROUP):
+    """Canonical (uint8 [N][K/2], int16/uint16 binary16 bits [N][K/group], uint8
+    [N][K/group]) device tensors -> packed uint8 device tensor."""
     import torch
     _need(qweight, torch.uint8, "qweight")
     _need(zeros, torch.uint8, "zeros")
     if out is None:
-        out = torch.empty(packed_bytes(N, K, flags), dtype=torch.uint8, device=qweight.device)
-    _check(lib().qi4_pack(_ptr(qweight), _ptr(scales), _ptr(zeros), N, K, GROUP, flags,
+        out = torch.empty(packed_bytes(N, K, flags, group), dtype=torch.uint8,
+                          device=qweight.device)
+    _check(lib().qi4_pack(_ptr(qweight), _ptr(scales), _ptr(zeros), N, K, group, flags,
                           _ptr(out), _stream(stream)), "qi4_pack")
     return out
 
 
-def unpack(packed, N: int, K: int, flags: int = 0, stream=None):
+def unpack(packed, N: int, K: int, flags: int = 0, stream=None, group: int = GROUP):
     import torch
     dev = packed.device
+    ng = _ngroups(K, group)
     qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    sc = torch.empty((N, K // GROUP), dtype=torch.int16, device=dev)
-    zr = torch.empty((N, K // GROUP), dtype=torch.uint8, device=dev)
-    _check(lib().qi4_unpack(_ptr(packed), N, K, GROUP, flags, _ptr(qw), _ptr(sc), _ptr(zr),
+    sc = torch.empty((N, ng), dtype=torch.int16, device=dev)
+    zr = torch.empty((N, ng), dtype=torch.uint8, device=dev)
+    _check(lib().qi4_unpack(_ptr(packed), N, K, group, flags, _ptr(qw), _ptr(sc), _ptr(zr),
                             _stream(stream)), "qi4_unpack")
     return qw, sc, zr
 
 
-def dequant_f32(packed, N: int, K: int, flags: int = 0, stream=None):
+def dequant_f32(packed, N: int, K: int, flags: int = 0, stream=None, group: int = GROUP):
     import torch
     w = torch.empty((N, K), dtype=torch.float32, device=packed.device)
-    _check(lib().qi4_dequant_f32(_ptr(packed), N, K, GROUP, flags, _ptr(w), _stream(stream)),
+    _check(lib().qi4_dequant_f32(_ptr(packed), N, K, group, flags, _ptr(w), _stream(stream)),
            "qi4_dequant_f32")
     return w
 
 
-def quantize(w, stream=None):
+def quantize(w, stream=None, group: int = GROUP):
     """float32 or bfloat16 device weights [N][K] -> canonical (qweight uint8 [N][K/2],
-    scales int16 binary16 bits [N][K/128], zeros uint8 [N][K/128]) device tensors."""
+    scales int16 binary16 bits [N][K/group], zeros uint8 [N][K/group]) device tensors."""
     import torch
     if w.dtype == torch.float32:
         wd = QI4_F32
@@ -166,10 +176,11 @@ def quantize(w, stream=None):
     if not (w.is_cuda and w.is_contiguous() and w.dim() == 2):
         raise ValueError("w must be a contiguous 2-D device tensor")
     N, K = w.shape
+    ng = _ngroups(K, group)
     qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-    sc = torch.empty((N, K // GROUP), dtype=torch.int16, device=w.device)
-    zr = torch.empty((N, K // GROUP), dtype=torch.uint8, device=w.device)
-    _check(lib().qi4_quantize(_ptr(w), wd, N, K, GROUP, _ptr(qw), _ptr(sc), _ptr(zr),
+    sc = torch.empty((N, ng), dtype=torch.int16, device=w.device)
+    zr = torch.empty((N, ng), dtype=torch.uint8, device=w.device)
+    _check(lib().qi4_quantize(_ptr(w), wd, N, K, group, _ptr(qw), _ptr(sc), _ptr(zr),
                               _stream(stream)), "qi4_quantize")
     return qw, sc, zr
 
@@ -177,7 +188,7 @@ def quantize(w, stream=None):
 # ---- linear ----------------------------------------------------------------------
 
 def qlinear(x, packed, N: int, flags: int = 0, out_dtype=None, epilogue: int = QI4_EPI_NONE,
-            out=None, stream=None):
+            out=None, stream=None, group: int = GROUP):
     """y = epilogue(x . dequant(W)^T); x is bfloat16 or float32 [T][K]."""
     import torch
     if x.dtype == torch.bfloat16:
@@ -194,8 +205,12 @@ def qlinear(x, packed, N: int, flags: int = 0, out_dtype=None, epilogue: int = Q
     if out is None:
         out = torch.empty((T, n_out), dtype=out_dtype, device=x.device)
     yd = QI4_BF16 if out.dtype == torch.bfloat16 else QI4_F32
-    _check(lib().qlinear_int4_g128(_ptr(x), xd, T, K, _ptr(packed), N, flags, _ptr(out), yd,
-                                   epilogue, _stream(stream)), "qlinear_int4_g128")
+    if group == GROUP:
+        _check(lib().qlinear_int4_g128(_ptr(x), xd, T, K, _ptr(packed), N, flags, _ptr(out), yd,
+                                       epilogue, _stream(stream)), "qlinear_int4_g128")
+    else:
+        _check(lib().qlinear_int4(_ptr(x), xd, T, K, _ptr(packed), N, group, flags, _ptr(out), yd,
+                                  epilogue, _stream(stream)), "qlinear_int4")
     return out
 
 
@@ -212,14 +227,15 @@ class MoeWeights:
     w_down: object
     shared_gate_up: object = None
     shared_down: object = None
+    group: int = GROUP
 
     def desc(self, top_k: int) -> _MoeDesc:
-        return _MoeDesc(self.E, self.H, self.I, top_k, GROUP,
+        return _MoeDesc(self.E, self.H, self.I, top_k, self.group,
                         1 if self.shared_gate_up is not None else 0, 0)
 
 
 def pack_moe(experts: dict, shared: dict | None, E: int, H: int, I: int, device="cuda",
-             stream=None) -> MoeWeights:
+             stream=None, group: int = GROUP) -> MoeWeights:
     """Pack canonical expert weights (numpy or torch; see workloads.moe_experts) expert by
     expert on the device."""
     import numpy as np
@@ -232,23 +248,24 @@ def pack_moe(experts: dict, shared: dict | None, E: int, H: int, I: int, device=
             a = torch.from_numpy(np.ascontiguousarray(a))
         return a.to(device)
 
-    gu_b, dn_b = packed_bytes(2 * I, H, QI4_PACK_GATEUP), packed_bytes(H, I, 0)
+    gu_b, dn_b = packed_bytes(2 * I, H, QI4_PACK_GATEUP, group), packed_bytes(H, I, 0, group)
     w_gu = torch.empty(E * gu_b, dtype=torch.uint8, device=device)
     w_dn = torch.empty(E * dn_b, dtype=torch.uint8, device=device)
     for e in range(E):
         pack(dev(experts["gu_q"][e], torch.uint8), dev(experts["gu_s"][e], torch.int16),
              dev(experts["gu_z"][e], torch.uint8), 2 * I, H, QI4_PACK_GATEUP,
-             out=w_gu[e * gu_b:(e + 1) * gu_b], stream=stream)
+             out=w_gu[e * gu_b:(e + 1) * gu_b], stream=stream, group=group)
         pack(dev(experts["dn_q"][e], torch.uint8), dev(experts["dn_s"][e], torch.int16),
              dev(experts["dn_z"][e], torch.uint8), H, I, 0,
-             out=w_dn[e * dn_b:(e + 1) * dn_b], stream=stream)
+             out=w_dn[e * dn_b:(e + 1) * dn_b], stream=stream, group=group)
     sgu = sdn = None
     if shared is not None:
         sgu = pack(dev(shared["gu_q"], torch.uint8), dev(shared["gu_s"], torch.int16),
-                   dev(shared["gu_z"], torch.uint8), 2 * I, H, QI4_PACK_GATEUP, stream=stream)
+                   dev(shared["gu_z"], torch.uint8), 2 * I, H, QI4_PACK_GATEUP, stream=stream,
+                   group=group)
         sdn = pack(dev(shared["dn_q"], torch.uint8), dev(shared["dn_s"], torch.int16),
-                   dev(shared["dn_z"], torch.uint8), H, I, 0, stream=stream)
-    return MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn)
+                   dev(shared["dn_z"], torch.uint8), H, I, 0, stream=stream, group=group)
+    return MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn, group)
 
 
 def moe_route_topk(logits, top_k: int, stream=None):

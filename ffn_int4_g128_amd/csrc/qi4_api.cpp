@@ -52,7 +52,7 @@ const char *qi4_status_string(int status) {
 int64_t qi4_packed_bytes(int64_t N, int64_t K, int group_size, int flags) {
     int rc = qi4::check_matrix(N, K, group_size, flags);
     if (rc != QI4_OK) return rc;
-    return qi4::PackedLayout(N, K, flags).bytes;
+    return qi4::PackedLayout(N, K, flags, (int)qi4::effective_group(group_size, K)).bytes;
 }
 
 }  // extern "C"

@@ -40,27 +40,42 @@ __host__ __device__ inline int64_t tile_row(int64_t t, int r, int64_t N, int fla
     return row < N ? row : -1;
 }
 
-// Byte offsets of the three regions of a packed matrix.
+// Quantization group sizes: 64, or a multiple of 128 that divides K (128,
+// 256, ..., K for one scale and zero per row).  The kernels work on 128-wide
+// blocks of K; with 64-wide groups a block holds two groups and its records
+// two halves, else the records of every block of a group repeat that group's
+// scale and zero (dequantization is per weight, so this is exact).
+__host__ __device__ inline int halves_for(int group_size) { return group_size == 64 ? 2 : 1; }
+
+// Byte offsets of the three regions of a packed matrix.  G counts 128-wide
+// blocks of K.
 struct PackedLayout {
     int64_t nt, nq, G;
+    int halves;                 // 2 for 64-wide groups, else 1
+    int64_t srec, zrec;         // bytes of one (quad, block) scale / zero record
     int64_t scales_off, zeros_off, bytes;
-    __host__ __device__ PackedLayout(int64_t N, int64_t K, int flags) {
+    __host__ __device__ PackedLayout(int64_t N, int64_t K, int flags, int group_size) {
         nt = num_tiles(N, flags);
         nq = (nt + kQuadTiles - 1) / kQuadTiles;
         G = K / kGroup;
+        halves = halves_for(group_size);
+        srec = (int64_t)kQuadScaleBytes * halves;
+        zrec = (int64_t)kQuadZeroBytes * halves;
         scales_off = nt * G * kTileGroupBytes;
-        zeros_off = scales_off + nq * G * kQuadScaleBytes;
-        int64_t end = zeros_off + nq * G * kQuadZeroBytes;
+        zeros_off = scales_off + nq * G * srec;
+        int64_t end = zeros_off + nq * G * zrec;
         bytes = (end + 255) & ~int64_t(255);
     }
-    // Start of the (quad of tile t, group g) scale and zero records.  Row r's
-    // scale of tile t is at scale_rec + 8 r + 2 (t & 3); its zero is nibble
-    // 4 (t & 1) of byte zero_rec + 2 r + ((t & 3) >> 1).
+    // Start of the (quad of tile t, block g) scale and zero records; half h
+    // (64-wide groups: k in 128 g + 64 h + [0, 64)) starts kQuadScaleBytes * h
+    // and kQuadZeroBytes * h further.  Within a half, row r's scale of tile t
+    // is at + 8 r + 2 (t & 3) and its zero is nibble 4 (t & 1) of byte
+    // + 2 r + ((t & 3) >> 1).
     __host__ __device__ int64_t scale_rec(int64_t t, int64_t g) const {
-        return scales_off + ((t / kQuadTiles) * G + g) * kQuadScaleBytes;
+        return scales_off + ((t / kQuadTiles) * G + g) * srec;
     }
     __host__ __device__ int64_t zero_rec(int64_t t, int64_t g) const {
-        return zeros_off + ((t / kQuadTiles) * G + g) * kQuadZeroBytes;
+        return zeros_off + ((t / kQuadTiles) * G + g) * zrec;
     }
 };
 

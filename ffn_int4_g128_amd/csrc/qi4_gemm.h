@@ -18,6 +18,7 @@ struct GemmArgs {
     const uint8_t *w_shared;   // shared expert (moe) or nullptr
     int64_t N, K;              // rows and reduction length of each matrix
     int flags;                 // QI4_PACK_GATEUP or 0
+    int group_size;            // quantization group size (64, or a multiple of 128)
     // activations
     const void *a;             // bf16 bits, or float32 when a_f32
     int64_t lda;               // elements per A source row

@@ -57,11 +57,11 @@ __device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
 // Loads of one 128-wide group: the codes, scale and zero byte of NB tiles and
 // the raw activation fragments of MT M tiles (bf16: one 16-byte load per k
 // step; float32: two).
-template <int NB, int MT, bool AF32>
+template <int NB, int MT, bool AF32, int H>
 struct Stage {
     uint4 cw[NB];
-    uint32_t sc[(NB + 1) / 2];   // binary16 scales of tiles 2i, 2i+1 in dword i
-    uint32_t zb;                 // zero of tile nb in nibble nb (+ the slot offset)
+    uint32_t sc[H][(NB + 1) / 2];   // per half: binary16 scales of tiles 2i, 2i+1 in dword i
+    uint32_t zb[H];                 // per half: zero of tile nb in nibble nb (+ the slot offset)
     uint4 af[MT][4][AF32 ? 2 : 1];
 };
 
@@ -86,7 +86,8 @@ __device__ inline uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
 template <int NB, int MT, bool AF32, int EPI>
 constexpr int kMinWaves = (!AF32 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL) ? 4 : 1;
 
-template <int NB, int MT, bool AF32, int S, int EPI>
+// H = 2: 64-wide groups, two scales and zeros per 128-wide block.
+template <int NB, int MT, bool AF32, int S, int EPI, int H>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AF32, EPI>)))
 qgemm_kernel(const GemmArgs args) {
@@ -125,7 +126,7 @@ qgemm_kernel(const GemmArgs args) {
     }
     if (n <= 0) return;
 
-    const PackedLayout L(args.N, args.K, args.flags);
+    const PackedLayout L(args.N, args.K, args.flags, args.group_size);
     const int64_t nt = L.nt, G = L.G;
     // Tile blocks of this workgroup: R consecutive blocks of NB tiles, streamed
     // back to back through one register pipeline, so a block's first loads are
@@ -168,7 +169,7 @@ qgemm_kernel(const GemmArgs args) {
 
         // S register stages: while one step is multiplied, the loads of the
         // next S - 1 steps are in flight.
-        Stage<NB, MT, AF32> st[S];
+        Stage<NB, MT, AF32, H> st[S];
         uint32_t abase[MT];
         int apart[MT];
         // Load cursor (wave-uniform): block lr, step li of that block, and the
@@ -188,14 +189,17 @@ qgemm_kernel(const GemmArgs args) {
             loa = (uint32_t)gb * 128u * ES;
             lnt = lr < nblk ? (int)(nt - tile < NB ? nt - tile : NB) : 0;
         };
-        auto load_w = [&](Stage<NB, MT, AF32> &q) {
+        auto load_w = [&](Stage<NB, MT, AF32, H> &q) {
             const bool in = lnt > 0 && gb + li < ge;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 q.cw[nb] = buf_b128(wr, vc, in && nb < lnt ? loc + nb * tstride : kOobS);
-            load_meta<NB>(wr, vs, vz, in ? los : kOobS, in ? loz : kOobS, q.sc, q.zb);
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+                load_meta<NB>(wr, vs, vz, in ? los + h * kQuadScaleBytes : kOobS,
+                              in ? loz + h * kQuadZeroBytes : kOobS, q.sc[h], q.zb[h]);
         };
-        auto load_a = [&](Stage<NB, MT, AF32> &q) {
+        auto load_a = [&](Stage<NB, MT, AF32, H> &q) {
             const bool in = lnt > 0 && gb + li < ge;
             const uint32_t oa = in ? loa : kOobS;
 #pragma unroll
@@ -208,8 +212,8 @@ qgemm_kernel(const GemmArgs args) {
         };
         auto advance = [&]() {
             loc += kTileGroupBytes;
-            los += kQuadScaleBytes;
-            loz += kQuadZeroBytes;
+            los += H * kQuadScaleBytes;
+            loz += H * kQuadZeroBytes;
             loa += 128u * ES;
             if (++li == ngp) {
                 li = 0;
@@ -217,7 +221,7 @@ qgemm_kernel(const GemmArgs args) {
                 rebase();
             }
         };
-        auto compute = [&](const Stage<NB, MT, AF32> &q, int zshift) {
+        auto compute = [&](const Stage<NB, MT, AF32, H> &q, int zshift) {
             bf16x8 a[MT][4];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -234,23 +238,43 @@ qgemm_kernel(const GemmArgs args) {
                 const bf16x8 b1 = as_bf16x8(unpack_codes_bf16(q.cw[nb].y));
                 const bf16x8 b2 = as_bf16x8(unpack_codes_bf16(q.cw[nb].z));
                 const bf16x8 b3 = as_bf16x8(unpack_codes_bf16(q.cw[nb].w));
-                const uint32_t z = (q.zb >> (zshift + 4 * nb)) & 15u;
-                const uint32_t zz = (0x4300u | z) * 0x00010001u;   // bf16 pair (128+z, 128+z)
-                const bf16x8 bz = as_bf16x8(make_uint4(zz, zz, zz, zz));
-                const float sc = f16_bits_to_f32((uint16_t)(q.sc[nb >> 1] >> (16 * (nb & 1))));
+                bf16x8 bz[H];
+                float sc[H];
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    const uint32_t z = (q.zb[h] >> (zshift + 4 * nb)) & 15u;
+                    const uint32_t zz = (0x4300u | z) * 0x00010001u;   // bf16 pair (128+z, 128+z)
+                    bz[h] = as_bf16x8(make_uint4(zz, zz, zz, zz));
+                    sc[h] = f16_bits_to_f32((uint16_t)(q.sc[h][nb >> 1] >> (16 * (nb & 1))));
+                }
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m >= m_used) break;
-                    f32x4 acc = mfma16x16x32(a[m][0], b0, zero4);
-                    f32x4 xz = mfma16x16x32(a[m][0], bz, zero4);
-                    acc = mfma16x16x32(a[m][1], b1, acc);
-                    xz = mfma16x16x32(a[m][1], bz, xz);
-                    acc = mfma16x16x32(a[m][2], b2, acc);
-                    xz = mfma16x16x32(a[m][2], bz, xz);
-                    acc = mfma16x16x32(a[m][3], b3, acc);
-                    xz = mfma16x16x32(a[m][3], bz, xz);
+                    if constexpr (H == 1) {
+                        f32x4 acc = mfma16x16x32(a[m][0], b0, zero4);
+                        f32x4 xz = mfma16x16x32(a[m][0], bz[0], zero4);
+                        acc = mfma16x16x32(a[m][1], b1, acc);
+                        xz = mfma16x16x32(a[m][1], bz[0], xz);
+                        acc = mfma16x16x32(a[m][2], b2, acc);
+                        xz = mfma16x16x32(a[m][2], bz[0], xz);
+                        acc = mfma16x16x32(a[m][3], b3, acc);
+                        xz = mfma16x16x32(a[m][3], bz[0], xz);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) res[m][nb][v] += sc * (acc[v] - xz[v]);
+                        for (int v = 0; v < 4; ++v) res[m][nb][v] += sc[0] * (acc[v] - xz[v]);
+                    } else {
+                        // k-steps 0, 1 are the first 64-wide group, 2, 3 the second
+                        f32x4 acc0 = mfma16x16x32(a[m][0], b0, zero4);
+                        f32x4 xz0 = mfma16x16x32(a[m][0], bz[0], zero4);
+                        acc0 = mfma16x16x32(a[m][1], b1, acc0);
+                        xz0 = mfma16x16x32(a[m][1], bz[0], xz0);
+                        f32x4 acc1 = mfma16x16x32(a[m][2], b2, zero4);
+                        f32x4 xz1 = mfma16x16x32(a[m][2], bz[H - 1], zero4);
+                        acc1 = mfma16x16x32(a[m][3], b3, acc1);
+                        xz1 = mfma16x16x32(a[m][3], bz[H - 1], xz1);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            res[m][nb][v] += sc[0] * (acc0[v] - xz0[v]) + sc[H - 1] * (acc1[v] - xz1[v]);
+                    }
                 }
             }
         };
@@ -381,23 +405,29 @@ qgemm_kernel(const GemmArgs args) {
     }
 }
 
-template <int NB, int MT, int S>
-int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
+template <int NB, int MT, int S, int H>
+int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
     if (a.epi == QI4_EPI_SILU_MUL) {
         if constexpr (NB % 2 == 0) {
             if (a.a_f32)
-                qgemm_kernel<NB, MT, true, 2, QI4_EPI_SILU_MUL><<<grid, threads, 0, st>>>(a);
+                qgemm_kernel<NB, MT, true, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
             else
-                qgemm_kernel<NB, MT, false, S, QI4_EPI_SILU_MUL><<<grid, threads, 0, st>>>(a);
+                qgemm_kernel<NB, MT, false, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
         } else {
             return QI4_ERR_UNSUPPORTED;
         }
     } else if (a.a_f32) {
-        qgemm_kernel<NB, MT, true, 2, QI4_EPI_NONE><<<grid, threads, 0, st>>>(a);
+        qgemm_kernel<NB, MT, true, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     } else {
-        qgemm_kernel<NB, MT, false, S, QI4_EPI_NONE><<<grid, threads, 0, st>>>(a);
+        qgemm_kernel<NB, MT, false, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     }
     return launch_status();
+}
+
+template <int NB, int MT, int S>
+int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
+    return halves_for(a.group_size) == 2 ? launch_cfg_h<NB, MT, S, 2>(a, grid, threads, st)
+                                         : launch_cfg_h<NB, MT, S, 1>(a, grid, threads, st);
 }
 
 }  // namespace
@@ -462,10 +492,10 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
 
 using namespace qi4;
 
-extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,
-                                 const void *packed_w, int64_t N, int flags, void *y,
-                                 int y_dtype, int epilogue, void *stream) {
-    int rc = check_matrix(N, K, 128, flags);
+extern "C" int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
+                            const void *packed_w, int64_t N, int group_size, int flags, void *y,
+                            int y_dtype, int epilogue, void *stream) {
+    int rc = check_matrix(N, K, group_size, flags);
     if (rc) return rc;
     if (x_dtype != QI4_F32 && x_dtype != QI4_BF16) return QI4_ERR_DTYPE;
     if (y_dtype != QI4_F32 && y_dtype != QI4_BF16) return QI4_ERR_DTYPE;
@@ -478,7 +508,8 @@ extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t 
     const int64_t n_out = epilogue == QI4_EPI_SILU_MUL ? N / 2 : N;
     const int64_t xb = T * K * (x_dtype == QI4_F32 ? 4 : 2);
     const int64_t yb = T * n_out * (y_dtype == QI4_F32 ? 4 : 2);
-    const int64_t wb = PackedLayout(N, K, flags).bytes;
+    const int gs = (int)effective_group(group_size, K);
+    const int64_t wb = PackedLayout(N, K, flags, gs).bytes;
     if (wb >= (int64_t(1) << 31) || xb >= (int64_t(1) << 31)) return QI4_ERR_SHAPE;
     if (overlaps(y, yb, x, xb) || overlaps(y, yb, packed_w, wb)) return QI4_ERR_ALIAS;
     if ((rc = check_device())) return rc;
@@ -488,6 +519,7 @@ extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t 
     a.N = N;
     a.K = K;
     a.flags = flags;
+    a.group_size = gs;
     a.a = x;
     a.lda = K;
     a.a_bytes = xb;
@@ -501,4 +533,10 @@ extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t 
     a.epi = epilogue;
     a.n_out = n_out;
     return launch_qgemm(a, 1, T, as_stream(stream));
+}
+
+extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,
+                                 const void *packed_w, int64_t N, int flags, void *y,
+                                 int y_dtype, int epilogue, void *stream) {
+    return qlinear_int4(x, x_dtype, T, K, packed_w, N, 128, flags, y, y_dtype, epilogue, stream);
 }

@@ -19,9 +19,15 @@ inline bool aligned(const void *p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
+// The group size a call means: 0 stands for one group per row (K).
+inline int64_t effective_group(int group_size, int64_t K) { return group_size == 0 ? K : group_size; }
+
 // Shape checks common to every call on a packed matrix.
 inline int check_matrix(int64_t N, int64_t K, int group_size, int flags) {
-    if (group_size != 128) return QI4_ERR_GROUP;
+    // 64, or a multiple of 128 dividing K (0 or K: one group per row)
+    const int64_t gs = effective_group(group_size, K);
+    if (group_size < 0 || (gs != 64 && (gs < 128 || gs % 128 != 0))) return QI4_ERR_GROUP;
+    if (gs > 64 && K % gs != 0) return QI4_ERR_SHAPE;
     if (flags & ~QI4_PACK_GATEUP) return QI4_ERR_UNSUPPORTED;
     if (N < 1 || K < 128 || (K % 128) != 0) return QI4_ERR_SHAPE;
     if ((flags & QI4_PACK_GATEUP) && (N % 2) != 0) return QI4_ERR_SHAPE;

@@ -314,16 +314,32 @@ combine_kernel(const float *__restrict__ y, const float *__restrict__ wts,
 
 int check_desc(const qi4_moe_desc *d) {
     if (!d) return QI4_ERR_NULL;
-    if (d->group_size != 128) return QI4_ERR_GROUP;
+    // one group size for both projections: 64, a multiple of 128 dividing both
+    // hidden and inter, or 0 (one group per row of each matrix)
+    if (d->group_size < 0 || (d->group_size != 0 && d->group_size != 64 &&
+                              (d->group_size < 128 || d->group_size % 128 != 0)))
+        return QI4_ERR_GROUP;
     if (d->flags != 0 || (d->has_shared != 0 && d->has_shared != 1)) return QI4_ERR_UNSUPPORTED;
     if (d->num_experts < 1 || d->num_experts > kMaxExperts) return QI4_ERR_SHAPE;
     if (d->hidden < 128 || d->hidden % 128 || d->inter < 128 || d->inter % 128) return QI4_ERR_SHAPE;
     if (d->hidden > (1 << 20) || d->inter > (1 << 20)) return QI4_ERR_SHAPE;
+    if (d->group_size > 64 && (d->hidden % d->group_size || d->inter % d->group_size))
+        return QI4_ERR_SHAPE;
     if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return QI4_ERR_SHAPE;
     return QI4_OK;
 }
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Group sizes of the gate/up (groups along hidden) and down (along inter) matrices.
+inline int gs_gate_up(const qi4_moe_desc *d) { return (int)effective_group(d->group_size, d->hidden); }
+inline int gs_down(const qi4_moe_desc *d) { return (int)effective_group(d->group_size, d->inter); }
+inline int64_t gate_up_bytes(const qi4_moe_desc *d) {
+    return PackedLayout(2 * d->inter, d->hidden, QI4_PACK_GATEUP, gs_gate_up(d)).bytes;
+}
+inline int64_t down_bytes(const qi4_moe_desc *d) {
+    return PackedLayout(d->hidden, d->inter, 0, gs_down(d)).bytes;
+}
 
 // Batches of at least this many tokens run the prefill GEMM (fp16 MFMA on
 // LDS-staged activation tiles); smaller ones the weight-streaming decode GEMM.
@@ -402,11 +418,12 @@ GemmArgs gate_up_args(const qi4_moe_desc *d, const void *x, int64_t T, const int
                       const void *sh_gu, void *h) {
     GemmArgs a = {};
     a.w = static_cast<const uint8_t *>(w_gu);
-    a.w_stride = PackedLayout(2 * d->inter, d->hidden, QI4_PACK_GATEUP).bytes;
+    a.w_stride = gate_up_bytes(d);
     a.w_shared = static_cast<const uint8_t *>(sh_gu);
     a.N = 2 * d->inter;
     a.K = d->hidden;
     a.flags = QI4_PACK_GATEUP;
+    a.group_size = gs_gate_up(d);
     a.a = x;
     a.lda = d->hidden;
     a.a_bytes = T * d->hidden * 2;
@@ -432,11 +449,12 @@ GemmArgs down_args(const qi4_moe_desc *d, const void *h, int64_t T, const int32_
                    const int32_t *active, const void *w_dn, const void *sh_dn, float *y) {
     GemmArgs a = {};
     a.w = static_cast<const uint8_t *>(w_dn);
-    a.w_stride = PackedLayout(d->hidden, d->inter, 0).bytes;
+    a.w_stride = down_bytes(d);
     a.w_shared = static_cast<const uint8_t *>(sh_dn);
     a.N = d->hidden;
     a.K = d->inter;
     a.flags = 0;
+    a.group_size = gs_down(d);
     a.a = h;
     a.lda = d->inter;
     a.a_bytes = (T * d->top_k + (d->has_shared ? T : 0)) * 2 * d->inter * 2;
@@ -474,7 +492,8 @@ PrefillArgs prefill_args(const qi4_moe_desc *d, int64_t T, bool gate_up, const i
     a.N = gate_up ? 2 * I : H;
     a.K = gate_up ? H : I;
     a.flags = gate_up ? QI4_PACK_GATEUP : 0;
-    a.w_stride = PackedLayout(a.N, a.K, a.flags).bytes;
+    a.group_size = gate_up ? gs_gate_up(d) : gs_down(d);
+    a.w_stride = PackedLayout(a.N, a.K, a.flags, a.group_size).bytes;
     a.a16 = a16;
     a.a_rows = gate_up ? T : T * d->top_k + (d->has_shared ? T : 0);
     a.a_exp = aexp;
@@ -552,8 +571,7 @@ int check_T(int64_t T, const qi4_moe_desc *d) {
     const int64_t R = T * d->top_k + (d->has_shared ? T : 0);
     if (R * 2 * d->inter * 2 >= (int64_t(1) << 31) || T * d->hidden * 2 >= (int64_t(1) << 31))
         return QI4_ERR_SHAPE;
-    if (PackedLayout(2 * d->inter, d->hidden, QI4_PACK_GATEUP).bytes >= (int64_t(1) << 31) ||
-        PackedLayout(d->hidden, d->inter, 0).bytes >= (int64_t(1) << 31))
+    if (gate_up_bytes(d) >= (int64_t(1) << 31) || down_bytes(d) >= (int64_t(1) << 31))
         return QI4_ERR_SHAPE;
     return QI4_OK;
 }

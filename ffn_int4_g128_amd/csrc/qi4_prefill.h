@@ -14,6 +14,7 @@ struct PrefillArgs {
     const uint8_t *w_shared;   // shared expert or nullptr
     int64_t N, K;
     int flags;
+    int group_size;            // quantization group size (64, or a multiple of 128)
     const uint16_t *a16;       // fp16 activation rows [a_rows][K]; value = a16 * 2^a_exp[row]
     int64_t a_rows;
     const int32_t *a_exp;

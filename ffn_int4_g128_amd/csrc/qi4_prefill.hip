@@ -242,7 +242,6 @@ struct Shape {
     static constexpr int kStageBytes = MS * 4 * kABlock;
     static constexpr int FPW = MS * 4 / W;   // operand fragments each wave copies per group
     static constexpr int NH = FPW >= 4 ? FPW / 4 : 1;   // distinct subtiles each wave copies
-    static constexpr int kReqs = FPW + 3 * NBW;   // memory requests per group per wave
     static_assert(W * NBW * 16 == kRowsPerWG, "workgroup rows");
     static constexpr int kLds = S * kStageBytes;   // LDS of one workgroup
     static_assert(kLds <= 160 * 1024, "LDS stages");
@@ -257,7 +256,8 @@ constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 
 
 // One tile: SH::MS 16-row activation subtiles times this workgroup's 256
 // weight rows, over the whole K.
-template <int EPI, class SH, int MU, bool WIDE>
+// H = 2: 64-wide quantization groups (two scale/zero records per block).
+template <int EPI, class SH, int MU, bool WIDE, int H>
 __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLayout &L, uint8_t *lds,
                                          int *wg_flag, int2 te, const uint8_t *w, int64_t row0,
                                          int64_t n, int64_t src0, const int32_t *gather, int64_t bx,
@@ -324,8 +324,11 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     };
     struct WStage {
         uint4 cw[NBW];
-        uint32_t sc[(NBW + 1) / 2], zb;
+        uint32_t sc[H][(NBW + 1) / 2], zb[H];
     };
+    // memory requests per group per wave: activation copies, codes, and a
+    // scale and a zero load per half
+    constexpr int kReqs = FPW + NBW + 2 * H;
     auto load_w = [&](WStage &q, int g) {
         const bool in = g < G && nt_here > 0;
 #pragma unroll
@@ -335,8 +338,11 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
             const uint32_t oc = ok ? (uint32_t)(tg * 1024) : kOobS;
             q.cw[nb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, vc, oc, 0));
         }
-        load_meta<NBW>(wr, vs, vz, in ? (uint32_t)L.scale_rec(tile0, g) : kOobS,
-                       in ? (uint32_t)L.zero_rec(tile0, g) : kOobS, q.sc, q.zb);
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+            load_meta<NBW>(wr, vs, vz, in ? (uint32_t)L.scale_rec(tile0, g) + h * kQuadScaleBytes : kOobS,
+                           in ? (uint32_t)L.zero_rec(tile0, g) + h * kQuadZeroBytes : kOobS, q.sc[h],
+                           q.zb[h]);
     };
 
     f32x4 acc[MS][NBW];
@@ -354,7 +360,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     bool big = false;
     if constexpr (!WIDE) {
         const bool scans = nt_here > 0 && (tile0 & (kQuadTiles - 1)) == 0;
-        const uint32_t span = scans ? (uint32_t)(G * kQuadScaleBytes) : 0u;
+        const uint32_t span = scans ? (uint32_t)(G * L.srec) : 0u;
         const uint32_t base = (uint32_t)L.scale_rec(tile0, 0);
         for (uint32_t o = 0; o < span; o += 1024) {
             const uint32_t lo = o + (uint32_t)lane * 16u;
@@ -402,23 +408,26 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
         static_assert(MU >= 1 && MU <= MS, "subtiles");
         auto compute = [&](const WStage &q, int stage) {
             const uint8_t *buf = lds + stage * SH::kStageBytes;
-            uint32_t negz[NBW], negz16[NBW], s2[NBW];
+            uint32_t negz[H][NBW], negz16[H][NBW], s2[H][NBW];
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const uint32_t z = (q.zb >> (4 * nb)) & 15u;
-                // fp16 -(1024 + z) and -(1024 + 16 z) in both halves; scale in both halves
-                negz[nb] = (0xE400u | z) * 0x00010001u;
-                negz16[nb] = (0xE400u | (z << 4)) * 0x00010001u;
-                s2[nb] = ((q.sc[nb >> 1] >> (16 * (nb & 1))) & 0xFFFFu) * 0x00010001u;
-            }
+            for (int h = 0; h < H; ++h)
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const uint32_t z = (q.zb[h] >> (4 * nb)) & 15u;
+                    // fp16 -(1024 + z) and -(1024 + 16 z) in both halves; scale in both halves
+                    negz[h][nb] = (0xE400u | z) * 0x00010001u;
+                    negz16[h][nb] = (0xE400u | (z << 4)) * 0x00010001u;
+                    s2[h][nb] = ((q.sc[h][nb >> 1] >> (16 * (nb & 1))) & 0xFFFFu) * 0x00010001u;
+                }
             auto deq = [&](int s, f16x8 (&b)[NBW]) {
+                const int h = H == 2 ? s >> 1 : 0;   // k steps 0, 1 / 2, 3: first / second 64-wide group
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb) {
                     const uint32_t d = s == 0 ? q.cw[nb].x : s == 1 ? q.cw[nb].y : s == 2 ? q.cw[nb].z : q.cw[nb].w;
                     if constexpr (WIDE)
-                        b[nb] = __builtin_bit_cast(f16x8, dequant_f16(d, negz[nb], s2[nb]));
+                        b[nb] = __builtin_bit_cast(f16x8, dequant_f16(d, negz[h][nb], s2[h][nb]));
                     else
-                        b[nb] = __builtin_bit_cast(f16x8, dequant_f16_x16(d, negz[nb], negz16[nb], s2[nb], magic));
+                        b[nb] = __builtin_bit_cast(f16x8, dequant_f16_x16(d, negz[h][nb], negz16[h][nb], s2[h][nb], magic));
                 }
             };
 #pragma unroll
@@ -451,7 +460,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
 #pragma unroll
             for (int u = 0; u < S; ++u) {
                 if (g + u >= G) break;
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(SH::kReqs * (S - 2)));
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(kReqs * (S - 2)));
                 __syncthreads();
                 const int nxt = (u + S - 1) % S;   // constant once unrolled
                 fill(nxt, g + u + S - 1);
@@ -503,12 +512,12 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
 }
 
 // Tile list entry -> problem, then run_tile.
-template <int EPI, class SH, int MU, bool WIDE>
+template <int EPI, class SH, int MU, bool WIDE, int H>
 __device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int64_t bx, uint8_t *lds,
                                            int *wg_flag) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const PackedLayout L(args.N, args.K, args.flags);
+    const PackedLayout L(args.N, args.K, args.flags, args.group_size);
     const uint8_t *w;
     int64_t row0, n, src0 = 0;
     const int32_t *gather = nullptr;
@@ -525,13 +534,13 @@ __device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int
         n = args.T;
         src0 = args.gather_tokens ? 0 : row0;
     }
-    run_tile<EPI, SH, MU, WIDE>(args, L, lds, wg_flag, te, w, row0, n, src0, gather, bx, wave, lane);
+    run_tile<EPI, SH, MU, WIDE, H>(args, L, lds, wg_flag, te, w, row0, n, src0, gather, bx, wave, lane);
 }
 
 // Workgroup ids are dealt to the 8 XCDs in turn (id mod 8): tile tix goes to
 // XCD tix mod 8 and all its column blocks run there back to back, so the
 // activation tile they share is fetched once into that XCD's L2.
-template <int EPI, class SH, int MU>
+template <int EPI, class SH, int MU, int H>
 __device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *tiles, int count) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[SH::kLds];
     __shared__ int wg_flag;
@@ -540,33 +549,33 @@ __device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *t
     const uint32_t kx = blockIdx.x >> 3;
     const int tix = (int)((kx / gx) * 8 + (blockIdx.x & 7));
     if (tix >= count) return;
-    tile_entry<EPI, SH, MU, false>(args, tiles[tix], kx % gx, lds, &wg_flag);
+    tile_entry<EPI, SH, MU, false, H>(args, tiles[tix], kx % gx, lds, &wg_flag);
 }
 
-template <int EPI>
+template <int EPI, int H>
 __global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
 prefill_big_kernel(const PrefillArgs args) {
-    fast_pass<EPI, BigShape, BigShape::MS>(args, args.tiles, args.tile_count[0]);
+    fast_pass<EPI, BigShape, BigShape::MS, H>(args, args.tiles, args.tile_count[0]);
 }
 
 // Small tiles of class C: at most 16 << C rows, 1 << C subtiles multiplied.
-template <int EPI, int C>
+template <int EPI, int C, int H>
 __global__ void __launch_bounds__(SmallShape::W * 64, SmallShape::OCC)
 prefill_small_kernel(const PrefillArgs args) {
-    fast_pass<EPI, SmallShape, 1 << C>(args, args.tiles + args.max_big + C * args.max_small,
+    fast_pass<EPI, SmallShape, 1 << C, H>(args, args.tiles + args.max_big + C * args.max_small,
                                       args.tile_count[1 + C]);
 }
 
 // Deferred (tile, column block) pairs, with the plain operands (big-tile shape
 // also for small tiles).  A grid-stride loop over the list.
-template <int EPI>
+template <int EPI, int H>
 __global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
 prefill_wide_kernel(const PrefillArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[BigShape::kLds];
     const int count = *args.deferred_count;
     for (int i = blockIdx.x; i < count; i += gridDim.x) {
         const int4 d = args.deferred[i];
-        tile_entry<EPI, BigShape, BigShape::MS, true>(args, make_int2(d.x, d.y), d.z, lds, nullptr);
+        tile_entry<EPI, BigShape, BigShape::MS, true, H>(args, make_int2(d.x, d.y), d.z, lds, nullptr);
         __syncthreads();   // LDS is reused by the next entry
     }
 }
@@ -653,7 +662,7 @@ int side_stream(SideStream **out) {
     return QI4_OK;
 }
 
-template <int EPI>
+template <int EPI, int H>
 int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsigned gs) {
     const unsigned tb = BigShape::W * 64, ts = SmallShape::W * 64;
     SideStream *ss = nullptr;
@@ -664,11 +673,11 @@ int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsign
         if (hipEventRecord(ss->fork, st) != hipSuccess) return QI4_ERR_HIP;
         for (int i = 0; i < kSideStreams; ++i)
             if (hipStreamWaitEvent(ss->s[i], ss->fork, 0) != hipSuccess) return QI4_ERR_HIP;
-        prefill_small_kernel<EPI, 0><<<gs, ts, 0, ss->s[0]>>>(a);
-        prefill_small_kernel<EPI, 1><<<gs, ts, 0, ss->s[1]>>>(a);
-        prefill_small_kernel<EPI, 2><<<gs, ts, 0, ss->s[2]>>>(a);
+        prefill_small_kernel<EPI, 0, H><<<gs, ts, 0, ss->s[0]>>>(a);
+        prefill_small_kernel<EPI, 1, H><<<gs, ts, 0, ss->s[1]>>>(a);
+        prefill_small_kernel<EPI, 2, H><<<gs, ts, 0, ss->s[2]>>>(a);
         if ((rc = launch_status())) return rc;
-        prefill_big_kernel<EPI><<<gb, tb, 0, st>>>(a);
+        prefill_big_kernel<EPI, H><<<gb, tb, 0, st>>>(a);
         if ((rc = launch_status())) return rc;
         for (int i = 0; i < kSideStreams; ++i) {
             if (hipEventRecord(ss->join[i], ss->s[i]) != hipSuccess) return QI4_ERR_HIP;
@@ -676,7 +685,7 @@ int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsign
         }
     }
     // tiles deferred by either kind, after both
-    prefill_wide_kernel<EPI><<<512, tb, 0, st>>>(a);   // two workgroups per CU
+    prefill_wide_kernel<EPI, H><<<512, tb, 0, st>>>(a);   // two workgroups per CU
     return launch_status();
 }
 }  // namespace
@@ -687,9 +696,12 @@ int launch_prefill(const PrefillArgs &a, hipStream_t st) {
     const int64_t gb = gx * ceil_div(a.max_big, 8) * 8, gs = gx * ceil_div(a.max_small, 8) * 8;
     if (gb > 0x7fffffff || gs > 0x7fffffff) return QI4_ERR_SHAPE;
     if (gb + 3 * gs > a.max_deferred) return QI4_ERR_SHAPE;
+    const bool h2 = halves_for(a.group_size) == 2;
     if (a.epi == QI4_EPI_SILU_MUL)
-        return launch_prefill_epi<QI4_EPI_SILU_MUL>(a, st, (unsigned)gb, (unsigned)gs);
-    return launch_prefill_epi<QI4_EPI_NONE>(a, st, (unsigned)gb, (unsigned)gs);
+        return h2 ? launch_prefill_epi<QI4_EPI_SILU_MUL, 2>(a, st, (unsigned)gb, (unsigned)gs)
+                  : launch_prefill_epi<QI4_EPI_SILU_MUL, 1>(a, st, (unsigned)gb, (unsigned)gs);
+    return h2 ? launch_prefill_epi<QI4_EPI_NONE, 2>(a, st, (unsigned)gb, (unsigned)gs)
+              : launch_prefill_epi<QI4_EPI_NONE, 1>(a, st, (unsigned)gb, (unsigned)gs);
 }
 
 }  // namespace qi4

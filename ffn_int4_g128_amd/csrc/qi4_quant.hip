@@ -1,10 +1,10 @@
 // Load-time int4 quantizer: float32 or bf16 weights -> canonical codes, scales
-// and zero points for groups of 128 along K.
+// and zero points for groups of 64, 128, 256, ... (up to a whole row) along K.
 //
 // The fastllm README (gittoolsai.com), section "model export", notes that
 // loading a model with an int4 dtype quantizes it online at every load, which is
-// slow.  This kernel does that step on the GPU.  Per group of 128 weights w of
-// one row (asymmetric min/max, with 0 always inside the range):
+// slow.  This kernel does that step on the GPU.  Per group of weights w of one
+// row (asymmetric min/max, with 0 always inside the range):
 //   lo = min(0, min w), hi = max(0, max w)
 //   scale = (hi - lo) / 15 rounded to binary16 (nearest, ties to even);
 //           1.0 when that rounds to 0
@@ -22,8 +22,7 @@ namespace qi4 {
 namespace {
 
 constexpr int kQuantWaves = 4;    // waves per workgroup
-constexpr int kQuantPasses = 4;   // passes of 4 groups per wave, loads issued together
-constexpr int kGroupsPerWave = 4 * kQuantPasses;
+constexpr int kQuantPasses = 4;   // passes per wave, loads issued together
 
 // Nearest binary16 (ties to even) of a non-negative, non-NaN double.  Scaling
 // by a power of two is exact, so rint of the scaled value is the rounding.
@@ -47,46 +46,83 @@ __device__ inline uint32_t f64_to_f16_bits_rne(double v) {
 
 __device__ inline double clamp15(double v) { return v < 0.0 ? 0.0 : (v > 15.0 ? 15.0 : v); }
 
-// Each 16-lane segment of a wave quantizes one group; lane j of the segment owns
-// the 8 weights 8j .. 8j+7 (one 16- or 32-byte load, one 4-byte code store).  A
-// wave takes kGroupsPerWave consecutive groups (row-major order), in passes of 4,
-// with every pass's loads issued before any is used.
+// Eight consecutive weights (float32 or bf16) at element offset off.
 template <bool F32>
+__device__ inline void load8(const void *w, int64_t off, float (&v)[8]) {
+    if constexpr (F32) {
+        const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + off);
+        const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + off + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + off);
+        const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v[2 * c] = bf16_to_f32(u[c] & 0xFFFFu);
+            v[2 * c + 1] = bf16_to_f32(u[c] >> 16);
+        }
+    }
+}
+
+// Scale (binary16 bits and value) and zero of a group with range [lo, hi].
+__device__ inline void scale_zero(float lo, float hi, uint32_t &sb, double &s, double &z) {
+    sb = f64_to_f16_bits_rne(((double)hi - (double)lo) / 15.0);
+    s = (double)__builtin_bit_cast(_Float16, (uint16_t)sb);
+    if (s == 0.0) {
+        sb = 0x3C00u;   // binary16 1.0
+        s = 1.0;
+    }
+    z = clamp15(rint(-(double)lo / s));
+}
+
+// Codes of eight weights, even k in the low nibble.  rint(w / s) is formed
+// from x = w * (1/s) in float32 (w and s are exact in float32; two roundings:
+// |x - w/s| <= |x| 2^-23 <= 4e-6 for |x| <= 32).  Away from the half-integers
+// x rounds like w/s; within 1e-4 of one the decision is taken on the binary64
+// quotient.  Beyond 32 both clamp alike (z <= 15).
+__device__ inline uint32_t codes8(const float (&v)[8], double s, double z) {
+    const float rs = 1.0f / (float)s;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = v[e] * rs;
+        const float r = rintf(x);
+        const double qf = (fabsf(x) > 32.0f || fabsf(fabsf(x - r) - 0.5f) > 1e-4f)
+                              ? (double)r : rint((double)v[e] / s);
+        codes |= (uint32_t)clamp15(qf + z) << (4 * e);
+    }
+    return codes;
+}
+
+// Groups of 8 * SEG weights (SEG = 8, 16, 32 or 64 lanes): each SEG-lane
+// segment of a wave quantizes one group; lane j of the segment owns the 8
+// weights 8j .. 8j+7 (one 16- or 32-byte load, one 4-byte code store).  A wave
+// takes kQuantPasses * (64 / SEG) consecutive groups (row-major order), with
+// every pass's loads issued before any is used.
+template <bool F32, int SEG>
 __global__ void __launch_bounds__(kQuantWaves * 64)
 quantize_kernel(const void *__restrict__ w, int64_t N, int64_t K, uint8_t *__restrict__ qweight,
                 uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros) {
-    const int lane = threadIdx.x & 63, seg = lane >> 4, j = lane & 15;
-    const int64_t G = K / kGroup, total = N * G;
-    const int64_t grp0 = ((int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6)) * kGroupsPerWave;
+    constexpr int GS = 8 * SEG, SPW = 64 / SEG;   // group size, segments per wave
+    const int lane = threadIdx.x & 63, seg = lane / SEG, j = lane % SEG;
+    const int64_t G = K / GS, total = N * G;
+    const int64_t grp0 = ((int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6)) * kQuantPasses * SPW;
     float v[kQuantPasses][8];
 #pragma unroll
     for (int p = 0; p < kQuantPasses; ++p) {
-        const int64_t grp = grp0 + 4 * p + seg;
+        const int64_t grp = grp0 + SPW * p + seg;
         if (grp >= total) {   // past the last group: nothing loaded, nothing stored
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[p][e] = 0.0f;
             continue;
         }
         const int64_t n = grp / G, g = grp - n * G;
-        const int64_t off = n * K + g * kGroup + 8 * j;
-        if constexpr (F32) {
-            const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + off);
-            const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + off + 4);
-            v[p][0] = a.x; v[p][1] = a.y; v[p][2] = a.z; v[p][3] = a.w;
-            v[p][4] = b.x; v[p][5] = b.y; v[p][6] = b.z; v[p][7] = b.w;
-        } else {
-            const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + off);
-            const uint32_t u[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                v[p][2 * c] = bf16_to_f32(u[c] & 0xFFFFu);
-                v[p][2 * c + 1] = bf16_to_f32(u[c] >> 16);
-            }
-        }
+        load8<F32>(w, n * K + g * GS + 8 * j, v[p]);
     }
 #pragma unroll
     for (int p = 0; p < kQuantPasses; ++p) {
-        const int64_t grp = grp0 + 4 * p + seg;
+        const int64_t grp = grp0 + SPW * p + seg;
         // fminf/fmaxf skip NaN operands; min/max are exact in float32
         float lo = 0.0f, hi = 0.0f;
 #pragma unroll
@@ -94,40 +130,88 @@ quantize_kernel(const void *__restrict__ w, int64_t N, int64_t K, uint8_t *__res
             lo = fminf(lo, v[p][e]);
             hi = fmaxf(hi, v[p][e]);
         }
-        for (int o = 8; o >= 1; o >>= 1) {   // within the 16-lane segment
+        for (int o = SEG / 2; o >= 1; o >>= 1) {   // within the segment
             lo = fminf(lo, __shfl_xor(lo, o));
             hi = fmaxf(hi, __shfl_xor(hi, o));
         }
         if (grp >= total) continue;
         const int64_t n = grp / G, g = grp - n * G;
-        uint32_t sb = f64_to_f16_bits_rne(((double)hi - (double)lo) / 15.0);
-        double s = (double)__builtin_bit_cast(_Float16, (uint16_t)sb);
-        if (s == 0.0) {
-            sb = 0x3C00u;   // binary16 1.0
-            s = 1.0;
-        }
-        const double z = clamp15(rint(-(double)lo / s));
-        // rint(w / s) from x = w * (1/s) in float32 (w and s are exact in
-        // float32; two roundings: |x - w/s| <= |x| 2^-23 <= 4e-6 for |x| <= 32).
-        // Away from the half-integers x rounds like w/s; within 1e-4 of one the
-        // decision is taken on the binary64 quotient.  Beyond 32 both clamp
-        // alike (z <= 15).
-        const float rs = 1.0f / (float)s;
-        uint32_t codes = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = v[p][e] * rs;
-            const float r = rintf(x);
-            const double qf = (fabsf(x) > 32.0f || fabsf(fabsf(x - r) - 0.5f) > 1e-4f)
-                                  ? (double)r : rint((double)v[p][e] / s);
-            codes |= (uint32_t)clamp15(qf + z) << (4 * e);   // even k in the low nibble
-        }
-        *reinterpret_cast<uint32_t *>(qweight + n * (K / 2) + g * (kGroup / 2) + 4 * j) = codes;
+        uint32_t sb;
+        double sd, z;
+        scale_zero(lo, hi, sb, sd, z);
+        *reinterpret_cast<uint32_t *>(qweight + n * (K / 2) + g * (GS / 2) + 4 * j) = codes8(v[p], sd, z);
         if (j == 0) {
             scales[n * G + g] = (uint16_t)sb;
             zeros[n * G + g] = (uint8_t)z;
         }
     }
+}
+
+// Other group sizes (multiples of 128 other than 128, 256, 512, up to a whole
+// row): one wave per group, two passes over it (range, then codes), 512
+// weights per wave step.
+template <bool F32>
+__global__ void __launch_bounds__(kQuantWaves * 64)
+quantize_long_kernel(const void *__restrict__ w, int64_t N, int64_t K, int64_t GS,
+                     uint8_t *__restrict__ qweight, uint16_t *__restrict__ scales,
+                     uint8_t *__restrict__ zeros) {
+    const int lane = threadIdx.x & 63;
+    const int64_t G = K / GS;
+    const int64_t grp = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
+    if (grp >= N * G) return;   // whole waves leave
+    const int64_t n = grp / G, g = grp - n * G;
+    const int64_t base = n * K + g * GS;
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t i = 8 * lane; i < GS; i += 512) {
+        float v[8];
+        load8<F32>(w, base + i, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo = fminf(lo, v[e]);
+            hi = fmaxf(hi, v[e]);
+        }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, o));
+        hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    uint32_t sb;
+    double sd, z;
+    scale_zero(lo, hi, sb, sd, z);
+    for (int64_t i = 8 * lane; i < GS; i += 512) {
+        float v[8];
+        load8<F32>(w, base + i, v);
+        *reinterpret_cast<uint32_t *>(qweight + n * (K / 2) + (g * GS + i) / 2) = codes8(v, sd, z);
+    }
+    if (lane == 0) {
+        scales[n * G + g] = (uint16_t)sb;
+        zeros[n * G + g] = (uint8_t)z;
+    }
+}
+
+template <bool F32>
+int launch_quantize(const void *w, int64_t N, int64_t K, int64_t gs, uint8_t *qweight,
+                    uint16_t *scales, uint8_t *zeros, hipStream_t st) {
+    const int64_t groups = N * (K / gs);
+    const unsigned threads = kQuantWaves * 64;
+    if (gs != 64 && gs != 128 && gs != 256 && gs != 512) {
+        const int64_t blocks = ceil_div(groups, kQuantWaves);
+        if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
+        quantize_long_kernel<F32><<<(unsigned)blocks, threads, 0, st>>>(w, N, K, gs, qweight, scales, zeros);
+        return launch_status();
+    }
+    const int seg = (int)(gs / 8);
+    const int64_t blocks = ceil_div(groups, (int64_t)kQuantWaves * kQuantPasses * (64 / seg));
+    if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
+    const dim3 g((unsigned)blocks);
+    switch (seg) {
+    case 8: quantize_kernel<F32, 8><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 16: quantize_kernel<F32, 16><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 32: quantize_kernel<F32, 32><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 64: quantize_kernel<F32, 64><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    default: return QI4_ERR_GROUP;
+    }
+    return launch_status();
 }
 
 }  // namespace
@@ -141,20 +225,16 @@ extern "C" int qi4_quantize(const void *w, int w_dtype, int64_t N, int64_t K, in
     if (w_dtype != QI4_F32 && w_dtype != QI4_BF16) return QI4_ERR_DTYPE;
     int rc = check_matrix(N, K, group_size, 0);
     if (rc) return rc;
+    const int64_t gs = effective_group(group_size, K);
     const int64_t es = w_dtype == QI4_F32 ? 4 : 2;
     if (!aligned(w, 16) || !aligned(qweight, 4) || !aligned(scales, 2)) return QI4_ERR_SHAPE;
-    const int64_t G = K / kGroup;
+    const int64_t G = K / gs;
     if (overlaps(w, N * K * es, qweight, N * K / 2) || overlaps(w, N * K * es, scales, N * G * 2) ||
         overlaps(w, N * K * es, zeros, N * G) || overlaps(qweight, N * K / 2, scales, N * G * 2) ||
         overlaps(qweight, N * K / 2, zeros, N * G) || overlaps(scales, N * G * 2, zeros, N * G))
         return QI4_ERR_ALIAS;
-    const int64_t blocks = ceil_div(N * G, kQuantWaves * kGroupsPerWave);
-    if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
     if ((rc = check_device())) return rc;
     hipStream_t st = as_stream(stream);
-    if (w_dtype == QI4_F32)
-        quantize_kernel<true><<<(unsigned)blocks, kQuantWaves * 64, 0, st>>>(w, N, K, qweight, scales, zeros);
-    else
-        quantize_kernel<false><<<(unsigned)blocks, kQuantWaves * 64, 0, st>>>(w, N, K, qweight, scales, zeros);
-    return launch_status();
+    return w_dtype == QI4_F32 ? launch_quantize<true>(w, N, K, gs, qweight, scales, zeros, st)
+                              : launch_quantize<false>(w, N, K, gs, qweight, scales, zeros, st);
 }

@@ -1,7 +1,7 @@
 /*
- * qi4.h -- C ABI of libqi4: int4 group-quantized (groups of 128 along K, one
- * binary16 scale and one 4-bit zero point per group) linear layer and routed
- * mixture-of-experts FFN for AMD MI355X (gfx950).
+ * qi4.h -- C ABI of libqi4: int4 group-quantized (groups of 128 along K by
+ * default, one binary16 scale and one 4-bit zero point per group) linear layer
+ * and routed mixture-of-experts FFN for AMD MI355X (gfx950).
  *
  * What is computed follows these pages:
  *  - "FastLLM: zero-dependency CPU inference framework ..." (pgsm.cn),
@@ -10,9 +10,12 @@
  *    group by group so the product reads contiguous memory, and the product
  *    runs "read 4-bit weight -> dequantize -> multiply" with no extra pass;
  *    section 2.3: the matrix multiply is a core operator below the model layer.
+ *    Section 4.2 "model conversion and format": the group size defaults to 128;
+ *    64 and 256 are allowed.
  *  - fastllm README (gittoolsai.com), "other parameters": --moe_experts sets
  *    how many routed experts each token uses; --cuda_se runs the shared expert
- *    on the GPU.  "Inference precision": int4g is the grouped int4 type.
+ *    on the GPU.  "Inference precision": int4g is the grouped int4 type, int4
+ *    the plain one (read here as one scale and zero per row: group_size 0).
  *  - FastLLM notes (wmrh.cn), part 1: a MoE layer holds many experts but each
  *    token activates only a few of them.
  * Dequantization is w = scale * (q - zero).  Expert FFN is
@@ -28,9 +31,12 @@
  *    nothing was launched and no output was touched.  A failed launch returns
  *    QI4_ERR_HIP.  No C++ exception crosses this ABI.
  *  - Outputs must not overlap inputs (QI4_ERR_ALIAS where checked).
- *  - Only group_size == 128 is built (QI4_ERR_GROUP otherwise); K must be a
- *    multiple of 128 (QI4_ERR_SHAPE).  The device must be gfx950
- *    (QI4_ERR_UNSUPPORTED otherwise).
+ *  - group_size is 64, a multiple of 128 that divides K (256, ...), or 0 for one
+ *    group per row (per-channel int4); anything else is QI4_ERR_GROUP, and a
+ *    group size that does not divide K is QI4_ERR_SHAPE.  K must be a multiple
+ *    of 128 (QI4_ERR_SHAPE).  A packed matrix is read with the group size it
+ *    was packed with.  The device must be gfx950 (QI4_ERR_UNSUPPORTED
+ *    otherwise).
  *  - Calls are reentrant.  The global state is a cached per-device
  *    architecture check and, for MoE batches of 128 tokens or more, three
  *    internal side streams per device (with their events), created on first
@@ -38,25 +44,28 @@
  *    ordered after the work already enqueued on `stream` and before anything
  *    enqueued on `stream` after the call, so the caller sees one stream.
  *
- * Canonical (interchange) format of a quantized matrix W [N][K] (out x in):
+ * Canonical (interchange) format of a quantized matrix W [N][K] (out x in), with
+ * Gs = group size (K when group_size is 0):
  *    qweight uint8  [N][K/2]    code of (n, k) in byte k/2, even k in the low nibble
- *    scales  uint16 [N][K/128]  IEEE binary16 bit patterns
- *    zeros   uint8  [N][K/128]  zero point, 0..15
+ *    scales  uint16 [N][K/Gs]   IEEE binary16 bit patterns
+ *    zeros   uint8  [N][K/Gs]   zero point, 0..15
  * A [gate; up] matrix of an FFN has N = 2*I rows: rows [0, I) gate, [I, 2I) up.
  *
  * Packed (device) format, produced by qi4_pack: rows are cut into 16-row tiles
  * (with QI4_PACK_GATEUP, tile 2m holds gate rows 16m.. and tile 2m+1 the up rows
  * with the same index, so a tile pair yields 16 outputs of SiLU(gate)*up).
- * Let nt = number of tiles, G = K/128, and nq = ceil(nt/4) "quads" of four
- * consecutive tiles (tile t is slot t%4 of quad t/4).  Three regions follow
- * each other:
- *    codes  nt*G*1024 bytes  [tile][group][lane 0..63][16 bytes]
- *    scales nq*G*128 bytes   [quad][group][row 0..15][slot 0..3] binary16
- *    zeros  nq*G*32 bytes    [quad][group][row 0..15][2 bytes], slot s in nibble s
- * and the total is rounded up to a multiple of 256 bytes.
- * Lane 16*j + r of a tile/group block holds row r's codes for k in
+ * Let nt = number of tiles, G = K/128 (128-wide blocks of K), nq = ceil(nt/4)
+ * "quads" of four consecutive tiles (tile t is slot t%4 of quad t/4), and
+ * h = 2 for 64-wide groups (a block holds two groups), else 1.  Three regions
+ * follow each other:
+ *    codes  nt*G*1024 bytes    [tile][block][lane 0..63][16 bytes]
+ *    scales nq*G*h*128 bytes   [quad][block][half][row 0..15][slot 0..3] binary16
+ *    zeros  nq*G*h*32 bytes    [quad][block][half][row 0..15][2 bytes], slot s in nibble s
+ * and the total is rounded up to a multiple of 256 bytes.  With groups of 128
+ * or more, the records of every block of a group repeat that group's values.
+ * Lane 16*j + r of a tile/block holds row r's codes for k in
  * 128*g + 32*s + 8*j + [0, 8) in its dword s (s = 0..3), so one 16-byte load per
- * lane brings a wave exactly one group of 16 rows.  Missing rows (N not a multiple
+ * lane brings a wave exactly one block of 16 rows.  Missing rows (N not a multiple
  * of 16) are packed as zeros.  The layout is private to this library: only
  * qi4_pack writes it and only the calls below read it.
  */
@@ -76,7 +85,7 @@ enum {
     QI4_ERR_NULL = -1,        /* a required pointer is NULL                          */
     QI4_ERR_SHAPE = -2,       /* a size is out of range or K % 128 != 0               */
     QI4_ERR_DTYPE = -3,       /* unknown dtype or epilogue code                       */
-    QI4_ERR_GROUP = -4,       /* group_size != 128                                    */
+    QI4_ERR_GROUP = -4,       /* group_size not 0, 64 or a multiple of 128            */
     QI4_ERR_WORKSPACE = -5,   /* workspace too small                                  */
     QI4_ERR_ALIAS = -6,       /* an output overlaps an input                          */
     QI4_ERR_UNSUPPORTED = -7, /* device is not gfx950, or flags/epilogue combination */
@@ -94,13 +103,13 @@ int qi4_abi_version(void);
 const char *qi4_status_string(int status);
 
 /* Bytes of the packed format for an N x K matrix; negative status on bad
-   arguments (N < 1, K < 128, K % 128, group_size != 128, unknown flags, or
-   QI4_PACK_GATEUP with odd N). */
+   arguments (N < 1, K < 128, K % 128, an unsupported group_size or one that
+   does not divide K, unknown flags, or QI4_PACK_GATEUP with odd N). */
 int64_t qi4_packed_bytes(int64_t N, int64_t K, int group_size, int flags);
 
 /* Canonical -> packed (the offline reorder: each group of 16 rows becomes one
    contiguous kilobyte per wave load).  Exact: qi4_unpack inverts it bit for
-   bit.  `packed` must hold qi4_packed_bytes(N, K, 128, flags) bytes. */
+   bit.  `packed` must hold qi4_packed_bytes(N, K, group_size, flags) bytes. */
 int qi4_pack(const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
              int64_t N, int64_t K, int group_size, int flags, void *packed, void *stream);
 
@@ -116,8 +125,8 @@ int qi4_dequant_f32(const void *packed, int64_t N, int64_t K, int group_size, in
                     float *w, void *stream);
 
 /* Load-time quantizer: w [N][K] (float32 or bf16 per w_dtype, 16-byte aligned;
- * qweight 4-byte aligned) -> canonical qweight, scales, zeros (the format above), groups
- * of 128.  The fastllm README (gittoolsai.com), section "model export": loading
+ * qweight 4-byte aligned) -> canonical qweight, scales, zeros (the format above), in
+ * groups of group_size (0: one per row).  The fastllm README (gittoolsai.com), section "model export": loading
  * with an int4 dtype quantizes online at every load, which is slow; this is that
  * step on the GPU.  Per group (asymmetric min/max, 0 always inside the range):
  *   lo = min(0, min w), hi = max(0, max w)
@@ -143,11 +152,19 @@ int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,
                       const void *packed_w, int64_t N, int flags,
                       void *y, int y_dtype, int epilogue, void *stream);
 
+/* The same linear layer for a matrix packed with any supported group_size (64,
+ * a multiple of 128 dividing K, or 0 for one group per row); qlinear_int4_g128
+ * is this call with group_size 128.  Section 4.2 of the FastLLM page above
+ * allows group sizes 64 and 256 besides 128. */
+int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
+                 const void *packed_w, int64_t N, int group_size, int flags,
+                 void *y, int y_dtype, int epilogue, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Routed mixture-of-experts FFN (decode and prefill).
  * Routed expert e uses packed gate/up block w_gate_up + e * qi4_packed_bytes(2I, H,
- * 128, QI4_PACK_GATEUP) and packed down block w_down + e * qi4_packed_bytes(H, I,
- * 128, 0).  The shared expert (has_shared != 0) has the same two shapes and is
+ * group_size, QI4_PACK_GATEUP) and packed down block w_down + e *
+ * qi4_packed_bytes(H, I, group_size, 0).  The shared expert (has_shared != 0) has the same two shapes and is
  * added with weight 1.
  * ------------------------------------------------------------------------- */
 typedef struct {
@@ -155,7 +172,7 @@ typedef struct {
     int64_t hidden;        /* H, multiple of 128                                */
     int64_t inter;         /* I, expert intermediate size, multiple of 128      */
     int32_t top_k;         /* routed experts per token (1..min(E, 32))           */
-    int32_t group_size;    /* must be 128                                       */
+    int32_t group_size;    /* 64, a multiple of 128 dividing H and I, or 0      */
     int32_t has_shared;    /* 0 or 1                                            */
     int32_t flags;         /* must be 0                                         */
 } qi4_moe_desc;            /* host struct                                       */

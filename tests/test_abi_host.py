@@ -50,15 +50,24 @@ def test_packed_bytes(q):
     # 16-row tiles x 128-wide groups: 1024 B of codes each; per group, the
     # scales (128 B) and zeros (32 B) of each quad of 4 tiles (the last quad
     # padded); the total rounded up to 256 B
-    def size(nt, G):
-        return ((nt * G * 1024 + -(-nt // 4) * G * 160 + 255) // 256) * 256
+    def size(nt, G, h=1):
+        return ((nt * G * 1024 + -(-nt // 4) * G * 160 * h + 255) // 256) * 256
     assert L.qi4_packed_bytes(16, 128, 128, 0) == 1280 == size(1, 1)  # 1184 rounded up
     assert L.qi4_packed_bytes(4096, 4096, 128, 0) == 256 * 32 * 1064 == size(256, 32)
     assert L.qi4_packed_bytes(17, 256, 128, 0) == 4608 == size(2, 2)
     # gate/up: each half padded to whole tiles
     assert L.qi4_packed_bytes(48, 128, 128, 1) == size(4, 1)
     assert L.qi4_packed_bytes(16, 100, 128, 0) == -2
-    assert L.qi4_packed_bytes(16, 128, 64, 0) == -4
+    # group sizes: 64 (two halves per block record), multiples of 128 dividing K
+    # and 0 (one group per row) share the g128 size
+    assert L.qi4_packed_bytes(17, 256, 64, 0) == size(2, 2, 2)
+    assert L.qi4_packed_bytes(17, 256, 256, 0) == size(2, 2)
+    assert L.qi4_packed_bytes(17, 768, 384, 0) == size(2, 6)
+    assert L.qi4_packed_bytes(17, 256, 0, 0) == size(2, 2)
+    assert L.qi4_packed_bytes(16, 128, 256, 0) == -2   # does not divide K
+    assert L.qi4_packed_bytes(16, 128, 100, 0) == -4
+    assert L.qi4_packed_bytes(16, 128, 32, 0) == -4
+    assert L.qi4_packed_bytes(16, 128, -128, 0) == -4
     assert L.qi4_packed_bytes(17, 128, 128, 1) == -2
     assert L.qi4_packed_bytes(0, 128, 128, 0) == -2
     assert L.qi4_packed_bytes(16, 128, 128, 4) == -7
@@ -79,7 +88,10 @@ def test_argument_errors_return_before_any_launch(q):
     assert L.qlinear_int4_g128(x, 1, 4, 128, ctypes.c_void_p(0x200000), 16, 0,
                                ctypes.c_void_p(0x100000 + 64), 1, 0, None) == -6
     assert L.qlinear_int4_g128(ctypes.c_void_p(0x1004), 1, 1, 128, p, 16, 0, p, 1, 0, None) == -2
-    assert L.qi4_pack(p, p, p, 16, 128, 64, 0, p, None) == -4
+    assert L.qi4_pack(p, p, p, 16, 128, 96, 0, p, None) == -4
+    assert L.qi4_pack(p, p, p, 16, 128, 256, 0, p, None) == -2   # group does not divide K
+    assert L.qlinear_int4(p, 1, 1, 128, p, 16, 192, 0, p, 1, 0, None) == -4
+    assert L.qlinear_int4(p, 1, 1, 384, p, 16, 256, 0, p, 1, 0, None) == -2
     assert L.qi4_pack(None, p, p, 16, 128, 128, 0, p, None) == -1
     assert L.qi4_dequant_f32(p, 16, 96, 128, 0, p, None) == -2
     assert L.moe_route_topk(p, 4, 8, 9, p, p, None) == -2
@@ -88,7 +100,7 @@ def test_argument_errors_return_before_any_launch(q):
     # quantizer: NULL, dtype, group size, K, alignment, overlapping outputs
     assert L.qi4_quantize(None, 1, 16, 128, 128, p, p, p, None) == -1
     assert L.qi4_quantize(p, 5, 16, 128, 128, p, p, p, None) == -3
-    assert L.qi4_quantize(p, 1, 16, 128, 64, p, p, p, None) == -4
+    assert L.qi4_quantize(p, 1, 16, 128, 32, p, p, p, None) == -4
     assert L.qi4_quantize(p, 1, 16, 100, 128, p, p, p, None) == -2
     assert L.qi4_quantize(ctypes.c_void_p(0x1008), 1, 16, 128, 128, p, p, p, None) == -2
     w = ctypes.c_void_p(0x100000)
@@ -100,7 +112,11 @@ def test_moe_descriptor_errors(q):
     D = q._MoeDesc
     ok = D(256, 7168, 2048, 8, 128, 1, 0)
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(ok), 32) > 0
-    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 64, 1, 0)), 1) == -4
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 64, 1, 0)), 1) > 0
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 0, 1, 0)), 1) > 0
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 96, 1, 0)), 1) == -4
+    # 896 (7 x 128) divides hidden (7168) but not inter (2048)
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 896, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7000, 2048, 8, 128, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(4, 7168, 2048, 8, 128, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 2, 0)), 1) == -7
