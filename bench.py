@@ -14,13 +14,13 @@ The step runs the five stages through the C ABI (route, sort, grouped
 gate/up + SiLU, grouped down, combine); HIP events on the launch stream time
 each grouped GEMM inside the timed region.  The events are created without a
 system-scope fence (TimingEvent): a fenced event writes back and invalidates the
-caches at every record, a 5-6 us gap that no real forward pays.  The JSON line reports tokens/s of
-the main batch size, the roofline of the dominant kernel (grouped gate/up),
+caches at every record, a 5-6 us gap that no real forward pays.  The JSON line
+reports tokens/s of the main batch size, the roofline of the dominant kernel (grouped gate/up),
 and the oracle's CPU time on a bounded sample as a baseline.  Extra fields
 report the other decode batch sizes, the T=2048 prefill step (Zipf-skewed
-routing) and, with a cold last-level cache, the dense linears (the
-Llama-7B-shaped decode stack at T=1 and the skinny sweep) and the load-time
-quantizer.
+routing), with a cold last-level cache the dense linears (the Llama-7B-shaped
+decode stack at T=1 and the skinny sweep), the load-time quantizer, and the
+main decode step with 64-wide groups and with one group per row.
 """
 from __future__ import annotations
 
@@ -122,6 +122,8 @@ def parse():
                     help="timed prefill steps (T=2048, Zipf-skewed routing); 0 to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-linear measurements")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="skip the decode step with other group sizes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     return ap.parse_args()
@@ -140,6 +142,49 @@ def build_layer(c, layer, q, torch):
     torch.cuda.synchronize()
     del ex, sh
     return mw
+
+
+def build_layer_quantized(c, layer, q, torch, group):
+    """A layer of the same shape for another group size: seeded random bf16
+    weights (N(0, 0.02^2)) quantized on the GPU with that group size and packed,
+    expert by expert (fast to build; the values feed timing only)."""
+    E, H, I = c["E"], c["H"], c["I"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 * c["seed"] + 17 * layer + group)
+
+    def one(N, K, flags, out):
+        w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32)
+        w = w.mul_(0.02).to(torch.bfloat16)
+        qw, sc, zr = q.quantize(w, group=group)
+        return q.pack(qw, sc, zr, N, K, flags, out=out, group=group)
+
+    gu_b = q.packed_bytes(2 * I, H, q.QI4_PACK_GATEUP, group)
+    dn_b = q.packed_bytes(H, I, 0, group)
+    w_gu = torch.empty(E * gu_b, dtype=torch.uint8, device="cuda")
+    w_dn = torch.empty(E * dn_b, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        one(2 * I, H, q.QI4_PACK_GATEUP, w_gu[e * gu_b:(e + 1) * gu_b])
+        one(H, I, 0, w_dn[e * dn_b:(e + 1) * dn_b])
+    sgu = one(2 * I, H, q.QI4_PACK_GATEUP, None)
+    sdn = one(H, I, 0, None)
+    torch.cuda.synchronize()
+    return q.MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn, group)
+
+
+def run_group_variants(q, torch, c, T, steps, warmup):
+    """The decode step at batch T with 64-wide groups and with one group per row
+    (group_size 0), two layers each, as the main measurement."""
+    res = []
+    for group in (64, 0):
+        layers = [build_layer_quantized(c, l, q, torch, group) for l in range(2)]
+        r = run_batch(q, torch, layers, c, T, steps, warmup)
+        res.append({"group_size": group, "T": T, "tokens_per_s": r["tokens_per_s"],
+                    "ms_per_step": r["ms_per_step"], "gate_up_GBps": r["gate_up_GBps"],
+                    "gate_up_hbm_frac": r["gate_up_GBps"] / HBM_PEAK_GBPS,
+                    "down_GBps": r["down_GBps"], "step_GBps": r["step_GBps"]})
+        del layers
+        torch.cuda.empty_cache()
+    return res
 
 
 class Stepper:
@@ -235,16 +280,19 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     gu_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     H, I = c["H"], c["I"]
-    per_w = workloads.packed_weight_bytes(1)
+    # bytes per weight of the gate/up (groups along H) and down (along I) matrices
+    g = layers[0].group
+    pw_gu = workloads.packed_weight_bytes(1, g or H)
+    pw_dn = workloads.packed_weight_bytes(1, g or I)
     gu_w, dn_w = 2 * I * H, H * I
     # algorithmic bytes per step: weights of the touched experts + the shared one,
     # activations in, outputs out, router logits in
     gu_bytes, dn_bytes, step_bytes = [], [], []
     for i in range(steps):
         n_e = touched[i % period] + 1
-        gu_bytes.append(n_e * gu_w * per_w + T * H * 2 + T * (k + 1) * 2 * I * 2)
-        dn_bytes.append(n_e * dn_w * per_w + T * (k + 1) * 2 * I * 2 + T * (k + 1) * H * 4)
-        step_bytes.append(n_e * (gu_w + dn_w) * per_w + 2 * T * H * 2 + T * c["E"] * 4)
+        gu_bytes.append(n_e * gu_w * pw_gu + T * H * 2 + T * (k + 1) * 2 * I * 2)
+        dn_bytes.append(n_e * dn_w * pw_dn + T * (k + 1) * 2 * I * 2 + T * (k + 1) * H * 4)
+        step_bytes.append(n_e * (gu_w * pw_gu + dn_w * pw_dn) + 2 * T * H * 2 + T * c["E"] * 4)
     mean = lambda v: sum(v) / len(v)
     ms_step = wall * 1e3 / steps
     return {
@@ -482,6 +530,11 @@ def main():
     quant = run_quantize(q, torch)
     log(f"quantize: {json.dumps(quant)}")
 
+    groups = None
+    if not args.no_groups:
+        groups = run_group_variants(q, torch, c, args.T, max(10, args.steps // 2), args.warmup)
+        log(f"group sizes: {json.dumps(groups)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         del layers
@@ -519,6 +572,7 @@ def main():
         "prefill": prefill,
         "dense": dense,
         "quantize": quant,
+        "group_sizes": groups,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
