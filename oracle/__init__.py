@@ -180,6 +180,17 @@ def gate_up_silu(x64: np.ndarray, qweight, scales, zeros, I: int, K: int, group:
 
 # ---- router and permutation ----------------------------------------------
 
+def router_logits(x64: np.ndarray, w_bits: np.ndarray):
+    """Router logits l[t][e] = sum_k x[t][k] * w[e][k] and the magnitude
+    S[t][e] = sum_k |x[t][k] * w[e][k]|, in fp64, for bf16 router weights w [E][H]
+    (bit patterns) and activations already widened to fp64.  The step before the
+    top-k selection (reading R28: a plain bias-free projection of the hidden
+    state onto the E experts); the library matmul is the step."""
+    w64 = widen(np.ascontiguousarray(w_bits), "bf16")
+    x64 = np.ascontiguousarray(x64, dtype=np.float64)
+    return x64 @ w64.T, np.abs(x64) @ np.abs(w64).T
+
+
 def topk_softmax(logits: np.ndarray, k: int):
     """Return (ids int32 [T][k], p float64 [T][k])."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)

@@ -202,3 +202,34 @@ def test_quantizer_error_bound_and_dequant_round_trip(G):
     q = oracle.unpack(qw, 8, 512).astype(np.int64)
     zz = np.repeat(z.astype(np.int64), G, axis=1)
     assert np.array_equal(np.clip(np.rint(wd / sc) + zz, 0, 15), q)
+
+
+# ---- router logits ---------------------------------------------------------------
+
+def test_router_logits_against_exact_rationals():
+    from fractions import Fraction
+    T, E, H = 3, 5, 64
+    w = workloads.router_weights(43, 1, E, H)
+    x = oracle.widen(workloads.activations(43, 2, T, H, "bf16"), "bf16")
+    y, S = oracle.router_logits(x, w)
+    wf = oracle.widen(w, "bf16")
+    for t in range(T):
+        for e in range(E):
+            ex = sum(Fraction(float(x[t, k])) * Fraction(float(wf[e, k])) for k in range(H))
+            mag = sum(abs(Fraction(float(x[t, k])) * Fraction(float(wf[e, k]))) for k in range(H))
+            assert abs(Fraction(float(y[t, e])) - ex) <= Fraction(2 * H) * Fraction(2.0 ** -53) * mag
+            assert abs(Fraction(float(S[t, e])) - mag) <= Fraction(2 * H) * Fraction(2.0 ** -53) * mag
+
+
+def test_router_logits_one_hot_token_reads_one_weight_column():
+    # x = unit vector at k: the logits are column k of the router matrix (rows are
+    # experts), which catches a transposed operand
+    E, H = 7, 256
+    w = workloads.router_weights(44, 1, E, H)
+    x = np.zeros((2, H))
+    x[0, 3] = 1.0
+    x[1, 200] = -2.0
+    y, S = oracle.router_logits(x, w)
+    wf = oracle.widen(w, "bf16")
+    assert np.array_equal(y[0], wf[:, 3]) and np.array_equal(y[1], -2.0 * wf[:, 200])
+    assert np.array_equal(S[1], 2.0 * np.abs(wf[:, 200]))

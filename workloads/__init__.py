@@ -21,7 +21,7 @@ import numpy as np
 GROUP = 128
 
 # tensor tags (stream ids)
-_T_QW, _T_SC, _T_ZR, _T_X, _T_LOGIT, _T_PERM = 1, 2, 3, 4, 5, 6
+_T_QW, _T_SC, _T_ZR, _T_X, _T_LOGIT, _T_PERM, _T_ROUTER = 1, 2, 3, 4, 5, 6, 7
 
 
 def rng(*key: int) -> np.random.Generator:
@@ -83,6 +83,14 @@ def _distinct_rows(draw, T: int, E: int) -> np.ndarray:
             attempt += 1
         out[t] = row
     return out
+
+
+def router_weights(seed: int, tag: int, E: int, H: int) -> np.ndarray:
+    """Router matrix [E][H] as bf16 bits: N(0, 1/H) drawn in float32 and rounded,
+    so that logits of N(0,1) activations are about N(0,1)."""
+    w = rng(seed, tag, _T_ROUTER).standard_normal(size=(E, H), dtype=np.float32)
+    w = (w * np.float32(1.0 / np.sqrt(H))).astype(np.float32)
+    return f32_to_bf16_bits(w)
 
 
 def logits_normal(seed: int, tag: int, T: int, E: int) -> np.ndarray:
