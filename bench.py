@@ -19,8 +19,9 @@ reports tokens/s of the main batch size, the roofline of the dominant kernel (gr
 and the oracle's CPU time on a bounded sample as a baseline.  Extra fields
 report the other decode batch sizes, the T=2048 prefill step (Zipf-skewed
 routing), with a cold last-level cache the dense linears (the Llama-7B-shaped
-decode stack at T=1 and the skinny sweep), the load-time quantizer, and the
-main decode step with 64-wide groups and with one group per row.
+decode stack at T=1 and the skinny sweep), the load-time quantizer, the router
+projection with its top-k, and the main decode step with 64-wide groups and with
+one group per row.
 """
 from __future__ import annotations
 
@@ -433,6 +434,40 @@ def run_dense(q, torch, reps=20):
                         f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep}
 
 
+def run_router(q, torch, reps=20):
+    """Router projection (bf16 [E][H] matrix, DeepSeek-V3 shape) plus top-8 through
+    moe_router_topk, with a cold last-level cache (1 GiB read before each rep,
+    outside the fence-free event pair); median over reps."""
+    import statistics
+    import workloads
+    c = workloads.MOE_DECODE
+    E, H, k = c["E"], c["H"], c["top_k"]
+    w = q_bf16(torch, workloads.router_weights(c["seed"], 900, E, H))
+    rd = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    res = []
+    for T in (1, 32, 2048):
+        x = q_bf16(torch, workloads.activations(c["seed"], 901 + T, T, H, "bf16"))
+        logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        ts = []
+        for r in range(reps + 3):
+            torch.sum(rd, dim=0, out=acc)
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record()
+            q.moe_router_topk(x, w, k, logits=logits)
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = statistics.median(ts)
+        b = E * H * 2 + T * H * 2 + T * E * 4 + T * k * 8
+        res.append({"T": T, "us": t * 1e6, "GBps": b / t / 1e9, "tokens_per_s": T / t,
+                    "mfma_TFLOPs": 2 * T * E * H / t / 1e12})
+    del rd
+    return {"workload": "router_deepseekv3_shape_e256_h7168_top8", "protocol": "cold last-level "
+            f"cache, median of {reps} reps; moe_router_topk (projection + top-k)", "points": res}
+
+
 def run_quantize(q, torch, reps=10):
     """Load-time quantizer throughput: bf16 weights [16384][7168] (four experts'
     gate/up rows of the MoE layer), N(0, 0.02), cold cache (1 GiB read before each
@@ -530,6 +565,9 @@ def main():
     quant = run_quantize(q, torch)
     log(f"quantize: {json.dumps(quant)}")
 
+    router = run_router(q, torch)
+    log(f"router: {json.dumps(router)}")
+
     groups = None
     if not args.no_groups:
         groups = run_group_variants(q, torch, c, args.T, max(10, args.steps // 2), args.warmup)
@@ -573,6 +611,7 @@ def main():
         "dense": dense,
         "quantize": quant,
         "group_sizes": groups,
+        "router": router,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

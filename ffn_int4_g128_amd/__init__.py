@@ -70,6 +70,7 @@ def lib():
             "qlinear_int4_g128": (ci, [vp, ci, i64, i64, vp, i64, ci, vp, ci, ci, vp]),
             "qlinear_int4": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
+            "moe_router_topk": (ci, [vp, i64, i64, vp, i64, i32, vp, vp, vp, vp]),
             "moe_sort_tokens": (ci, [vp, i64, i32, i64, vp, vp, vp, vp, vp]),
             "moe_ffn_int4_workspace_bytes": (i64, [dp, i64]),
             "moe_expert_gate_up": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
@@ -87,7 +88,7 @@ def lib():
 # declared in include/qi4.h, in header order
 EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pack", "qi4_unpack",
             "qi4_dequant_f32", "qi4_quantize", "qlinear_int4_g128", "qlinear_int4", "moe_route_topk",
-            "moe_sort_tokens",
+            "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4"]
 
@@ -277,6 +278,23 @@ def moe_route_topk(logits, top_k: int, stream=None):
     _check(lib().moe_route_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(wts), _stream(stream)),
            "moe_route_topk")
     return ids, wts
+
+
+def moe_router_topk(x, w_router, top_k: int, logits=None, stream=None):
+    """x bf16 [T][H], w_router bf16 [E][H] -> (logits float32 [T][E], ids int32 [T][k],
+    weights float32 [T][k])."""
+    import torch
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_topk(_ptr(x), T, H, _ptr(w_router), E, top_k, _ptr(logits), _ptr(ids),
+                                 _ptr(wts), _stream(stream)), "moe_router_topk")
+    return logits, ids, wts
 
 
 def moe_sort_tokens(ids, E: int, stream=None):

@@ -66,20 +66,6 @@ struct Stage {
 };
 
 
-// Buffer resource over [base, base + bytes): loads at offsets past the end
-// return zero, which lets every load of the K loop run unconditionally.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-// Out-of-range offsets.  Valid lane offsets stay below 2^31 (every buffer is
-// smaller than 2 GiB), so kOob (lane part) and kOobS (wave part) reach past
-// every resource and their sum, at most 2^32 - 1, never wraps around.
-constexpr uint32_t kOob = 0x80000000u;
-constexpr uint32_t kOobS = 0x7FFFFFFFu;
-
-__device__ inline uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
 
 // Waves per SIMD the register allocation must allow: the grouped gate/up GEMM
 // sits one register above the four-wave limit without this.

@@ -37,13 +37,9 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 
-// Out-of-range offsets (every buffer here is smaller than 2 GiB): kOob for a
-// lane part, kOobS for a wave part; their sum never wraps around.
-constexpr uint32_t kOob = 0x80000000u;
-constexpr uint32_t kOobS = 0x7FFFFFFFu;
-
+// (kOob / kOobS out-of-range offsets and buffer resources: qi4_dev.h)
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+    return make_rsrc(base, bytes);
 }
 
 __device__ inline f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {

@@ -184,6 +184,19 @@ typedef struct {
 int moe_route_topk(const float *logits, int64_t T, int64_t E, int32_t top_k,
                    int32_t *topk_ids, float *topk_weights, void *stream);
 
+/* Router projection and top-k in one call: the step before the routing above,
+ * logits[t][e] = sum_k x[t][k] * w_router[e][k] with x bf16 [T][H] and
+ * w_router bf16 [E][H] (row e = expert e), no bias, float32 accumulation in a
+ * fixed order (deterministic), written to `logits` [T][E] float32; then the
+ * moe_route_topk selection on those logits.  The pages route each token to a
+ * few of many experts (FastLLM notes, wmrh.cn, part 1; --moe_experts in the
+ * fastllm README); the projection itself is read as a plain linear layer.
+ * H must be a multiple of 32, x and w_router 16-byte aligned; outputs must not
+ * overlap the inputs or each other (QI4_ERR_ALIAS). */
+int moe_router_topk(const void *x, int64_t T, int64_t H, const void *w_router, int64_t E,
+                    int32_t top_k, float *logits, int32_t *topk_ids, float *topk_weights,
+                    void *stream);
+
 /* Token-by-expert permutation (stable counting sort of the T*top_k pairs
  * p = t*top_k + j by expert):
  *   sorted_pairs   [T*top_k]  pairs grouped by expert ascending, tokens ascending

@@ -96,6 +96,12 @@ def test_argument_errors_return_before_any_launch(q):
     assert L.qi4_dequant_f32(p, 16, 96, 128, 0, p, None) == -2
     assert L.moe_route_topk(p, 4, 8, 9, p, p, None) == -2
     assert L.moe_route_topk(p, 4, 2000, 8, p, p, None) == -2
+    # router: H not a multiple of 32, NULL, overlapping logits
+    assert L.moe_router_topk(p, 4, 100, p, 256, 8, p, p, p, None) == -2
+    assert L.moe_router_topk(None, 4, 128, p, 256, 8, p, p, p, None) == -1
+    assert L.moe_router_topk(ctypes.c_void_p(0x100000), 4, 128, ctypes.c_void_p(0x200000), 256, 8,
+                             ctypes.c_void_p(0x100000 + 512), ctypes.c_void_p(0x300000),
+                             ctypes.c_void_p(0x400000), None) == -6
     assert L.moe_sort_tokens(None, 4, 8, 256, p, p, p, None, None) == -1
     # quantizer: NULL, dtype, group size, K, alignment, overlapping outputs
     assert L.qi4_quantize(None, 1, 16, 128, 128, p, p, p, None) == -1

@@ -209,3 +209,32 @@ def test_dsv3_prefill_zipf(dsv3):
     logits = workloads.logits_zipf(p["seed"], 5, T, p["E"], p["zipf"])
     x = workloads.activations(p["seed"], 6, T, p["H"], "bf16")
     _check_layer(c, ex, sh, mw, T, logits, x, "dsv3 prefill zipf", [0, 777, T - 1])
+
+
+@pytest.mark.parametrize("T,E,H,k", [(1, 256, 7168, 8), (32, 256, 7168, 8), (5, 64, 512, 4),
+                                     (70, 300, 1024, 8), (2048, 256, 7168, 8), (3, 8, 32, 8)])
+def test_router_logits_and_topk(T, E, H, k):
+    """Router projection within 2e-3 * sum|x*w| of the oracle; the selection on the
+    GPU's logits bit for bit (the same decision in the same precision), and valid
+    against the oracle's logits within that tolerance."""
+    import torch
+    import ffn_int4_g128_amd as q
+    w = workloads.router_weights(88, E + H, E, H)
+    x = workloads.activations(89, T, T, H, "bf16")
+    logits, ids, wts = q.moe_router_topk(bf16_dev(x), bf16_dev(w), k)
+    torch.cuda.synchronize()
+    L, S = oracle.router_logits(oracle.widen(x, "bf16"), w)
+    got = logits.cpu().numpy()
+    tol = oracle.C_TOL * S
+    assert_within(got.astype(np.float64), L, tol, f"router T{T} E{E} H{H}")
+    oids, op = oracle.topk_softmax(got, k)
+    gids = ids.cpu().numpy()
+    assert np.array_equal(gids, oids)
+    assert np.max(np.abs(wts.cpu().numpy().astype(np.float64) - op)) <= oracle.EPS_P
+    # every selected expert is within tolerance of every one left out
+    for t in range(T):
+        sel = np.zeros(E, dtype=bool)
+        sel[gids[t]] = True
+        if sel.all():
+            continue
+        assert np.min(L[t, sel] + tol[t, sel]) >= np.max(L[t, ~sel] - tol[t, ~sel])
