@@ -106,56 +106,81 @@ __device__ inline float wave_sum(float x) {
 // ---- router logits: a bf16 MFMA GEMM, hidden -> experts -------------------------
 
 constexpr int kRouterWaves = 16;   // waves of a workgroup; they split K
-constexpr int kRouterMT = 4;       // 16-token tiles of a workgroup
 
 // logits[t][e] = sum_k x[t][k] * w[e][k] with x bf16 [T][H], w bf16 [E][H] and
-// float32 accumulation.  A workgroup owns 16 experts x 64 tokens; its waves
-// take consecutive 32-wide k steps and their partial sums are added in LDS in
-// wave order, so the result does not depend on timing.  Out-of-range rows
-// (tokens past T, experts past E) load zeros.
+// float32 accumulation.  A workgroup owns 16 experts x 16 MT tokens; its waves
+// take consecutive 32-wide k steps, CH at a time with all their loads issued
+// before the first MFMA (the k range of a wave is a few steps, so this is most
+// of its memory parallelism), and their partial sums are added in LDS in wave
+// order, so the result does not depend on timing.  Out-of-range rows (tokens
+// past T, experts past E) and steps past the wave's range load zeros.
+template <int MT>
 __global__ void __launch_bounds__(kRouterWaves * 64)
 router_gemm_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int64_t T,
                    int64_t H, int E, float *__restrict__ logits) {
-    __shared__ float red[kRouterWaves * kRouterMT * 256];
+    constexpr int CH = MT == 4 ? 4 : 8;
+    __shared__ float red[kRouterWaves * MT * 256];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, j = lane >> 4;
-    const int64_t e0 = (int64_t)blockIdx.x * 16, t0 = (int64_t)blockIdx.y * (16 * kRouterMT);
+    const int64_t e0 = (int64_t)blockIdx.x * 16, t0 = (int64_t)blockIdx.y * (16 * MT);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(T * H * 2));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)(E * H * 2));
     const int nks = (int)(H / 32);
     const int kb = nks * wave / kRouterWaves, ke = nks * (wave + 1) / kRouterWaves;
     // lane parts of the offsets: the operand row and its 8-element k chunk
     const uint32_t wo = e0 + r16 < E ? (uint32_t)(((e0 + r16) * H + 8 * j) * 2) : kOob;
-    uint32_t xo[kRouterMT];
+    uint32_t xo[MT];
 #pragma unroll
-    for (int m = 0; m < kRouterMT; ++m) {
+    for (int m = 0; m < MT; ++m) {
         const int64_t t = t0 + 16 * m + r16;
         xo[m] = t < T ? (uint32_t)((t * H + 8 * j) * 2) : kOob;
     }
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[kRouterMT];
+    f32x4 acc[MT];
 #pragma unroll
-    for (int m = 0; m < kRouterMT; ++m) acc[m] = zero4;
-    for (int ks = kb; ks < ke; ++ks) {
-        const uint32_t ko = (uint32_t)ks * 64u;   // 32 bf16 per k step (wave-uniform)
-        const bf16x8 b = as_bf16x8(buf_b128(wr, wo, ko));
+    for (int m = 0; m < MT; ++m) acc[m] = zero4;
+    for (int k0 = kb; k0 < ke; k0 += CH) {
+        bf16x8 bv[CH], av[CH][MT];
 #pragma unroll
-        for (int m = 0; m < kRouterMT; ++m)
-            acc[m] = mfma16x16x32(as_bf16x8(buf_b128(xr, xo[m], ko)), b, acc[m]);
+        for (int c = 0; c < CH; ++c) {
+            // 32 bf16 per k step (wave-uniform); steps past the range load zeros
+            const uint32_t ko = k0 + c < ke ? (uint32_t)(k0 + c) * 64u : kOobS;
+            bv[c] = as_bf16x8(buf_b128(wr, wo, ko));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) av[c][m] = as_bf16x8(buf_b128(xr, xo[m], ko));
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32(av[c][m], bv[c], acc[m]);
     }
 #pragma unroll
-    for (int m = 0; m < kRouterMT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[((wave * kRouterMT + m) * 4 + v) * 64 + lane] = acc[m][v];
+        for (int v = 0; v < 4; ++v) red[((wave * MT + m) * 4 + v) * 64 + lane] = acc[m][v];
     __syncthreads();
     // one output per thread: tile m, register v, lane l -> token 4 (l >> 4) + v, expert l & 15
-    const int it = threadIdx.x;
-    const int m = it >> 8, v = (it >> 6) & 3, l = it & 63;
-    float sum = 0.f;
-    for (int ww = 0; ww < kRouterWaves; ++ww) sum += red[((ww * kRouterMT + m) * 4 + v) * 64 + l];
-    const int64_t t = t0 + 16 * m + 4 * (l >> 4) + v, e = e0 + (l & 15);
-    if (t < T && e < E) logits[t * E + e] = sum;
+    for (int it = threadIdx.x; it < MT * 256; it += kRouterWaves * 64) {
+        const int m = it >> 8, v = (it >> 6) & 3, l = it & 63;
+        float sum = 0.f;
+        for (int ww = 0; ww < kRouterWaves; ++ww) sum += red[((ww * MT + m) * 4 + v) * 64 + l];
+        const int64_t t = t0 + 16 * m + 4 * (l >> 4) + v, e = e0 + (l & 15);
+        if (t < T && e < E) logits[t * E + e] = sum;
+    }
+}
+
+int launch_router_gemm(const uint16_t *x, const uint16_t *w, int64_t T, int64_t H, int E,
+                       float *logits, hipStream_t st) {
+    const int MT = T <= 16 ? 1 : T <= 32 ? 2 : 4;
+    const int64_t gy = ceil_div(T, 16 * MT);
+    if (gy > 65535) return QI4_ERR_SHAPE;
+    const dim3 g((unsigned)ceil_div(E, 16), (unsigned)gy);
+    const unsigned tb = kRouterWaves * 64;
+    if (MT == 1) router_gemm_kernel<1><<<g, tb, 0, st>>>(x, w, T, H, E, logits);
+    else if (MT == 2) router_gemm_kernel<2><<<g, tb, 0, st>>>(x, w, T, H, E, logits);
+    else router_gemm_kernel<4><<<g, tb, 0, st>>>(x, w, T, H, E, logits);
+    return launch_status();
 }
 
 // ---- router: one wave per token --------------------------------------------------
@@ -644,7 +669,7 @@ int moe_router_topk(const void *x, int64_t T, int64_t H, const void *w_router, i
     if (E < 1 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK || top_k > E) return QI4_ERR_SHAPE;
     if (H < 32 || H % 32 != 0 || T < 0) return QI4_ERR_SHAPE;
     if (T * H * 2 >= (int64_t(1) << 31) || E * H * 2 >= (int64_t(1) << 31) ||
-        ceil_div(T, 16 * kRouterMT) > 65535)
+        ceil_div(T, 64) > 65535)
         return QI4_ERR_SHAPE;
     if (T == 0) return QI4_OK;
     if (!x || !w_router || !logits || !topk_ids || !topk_weights) return QI4_ERR_NULL;
@@ -659,11 +684,10 @@ int moe_router_topk(const void *x, int64_t T, int64_t H, const void *w_router, i
     int rc = check_device();
     if (rc) return rc;
     hipStream_t st = as_stream(stream);
-    const dim3 g((unsigned)ceil_div(E, 16), (unsigned)ceil_div(T, 16 * kRouterMT));
-    router_gemm_kernel<<<g, kRouterWaves * 64, 0, st>>>(static_cast<const uint16_t *>(x),
-                                                         static_cast<const uint16_t *>(w_router),
-                                                         T, H, (int)E, logits);
-    if ((rc = launch_status())) return rc;
+    if ((rc = launch_router_gemm(static_cast<const uint16_t *>(x),
+                                 static_cast<const uint16_t *>(w_router), T, H, (int)E, logits,
+                                 st)))
+        return rc;
     return launch_route(logits, T, (int)E, top_k, topk_ids, topk_weights, st);
 }
 
