@@ -279,60 +279,96 @@ qgemm_kernel(const GemmArgs args) {
 
             const int64_t tile_b = tile0 + (int64_t)r * NB;
             const int pairs = EPI == QI4_EPI_SILU_MUL ? NB / 2 : NB;
-            const int items = MT * pairs * 64;
+            auto store = [&](int64_t slot, int64_t oc, float val, float uval) {
+                if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
+                const int64_t dst = row0 + slot;
+                if (args.out_mode == OUT_F32) {
+                    static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
+                } else if (args.out_mode == OUT_BF16) {
+                    static_cast<uint16_t *>(args.out)[dst * args.ldo + oc] = (uint16_t)f32_to_bf16_rne(val);
+                } else {
+                    const uint32_t hi = f32_to_bf16_rne(val);
+                    const uint32_t lo = f32_to_bf16_rne(val - bf16_to_f32(hi));
+                    uint16_t *o = static_cast<uint16_t *>(args.out);
+                    o[(dst * 2) * args.ldo + oc] = (uint16_t)hi;
+                    o[(dst * 2 + 1) * args.ldo + oc] = (uint16_t)lo;
+                }
+            };
+            auto out_col = [&](int nbA, int col) -> int64_t {
+                const int64_t tile = tile_b + nbA;
+                if (EPI == QI4_EPI_SILU_MUL) return (tile >> 1) * 16 + col;
+                return tile < nt ? tile_row(tile, col, args.N, args.flags) : -1;
+            };
+            if constexpr (NB == 4) {
+                // grouped expert GEMMs: one thread per result lane, its four rows
+                // together (the register budget of these kernels is tight)
+                const int items = MT * pairs * 64;
+                for (int it = threadIdx.x; it < items; it += blockDim.x) {
+                    const int l = it & 63;
+                    const int rest = it >> 6;
+                    const int pi = rest % pairs;
+                    const int m = rest / pairs;
+                    const int nbA = EPI == QI4_EPI_SILU_MUL ? 2 * pi : pi;
+                    float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int ww = 0; ww < W; ++ww) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            a4[v] += red[((ww * MT + m) * NB + nbA) * 256 + v * 64 + l];
+                            if (EPI == QI4_EPI_SILU_MUL)
+                                b4[v] += red[((ww * MT + m) * NB + nbA + 1) * 256 + v * 64 + l];
+                        }
+                    }
+                    const int64_t oc = out_col(nbA, l & 15);
+                    if (oc < 0 || oc >= args.n_out) continue;
+                    const int rbase = 4 * (l >> 4);
+                    // (static register indices: v0 and p are unrolled, P is 1, 2 or 4)
+#pragma unroll
+                    for (int v0 = 0; v0 < 4; ++v0) {
+                        if (v0 % P != 0) continue;
+                        const int64_t slot = c0 + (int64_t)m * spt + (rbase + v0) / P;
+                        if ((rbase + v0) / P >= spt || slot >= n) continue;
+                        float val = 0.f, uval = 0.f;
+#pragma unroll
+                        for (int p = 0; v0 + p < 4; ++p) {
+                            if (p >= P) break;
+                            val += a4[v0 + p];
+                            uval += b4[v0 + p];
+                        }
+                        store(slot, oc, val, uval);
+                    }
+                }
+            } else {
+            // one thread per output element (M tile, tile or gate/up pair, slot,
+            // column); slots past the end are skipped before any LDS read.  The
+            // sums run over the waves, then over a slot's P parts.
+            const int items = MT * pairs * spt * 16;
             for (int it = threadIdx.x; it < items; it += blockDim.x) {
-                const int l = it & 63;
-                const int rest = it >> 6;
+                const int col = it & 15;
+                int rest = it >> 4;
+                const int sq = rest % spt;
+                rest /= spt;
                 const int pi = rest % pairs;
                 const int m = rest / pairs;
+                const int64_t slot = c0 + (int64_t)m * spt + sq;
+                if (slot >= n) continue;
                 const int nbA = EPI == QI4_EPI_SILU_MUL ? 2 * pi : pi;
-                float a4[4] = {0.f, 0.f, 0.f, 0.f}, b4[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int ww = 0; ww < W; ++ww) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        a4[v] += red[((ww * MT + m) * NB + nbA) * 256 + v * 64 + l];
-                        if (EPI == QI4_EPI_SILU_MUL)
-                            b4[v] += red[((ww * MT + m) * NB + nbA + 1) * 256 + v * 64 + l];
-                    }
-                }
-                const int col = l & 15;
-                const int64_t tile = tile_b + nbA;
-                int64_t oc;
-                if (EPI == QI4_EPI_SILU_MUL)
-                    oc = (tile >> 1) * 16 + col;
-                else
-                    oc = tile < nt ? tile_row(tile, col, args.N, args.flags) : -1;
+                const int64_t oc = out_col(nbA, col);
                 if (oc < 0 || oc >= args.n_out) continue;
-                const int rbase = 4 * (l >> 4);
-                // (static register indices: v0 and p are unrolled, P is 1, 2 or 4)
-#pragma unroll
-                for (int v0 = 0; v0 < 4; ++v0) {
-                    if (v0 % P != 0) continue;
-                    const int rr = rbase + v0;
-                    if (rr / P >= spt) continue;
-                    const int64_t slot = c0 + (int64_t)m * spt + rr / P;
-                    if (slot >= n) continue;
-                    float val = 0.f, uval = 0.f;
-#pragma unroll
-                    for (int p = 0; v0 + p < 4; ++p) {
-                        if (p >= P) break;
-                        val += a4[v0 + p];
-                        uval += b4[v0 + p];
+                const float *ra = red + ((m * NB + nbA) * 256);
+                float val = 0.f, uval = 0.f;
+                for (int p = 0; p < P; ++p) {
+                    const int rr = sq * P + p;   // result row: register rr & 3 of lane group rr >> 2
+                    const int idx = (rr & 3) * 64 + 16 * (rr >> 2) + col;
+                    float a = 0.f, b = 0.f;
+                    for (int ww = 0; ww < W; ++ww) {
+                        a += ra[ww * MT * NB * 256 + idx];
+                        if (EPI == QI4_EPI_SILU_MUL) b += ra[ww * MT * NB * 256 + 256 + idx];
                     }
-                    if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
-                    const int64_t dst = row0 + slot;
-                    if (args.out_mode == OUT_F32) {
-                        static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
-                    } else if (args.out_mode == OUT_BF16) {
-                        static_cast<uint16_t *>(args.out)[dst * args.ldo + oc] = (uint16_t)f32_to_bf16_rne(val);
-                    } else {
-                        const uint32_t hi = f32_to_bf16_rne(val);
-                        const uint32_t lo = f32_to_bf16_rne(val - bf16_to_f32(hi));
-                        uint16_t *o = static_cast<uint16_t *>(args.out);
-                        o[(dst * 2) * args.ldo + oc] = (uint16_t)hi;
-                        o[(dst * 2 + 1) * args.ldo + oc] = (uint16_t)lo;
-                    }
+                    val += a;
+                    uval += b;
                 }
+                store(slot, oc, val, uval);
+            }
             }
             __syncthreads();
 #pragma unroll
