@@ -189,8 +189,9 @@ def run_group_variants(q, torch, c, T, steps, warmup):
 
 
 class Stepper:
-    """Runs the five stages of one MoE forward through the C ABI, with events
-    around the two grouped GEMMs."""
+    """Runs the stages of one MoE forward through the C ABI (routing with the
+    permutation, gate/up, down, combine), with events around the two grouped
+    GEMMs."""
 
     def __init__(self, q, torch, layers, T, top_k, n_batches, c, zipf=None):
         import numpy as np
@@ -231,10 +232,9 @@ class Stepper:
         st = q._stream()
         P = q._ptr
         T, E = self.T, self.c["E"]
-        q._check(L.moe_route_topk(P(self.logits[b]), T, E, self.k, P(self.ids), P(self.wts), st),
-                 "route")
-        q._check(L.moe_sort_tokens(P(self.ids), T, self.k, E, P(self.sp), P(self.off), P(self.inv),
-                                   P(self.act), st), "sort")
+        q._check(L.moe_route_sort(P(self.logits[b]), T, E, self.k, P(self.ids), P(self.wts),
+                                  P(self.sp), P(self.off), P(self.inv), P(self.act), st),
+                 "route_sort")
         if ev is not None:
             ev[0].record()
         q._check(L.moe_expert_gate_up(dref, P(self.x[b]), T, P(self.sp), P(self.off), P(self.act),

@@ -70,6 +70,7 @@ def lib():
             "qlinear_int4_g128": (ci, [vp, ci, i64, i64, vp, i64, ci, vp, ci, ci, vp]),
             "qlinear_int4": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
+            "moe_route_sort": (ci, [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]),
             "moe_router_topk": (ci, [vp, i64, i64, vp, i64, i32, vp, vp, vp, vp]),
             "moe_sort_tokens": (ci, [vp, i64, i32, i64, vp, vp, vp, vp, vp]),
             "moe_ffn_int4_workspace_bytes": (i64, [dp, i64]),
@@ -88,7 +89,7 @@ def lib():
 # declared in include/qi4.h, in header order
 EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pack", "qi4_unpack",
             "qi4_dequant_f32", "qi4_quantize", "qlinear_int4_g128", "qlinear_int4", "moe_route_topk",
-            "moe_router_topk", "moe_sort_tokens",
+            "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4"]
 
@@ -278,6 +279,24 @@ def moe_route_topk(logits, top_k: int, stream=None):
     _check(lib().moe_route_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(wts), _stream(stream)),
            "moe_route_topk")
     return ids, wts
+
+
+def moe_route_sort(logits, top_k: int, stream=None):
+    """Routing and permutation in one call: (ids, weights, sorted_pairs, offsets,
+    pair_to_sorted, active)."""
+    import torch
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    sp = torch.empty(T * top_k, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * top_k, dtype=torch.int32, device=dev)
+    act = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    _check(lib().moe_route_sort(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(wts), _ptr(sp), _ptr(off),
+                                _ptr(inv), _ptr(act), _stream(stream)), "moe_route_sort")
+    return ids, wts, sp, off, inv, act
 
 
 def moe_router_topk(x, w_router, top_k: int, logits=None, stream=None):

@@ -184,6 +184,13 @@ typedef struct {
 int moe_route_topk(const float *logits, int64_t T, int64_t E, int32_t top_k,
                    int32_t *topk_ids, float *topk_weights, void *stream);
 
+/* moe_route_topk followed by moe_sort_tokens (active required), in one call;
+ * for batches of at most 16 tokens one workgroup does both, passing the ids
+ * through on-chip memory (one launch instead of two).  Same outputs. */
+int moe_route_sort(const float *logits, int64_t T, int64_t E, int32_t top_k, int32_t *topk_ids,
+                   float *topk_weights, int32_t *sorted_pairs, int32_t *expert_offsets,
+                   int32_t *pair_to_sorted, int32_t *active, void *stream);
+
 /* Router projection and top-k in one call: the step before the routing above,
  * logits[t][e] = sum_k x[t][k] * w_router[e][k] with x bf16 [T][H] and
  * w_router bf16 [E][H] (row e = expert e), no bias, float32 accumulation in a

@@ -103,6 +103,14 @@ def test_argument_errors_return_before_any_launch(q):
                              ctypes.c_void_p(0x100000 + 512), ctypes.c_void_p(0x300000),
                              ctypes.c_void_p(0x400000), None) == -6
     assert L.moe_sort_tokens(None, 4, 8, 256, p, p, p, None, None) == -1
+    # fused routing + permutation: shape, NULL, aliasing, T == 0
+    assert L.moe_route_sort(p, 4, 8, 9, p, p, p, p, p, p, None) == -2
+    assert L.moe_route_sort(p, 4, 2000, 8, p, p, p, p, p, p, None) == -2
+    assert L.moe_route_sort(p, 4, 256, 8, p, p, p, p, p, None, None) == -1
+    assert L.moe_route_sort(p, 0, 256, 8, p, p, p, p, p, p, None) == 0
+    a = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(7)]
+    assert L.moe_route_sort(a[0], 4, 256, 8, a[1], a[2], a[3], a[4], ctypes.c_void_p(0x500000 + 16),
+                            a[6], None) == -6
     # quantizer: NULL, dtype, group size, K, alignment, overlapping outputs
     assert L.qi4_quantize(None, 1, 16, 128, 128, p, p, p, None) == -1
     assert L.qi4_quantize(p, 5, 16, 128, 128, p, p, p, None) == -3

@@ -63,6 +63,27 @@ def test_sort_tokens_bit_exact(T, E, k):
     assert a[0] == len(nonempty) and np.array_equal(a[1:1 + a[0]], nonempty)
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (8, 256, 8), (16, 256, 8), (17, 256, 8),
+                                   (32, 256, 8), (2048, 256, 8), (3, 1000, 32), (9, 8, 8),
+                                   (16, 1024, 32), (17, 1024, 32), (70, 64, 1), (1, 1, 1)])
+def test_route_sort_bit_exact(T, E, k):
+    """The routing + permutation call (one fused workgroup up to 16 tokens,
+    else the two kernels) gives the oracle's ids and permutation bit for bit."""
+    import ffn_int4_g128_amd as q
+    logits = workloads.logits_normal(63, E + k, T, E)
+    ids, wts, sp, off, inv, act = q.moe_route_sort(to_dev(logits), k)
+    oids, op = oracle.topk_softmax(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.max(np.abs(wts.cpu().numpy().astype(np.float64) - op)) <= oracle.EPS_P
+    osp, ooff, oinv = oracle.sort_tokens(oids, E)
+    assert np.array_equal(sp.cpu().numpy(), osp)
+    assert np.array_equal(off.cpu().numpy(), ooff)
+    assert np.array_equal(inv.cpu().numpy(), oinv)
+    a = act.cpu().numpy()
+    nonempty = np.nonzero(np.diff(ooff))[0]
+    assert a[0] == len(nonempty) and np.array_equal(a[1:1 + a[0]], nonempty)
+
+
 def _small_layer(E, H, I, seed, shared=True):
     ex = workloads.moe_experts(seed, 0, E, H, I, 0.005, 0.02)
     sh = workloads.moe_shared(seed, 0, H, I, 0.005, 0.02) if shared else None
