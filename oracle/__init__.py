@@ -1,7 +1,7 @@
 """qi4 oracle -- TEST INFRASTRUCTURE, NOT PRODUCT CODE.
 
-A plain fp64 CPU implementation of the int4 group-quantized linear layer and
-the routed MoE expert FFN (see ``qi4_oracle.c`` for the definitions and the
+A plain fp64 CPU implementation of the int4 (and 8-bit) group-quantized
+linear layer and the routed MoE expert FFN (see ``qi4_oracle.c`` for the definitions and the
 page passages they follow).  Only ``tests/``, ``__graft_entry__.smoke()`` and
 ``bench.py``'s CPU-baseline leg may import this package.  It shares no code
 with the GPU library and never imports it.
@@ -54,21 +54,24 @@ def lib():
         L.qi4o_f64_to_f16.restype = ctypes.c_uint16
         L.qi4o_silu.argtypes = [ctypes.c_double]
         L.qi4o_silu.restype = ctypes.c_double
-        L.qi4o_unpack.argtypes = [_u8p, _i64, _i64, _u8p]
-        L.qi4o_dequant.argtypes = [_u8p, _u16p, _u8p, _i64, _i64, _i64, _dp]
-        L.qi4o_linear.argtypes = [_dp, _i64, _i64, _u8p, _u16p, _u8p, _i64, _i64,
-                                  _dp, _dp, ctypes.c_int]
-        L.qi4o_gate_up_silu.argtypes = [_dp, _i64, _i64, _u8p, _u16p, _u8p, _i64, _i64,
-                                        ctypes.c_double, _dp, _dp, ctypes.c_int]
+        ci = ctypes.c_int
+        L.qi4o_unpack.argtypes = [_u8p, _i64, _i64, ci, _u8p]
+        L.qi4o_dequant.argtypes = [_u8p, _u16p, _u8p, _i64, _i64, _i64, ci, _dp]
+        L.qi4o_linear.argtypes = [_dp, _i64, _i64, _u8p, _u16p, _u8p, _i64, _i64, ci,
+                                  _dp, _dp, ci]
+        L.qi4o_gate_up_silu.argtypes = [_dp, _i64, _i64, _u8p, _u16p, _u8p, _i64, _i64, ci,
+                                        ctypes.c_double, _dp, _dp, ci]
         L.qi4o_topk_softmax.argtypes = [_fp, _i64, _i64, ctypes.c_int, _i32p, _dp]
         L.qi4o_sort.argtypes = [_i32p, _i64, ctypes.c_int, _i64, _i32p, _i32p, _i32p]
         L.qi4o_moe.argtypes = ([_dp, _i64, _i64, _i64, _i64, ctypes.c_int, _i32p, _dp]
                                + [_u8p, _u16p, _u8p] * 4
-                               + [_i64, ctypes.c_double, ctypes.c_double, _dp, _dp, ctypes.c_int])
-        L.qi4o_quantize.argtypes = [_dp, _i64, _i64, _i64, _u8p, _u16p, _u8p]
+                               + [_i64, ci, ctypes.c_double, ctypes.c_double, _dp, _dp, ci])
+        L.qi4o_quantize.argtypes = [_dp, _i64, _i64, _i64, ci, _u8p, _u16p, _u8p]
         for f in ("qi4o_unpack", "qi4o_dequant", "qi4o_linear", "qi4o_gate_up_silu",
                   "qi4o_topk_softmax", "qi4o_sort", "qi4o_moe", "qi4o_quantize"):
             getattr(L, f).restype = ctypes.c_int
+        if L.qi4o_abi_version() != 2:
+            raise RuntimeError("stale oracle library: rebuild it (oracle.build())")
         _lib = L
     return _lib
 
@@ -123,47 +126,53 @@ def silu(v: float) -> float:
 
 
 # ---- the format ----------------------------------------------------------
+# ``bits`` 4: two codes per byte (qweight [N][K/2]); 8: one code per byte
+# (qweight [N][K]), zeros 0..255.
 
-def unpack(qweight: np.ndarray, N: int, K: int) -> np.ndarray:
+def code_bytes(N: int, K: int, bits: int = 4) -> int:
+    return N * K if bits == 8 else N * (K // 2)
+
+
+def unpack(qweight: np.ndarray, N: int, K: int, bits: int = 4) -> np.ndarray:
     qweight = np.ascontiguousarray(qweight, dtype=np.uint8)
-    assert qweight.size == N * (K // 2)
+    assert qweight.size == code_bytes(N, K, bits)
     q = np.empty((N, K), dtype=np.uint8)
-    _check(lib().qi4o_unpack(_ptr(qweight, _u8p), N, K, _ptr(q, _u8p)), "unpack")
+    _check(lib().qi4o_unpack(_ptr(qweight, _u8p), N, K, bits, _ptr(q, _u8p)), "unpack")
     return q
 
 
-def dequant(qweight, scales, zeros, N: int, K: int, group: int = 128) -> np.ndarray:
+def dequant(qweight, scales, zeros, N: int, K: int, group: int = 128, bits: int = 4) -> np.ndarray:
     qweight = np.ascontiguousarray(qweight, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
-    assert qweight.size == N * (K // 2) and scales.size == N * (K // group) == zeros.size
+    assert qweight.size == code_bytes(N, K, bits) and scales.size == N * (K // group) == zeros.size
     w = np.empty((N, K), dtype=np.float64)
     _check(lib().qi4o_dequant(_ptr(qweight, _u8p), _ptr(scales, _u16p), _ptr(zeros, _u8p),
-                              N, K, group, _ptr(w, _dp)), "dequant")
+                              N, K, group, bits, _ptr(w, _dp)), "dequant")
     return w
 
 
 # ---- the linear layer ------------------------------------------------------
 
 def linear(x64: np.ndarray, qweight, scales, zeros, N: int, K: int, group: int = 128,
-           threads: int | None = None):
+           threads: int | None = None, bits: int = 4):
     """Return (y, S): y = x . dequant(W)^T and S = sum_k |x*w|, both [T][N] float64."""
     x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(-1, K)
     T = x64.shape[0]
     qweight = np.ascontiguousarray(qweight, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
-    assert qweight.size == N * (K // 2) and scales.size == N * (K // group) == zeros.size
+    assert qweight.size == code_bytes(N, K, bits) and scales.size == N * (K // group) == zeros.size
     y = np.empty((T, N), dtype=np.float64)
     S = np.empty((T, N), dtype=np.float64)
     _check(lib().qi4o_linear(_ptr(x64, _dp), T, K, _ptr(qweight, _u8p), _ptr(scales, _u16p),
-                             _ptr(zeros, _u8p), N, group, _ptr(y, _dp), _ptr(S, _dp),
+                             _ptr(zeros, _u8p), N, group, bits, _ptr(y, _dp), _ptr(S, _dp),
                              threads or default_threads()), "linear")
     return y, S
 
 
 def gate_up_silu(x64: np.ndarray, qweight, scales, zeros, I: int, K: int, group: int = 128,
-                 c: float = C_TOL, threads: int | None = None):
+                 c: float = C_TOL, threads: int | None = None, bits: int = 4):
     """Return (h, tol_h) for the fused SiLU(gate)*up of a [gate; up] weight (2I x K)."""
     x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(-1, K)
     T = x64.shape[0]
@@ -173,7 +182,7 @@ def gate_up_silu(x64: np.ndarray, qweight, scales, zeros, I: int, K: int, group:
                                    _ptr(np.ascontiguousarray(qweight, dtype=np.uint8), _u8p),
                                    _ptr(np.ascontiguousarray(scales, dtype=np.uint16), _u16p),
                                    _ptr(np.ascontiguousarray(zeros, dtype=np.uint8), _u8p),
-                                   I, group, c, _ptr(h, _dp), _ptr(tol, _dp),
+                                   I, group, bits, c, _ptr(h, _dp), _ptr(tol, _dp),
                                    threads or default_threads()), "gate_up_silu")
     return h, tol
 
@@ -218,11 +227,12 @@ def sort_tokens(ids: np.ndarray, E: int):
 
 def moe(x64: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: dict, shared: dict | None,
         H: int, I: int, E: int, group: int = 128, c: float = C_TOL, eps_p: float = EPS_P,
-        threads: int | None = None):
+        threads: int | None = None, bits: int = 4):
     """Return (out, tol), both [T][H] float64.
 
     ``experts`` holds canonical arrays for all E routed experts:
-    gu_q [E][2I][H/2], gu_s/gu_z [E][2I][H/G], dn_q [E][H][I/2], dn_s/dn_z [E][H][I/G].
+    gu_q [E][2I][H/2], gu_s/gu_z [E][2I][H/G], dn_q [E][H][I/2], dn_s/dn_z [E][H][I/G]
+    (with ``bits`` 8 the code arrays are [E][2I][H] and [E][H][I]).
     ``shared`` holds the same keys for one expert (no leading E), or None.
     ``group`` 0 means one group per row of each matrix (H for gate/up, I for down).
     """
@@ -249,20 +259,21 @@ def moe(x64: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: dict, shared: 
     _check(lib().qi4o_moe(_ptr(x64, _dp), T, H, I, E, k, _ptr(ids, _i32p), _ptr(p, _dp),
                           *[_ptr(a, t) for a, t in zip(ea, types)],
                           *[_ptr(a, t) for a, t in zip(sa, types)],
-                          group, c, eps_p, _ptr(out, _dp), _ptr(tol, _dp),
+                          group, bits, c, eps_p, _ptr(out, _dp), _ptr(tol, _dp),
                           threads or default_threads()), "moe")
     return out, tol
 
 
 # ---- reference quantizer -------------------------------------------------
 
-def quantize(w: np.ndarray, group: int = 128):
-    """Min/max asymmetric quantizer; returns canonical (qweight, scales, zeros)."""
+def quantize(w: np.ndarray, group: int = 128, bits: int = 4):
+    """Min/max asymmetric quantizer with 2^bits - 1 levels; returns canonical
+    (qweight, scales, zeros)."""
     w = np.ascontiguousarray(w, dtype=np.float64)
     N, K = w.shape
-    qw = np.empty((N, K // 2), dtype=np.uint8)
+    qw = np.empty((N, K if bits == 8 else K // 2), dtype=np.uint8)
     s = np.empty((N, K // group), dtype=np.uint16)
     z = np.empty((N, K // group), dtype=np.uint8)
-    _check(lib().qi4o_quantize(_ptr(w, _dp), N, K, group, _ptr(qw, _u8p), _ptr(s, _u16p),
+    _check(lib().qi4o_quantize(_ptr(w, _dp), N, K, group, bits, _ptr(qw, _u8p), _ptr(s, _u16p),
                                _ptr(z, _u8p)), "quantize")
     return qw, s, z

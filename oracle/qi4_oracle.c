@@ -28,7 +28,12 @@
  *   R10 combine weights = softmax over the selected k logits only;
  *   R11 the shared expert is added with weight 1;
  *   R12 token permutation: expert ascending, then token ascending;
- *   R19 reference quantizer: asymmetric min/max with 0 inside the range.
+ *   R19 reference quantizer: asymmetric min/max with 0 inside the range;
+ *   R29 8-bit weights (--quant-bit 8): one byte per code, q in 0..255, same
+ *       groups, binary16 scale and a zero in 0..255, w = scale * (q - zero).
+ *
+ * `bits` (4 or 8) selects the code width everywhere: 4-bit codes pack two per
+ * byte (qweight [N][K/2]), 8-bit codes one per byte (qweight [N][K]).
  *
  * Everything is computed in double.  Scales arrive as IEEE binary16 bit
  * patterns and are decoded exactly.  Activations arrive already widened to
@@ -41,7 +46,7 @@
 #include <string.h>
 #include <math.h>
 
-#define ORACLE_ABI 1
+#define ORACLE_ABI 2
 int qi4o_abi_version(void) { return ORACLE_ABI; }
 
 /* ---- IEEE binary16 <-> double ----------------------------------------- */
@@ -98,50 +103,59 @@ uint16_t qi4o_f64_to_f16(double v)
 
 /* ---- the quantized format ----------------------------------------------- */
 
-/* [P3 s3.1] one 4-bit code per weight; two codes per byte (R1: even k low). */
-static inline int q_at(const uint8_t *qweight, int64_t K, int64_t n, int64_t k)
+/* [P3 s3.1] one 4-bit code per weight, two codes per byte (R1: even k low);
+   [P3 s4.2] with 8-bit quantization one code per byte (R29). */
+static inline int q_at(const uint8_t *qweight, int64_t K, int64_t n, int64_t k, int bits)
 {
+    if (bits == 8) return qweight[n * K + k];
     uint8_t b = qweight[n * (K / 2) + k / 2];
     return (k & 1) ? (b >> 4) : (b & 15);
+}
+
+/* Bytes of the codes of one N x K matrix. */
+static inline int64_t code_bytes(int64_t N, int64_t K, int bits)
+{
+    return bits == 8 ? N * K : N * (K / 2);
 }
 
 /* Dequantize one weight: w = scale * (q - zero) with the scale and zero of the
    group that holds k ([P3 s3.1]; formula R5). */
 static inline double w_at(const uint8_t *qweight, const uint16_t *scales,
-                          const uint8_t *zeros, int64_t K, int64_t G,
+                          const uint8_t *zeros, int64_t K, int64_t G, int bits,
                           int64_t n, int64_t k)
 {
     int64_t ng = K / G;
     int64_t g = k / G;
     double s = qi4o_f16_to_f64(scales[n * ng + g]);
     int z = zeros[n * ng + g];
-    int q = q_at(qweight, K, n, k);
+    int q = q_at(qweight, K, n, k, bits);
     return s * (double)(q - z);
 }
 
-static int bad_shape(int64_t N, int64_t K, int64_t G)
+static int bad_shape(int64_t N, int64_t K, int64_t G, int bits)
 {
-    return N < 0 || K <= 0 || G <= 0 || (K % G) != 0 || (K % 2) != 0;
+    return N < 0 || K <= 0 || G <= 0 || (K % G) != 0 || (K % 2) != 0 ||
+           (bits != 4 && bits != 8);
 }
 
-/* Unpack the codes: q[n][k] in 0..15. */
-int qi4o_unpack(const uint8_t *qweight, int64_t N, int64_t K, uint8_t *q)
+/* Unpack the codes: q[n][k] in 0..15 (4-bit) or 0..255 (8-bit). */
+int qi4o_unpack(const uint8_t *qweight, int64_t N, int64_t K, int bits, uint8_t *q)
 {
-    if (N < 0 || K <= 0 || (K % 2)) return -2;
+    if (N < 0 || K <= 0 || (K % 2) || (bits != 4 && bits != 8)) return -2;
     for (int64_t n = 0; n < N; n++)
         for (int64_t k = 0; k < K; k++)
-            q[n * K + k] = (uint8_t)q_at(qweight, K, n, k);
+            q[n * K + k] = (uint8_t)q_at(qweight, K, n, k, bits);
     return 0;
 }
 
 /* Dequantize the whole matrix: w[n][k] = scale(n, k/G) * (q(n,k) - zero(n, k/G)). */
 int qi4o_dequant(const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
-                 int64_t N, int64_t K, int64_t G, double *w)
+                 int64_t N, int64_t K, int64_t G, int bits, double *w)
 {
-    if (bad_shape(N, K, G)) return -2;
+    if (bad_shape(N, K, G, bits)) return -2;
     for (int64_t n = 0; n < N; n++)
         for (int64_t k = 0; k < K; k++)
-            w[n * K + k] = w_at(qweight, scales, zeros, K, G, n, k);
+            w[n * K + k] = w_at(qweight, scales, zeros, K, G, bits, n, k);
     return 0;
 }
 
@@ -152,9 +166,9 @@ int qi4o_dequant(const uint8_t *qweight, const uint16_t *scales, const uint8_t *
    is the magnitude the tolerance is stated against.  S may be NULL. */
 int qi4o_linear(const double *x, int64_t T, int64_t K,
                 const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
-                int64_t N, int64_t G, double *y, double *S, int threads)
+                int64_t N, int64_t G, int bits, double *y, double *S, int threads)
 {
-    if (bad_shape(N, K, G) || T < 0) return -2;
+    if (bad_shape(N, K, G, bits) || T < 0) return -2;
     if (threads < 1) threads = 1;
     for (int64_t t = 0; t < T; t++) {
         const double *xt = x + t * K;
@@ -162,7 +176,7 @@ int qi4o_linear(const double *x, int64_t T, int64_t K,
         for (int64_t n = 0; n < N; n++) {
             double acc = 0.0, mag = 0.0;
             for (int64_t k = 0; k < K; k++) {
-                double p = xt[k] * w_at(qweight, scales, zeros, K, G, n, k);
+                double p = xt[k] * w_at(qweight, scales, zeros, K, G, bits, n, k);
                 acc += p;
                 mag += fabs(p);
             }
@@ -191,14 +205,15 @@ static double silu_prime(double v)
    tol_h = c * (|SiLU'(g)| * |u| * S_g + |SiLU(g)| * S_u). */
 int qi4o_gate_up_silu(const double *x, int64_t T, int64_t K,
                       const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
-                      int64_t I, int64_t G, double c, double *h, double *tol_h, int threads)
+                      int64_t I, int64_t G, int bits, double c, double *h, double *tol_h,
+                      int threads)
 {
     int64_t N = 2 * I;
-    if (bad_shape(N, K, G) || T < 0) return -2;
+    if (bad_shape(N, K, G, bits) || T < 0) return -2;
     double *gu = (double *)malloc(sizeof(double) * (size_t)(T * N + 1));
     double *S = (double *)malloc(sizeof(double) * (size_t)(T * N + 1));
     if (!gu || !S) { free(gu); free(S); return -9; }
-    int rc = qi4o_linear(x, T, K, qweight, scales, zeros, N, G, gu, S, threads);
+    int rc = qi4o_linear(x, T, K, qweight, scales, zeros, N, G, bits, gu, S, threads);
     if (rc == 0) {
         for (int64_t t = 0; t < T; t++)
             for (int64_t i = 0; i < I; i++) {
@@ -279,17 +294,17 @@ int qi4o_sort(const int32_t *ids, int64_t T, int k, int64_t E,
    A (may be NULL) receives the first-order tolerance of y:
    A[n] = sum_i |W_d[n][i]| * (c*|h_i| + tol_h[i]). */
 static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t Ggu, int64_t Gdn,
-                      double c, const uint8_t *gq, const uint16_t *gs, const uint8_t *gz,
+                      int bits, double c, const uint8_t *gq, const uint16_t *gs, const uint8_t *gz,
                       const uint8_t *dq, const uint16_t *ds, const uint8_t *dz,
                       double *y, double *A, double *h, double *tol_h, int threads)
 {
-    int rc = qi4o_gate_up_silu(xt, 1, H, gq, gs, gz, I, Ggu, c, h, tol_h, threads);
+    int rc = qi4o_gate_up_silu(xt, 1, H, gq, gs, gz, I, Ggu, bits, c, h, tol_h, threads);
     if (rc) return rc;
 #pragma omp parallel for num_threads(threads) schedule(static)
     for (int64_t n = 0; n < H; n++) {
         double acc = 0.0, a = 0.0;
         for (int64_t i = 0; i < I; i++) {
-            double w = w_at(dq, ds, dz, I, Gdn, n, i);
+            double w = w_at(dq, ds, dz, I, Gdn, bits, n, i);
             acc += w * h[i];
             a += fabs(w) * (c * fabs(h[i]) + tol_h[i]);
         }
@@ -315,13 +330,15 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
              const uint8_t *dn_q, const uint16_t *dn_s, const uint8_t *dn_z,
              const uint8_t *sh_gu_q, const uint16_t *sh_gu_s, const uint8_t *sh_gu_z,
              const uint8_t *sh_dn_q, const uint16_t *sh_dn_s, const uint8_t *sh_dn_z,
-             int64_t G, double c, double eps_p, double *out, double *tol, int threads)
+             int64_t G, int bits, double c, double eps_p, double *out, double *tol,
+             int threads)
 {
     const int64_t Ggu = G ? G : H, Gdn = G ? G : I;
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || G < 0 || H % Ggu || I % Gdn) return -2;
+    if (bits != 4 && bits != 8) return -2;
     if (threads < 1) threads = 1;
-    const int64_t gu_qb = 2 * I * (H / 2), gu_mb = 2 * I * (H / Ggu);
-    const int64_t dn_qb = H * (I / 2), dn_mb = H * (I / Gdn);
+    const int64_t gu_qb = code_bytes(2 * I, H, bits), gu_mb = 2 * I * (H / Ggu);
+    const int64_t dn_qb = code_bytes(H, I, bits), dn_mb = H * (I / Gdn);
     double *y = (double *)malloc(sizeof(double) * (size_t)H);
     double *A = (double *)malloc(sizeof(double) * (size_t)H);
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
@@ -337,7 +354,7 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
             int64_t e = ids[t * k + j];
             if (e < 0 || e >= E) { rc = -3; break; }
             double pj = p[t * k + j];
-            rc = expert_ffn(xt, H, I, Ggu, Gdn, c,
+            rc = expert_ffn(xt, H, I, Ggu, Gdn, bits, c,
                             gu_q + e * gu_qb, gu_s + e * gu_mb, gu_z + e * gu_mb,
                             dn_q + e * dn_qb, dn_s + e * dn_mb, dn_z + e * dn_mb,
                             y, A, h, th, threads);
@@ -347,7 +364,7 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
             }
         }
         if (rc == 0 && sh_gu_q) {
-            rc = expert_ffn(xt, H, I, Ggu, Gdn, c, sh_gu_q, sh_gu_s, sh_gu_z,
+            rc = expert_ffn(xt, H, I, Ggu, Gdn, bits, c, sh_gu_q, sh_gu_s, sh_gu_z,
                             sh_dn_q, sh_dn_s, sh_dn_z, y, A, h, th, threads);
             for (int64_t n = 0; n < H; n++) {
                 ot[n] += y[n];
@@ -361,17 +378,19 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
 
 /* ---- reference quantizer (round-trip checks only) ----------------------- */
 
-/* Asymmetric min/max quantizer per group (R19): lo = min(min w, 0),
-   hi = max(max w, 0), scale = fp16(hi - lo)/15 (1 if that is 0),
-   zero = clamp(rint(-lo/scale), 0, 15), q = clamp(rint(w/scale) + zero, 0, 15);
-   rint rounds half to even.  The scale is rounded to binary16 before it is used,
-   so dequantizing with the stored scale reproduces what q was chosen against. */
-int qi4o_quantize(const double *w, int64_t N, int64_t K, int64_t G,
+/* Asymmetric min/max quantizer per group (R19) with L = 2^bits - 1 levels
+   (15 or 255): lo = min(min w, 0), hi = max(max w, 0), scale = fp16((hi - lo)/L)
+   (1 if that is 0), zero = clamp(rint(-lo/scale), 0, L),
+   q = clamp(rint(w/scale) + zero, 0, L); rint rounds half to even.  The scale is
+   rounded to binary16 before it is used, so dequantizing with the stored scale
+   reproduces what q was chosen against. */
+int qi4o_quantize(const double *w, int64_t N, int64_t K, int64_t G, int bits,
                   uint8_t *qweight, uint16_t *scales, uint8_t *zeros)
 {
-    if (bad_shape(N, K, G)) return -2;
+    if (bad_shape(N, K, G, bits)) return -2;
+    const double L = (double)((1 << bits) - 1);
     int64_t ng = K / G;
-    memset(qweight, 0, (size_t)(N * (K / 2)));
+    memset(qweight, 0, (size_t)code_bytes(N, K, bits));
     for (int64_t n = 0; n < N; n++)
         for (int64_t g = 0; g < ng; g++) {
             const double *wg = w + n * K + g * G;
@@ -380,22 +399,23 @@ int qi4o_quantize(const double *w, int64_t N, int64_t K, int64_t G,
                 if (wg[i] < lo) lo = wg[i];
                 if (wg[i] > hi) hi = wg[i];
             }
-            uint16_t sb = qi4o_f64_to_f16((hi - lo) / 15.0);
+            uint16_t sb = qi4o_f64_to_f16((hi - lo) / L);
             double s = qi4o_f16_to_f64(sb);
             if (s == 0.0) { sb = 0x3c00; s = 1.0; }
             double zf = nearbyint(-lo / s);
             if (zf < 0) zf = 0;
-            if (zf > 15) zf = 15;
+            if (zf > L) zf = L;
             int z = (int)zf;
             scales[n * ng + g] = sb;
             zeros[n * ng + g] = (uint8_t)z;
             for (int64_t i = 0; i < G; i++) {
                 double qf = nearbyint(wg[i] / s) + z;
                 if (qf < 0) qf = 0;
-                if (qf > 15) qf = 15;
+                if (qf > L) qf = L;
                 int64_t k = g * G + i;
                 uint8_t q = (uint8_t)qf;
-                qweight[n * (K / 2) + k / 2] |= (k & 1) ? (uint8_t)(q << 4) : q;
+                if (bits == 8) qweight[n * K + k] = q;
+                else qweight[n * (K / 2) + k / 2] |= (k & 1) ? (uint8_t)(q << 4) : q;
             }
         }
     return 0;

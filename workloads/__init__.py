@@ -43,18 +43,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # ---- weights ------------------------------------------------------------------
 
 def weights(seed: int, tag: int, N: int, K: int, scale_lo: float, scale_hi: float,
-            group: int = GROUP) -> dict:
+            group: int = GROUP, bits: int = 4) -> dict:
     """q uniform in 0..15 (so a packed byte is uniform in 0..255), zero uniform in
     0..15, scale uniform in [scale_lo, scale_hi] rounded to binary16.  group 0 means
-    one group per row."""
+    one group per row.  bits 8: q and zero uniform in 0..255, one code per byte
+    (qweight [N][K])."""
     group = group or K
-    assert K % group == 0 and K % 2 == 0
+    assert K % group == 0 and K % 2 == 0 and bits in (4, 8)
     G = K // group
-    qw = rng(seed, tag, _T_QW).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    qw = rng(seed, tag, _T_QW).integers(0, 256, size=(N, K if bits == 8 else K // 2),
+                                        dtype=np.uint8)
     sc = rng(seed, tag, _T_SC).uniform(scale_lo, scale_hi, size=(N, G)).astype(np.float16)
-    zr = rng(seed, tag, _T_ZR).integers(0, 16, size=(N, G), dtype=np.uint8)
+    zr = rng(seed, tag, _T_ZR).integers(0, 1 << bits, size=(N, G), dtype=np.uint8)
     return {"qweight": qw, "scales": sc.view(np.uint16), "zeros": zr, "N": N, "K": K,
-            "group": group}
+            "group": group, "bits": bits}
 
 
 def activations(seed: int, tag: int, T: int, K: int, dtype: str = "bf16",
@@ -121,13 +123,13 @@ def logits_zipf(seed: int, tag: int, T: int, E: int, s: float = 1.1) -> np.ndarr
 # ---- MoE expert weights ------------------------------------------------------------
 
 def moe_experts(seed: int, layer: int, E: int, H: int, I: int, scale_lo: float,
-                scale_hi: float, group: int = GROUP) -> dict:
+                scale_hi: float, group: int = GROUP, bits: int = 4) -> dict:
     """Canonical weights of E routed experts stacked on a leading axis:
     gu_* is the [gate; up] matrix (2I x H), dn_* the down matrix (H x I)."""
-    gu = [weights(seed, 1000 * layer + 10 * e + 1 + 100000, 2 * I, H, scale_lo, scale_hi, group)
-          for e in range(E)]
-    dn = [weights(seed, 1000 * layer + 10 * e + 2 + 100000, H, I, scale_lo, scale_hi, group)
-          for e in range(E)]
+    gu = [weights(seed, 1000 * layer + 10 * e + 1 + 100000, 2 * I, H, scale_lo, scale_hi, group,
+                  bits) for e in range(E)]
+    dn = [weights(seed, 1000 * layer + 10 * e + 2 + 100000, H, I, scale_lo, scale_hi, group,
+                  bits) for e in range(E)]
     return {"gu_q": np.stack([w["qweight"] for w in gu]),
             "gu_s": np.stack([w["scales"] for w in gu]),
             "gu_z": np.stack([w["zeros"] for w in gu]),
@@ -137,9 +139,9 @@ def moe_experts(seed: int, layer: int, E: int, H: int, I: int, scale_lo: float,
 
 
 def moe_shared(seed: int, layer: int, H: int, I: int, scale_lo: float, scale_hi: float,
-               group: int = GROUP) -> dict:
-    gu = weights(seed, 1000 * layer + 7, 2 * I, H, scale_lo, scale_hi, group)
-    dn = weights(seed, 1000 * layer + 8, H, I, scale_lo, scale_hi, group)
+               group: int = GROUP, bits: int = 4) -> dict:
+    gu = weights(seed, 1000 * layer + 7, 2 * I, H, scale_lo, scale_hi, group, bits)
+    dn = weights(seed, 1000 * layer + 8, H, I, scale_lo, scale_hi, group, bits)
     return {"gu_q": gu["qweight"], "gu_s": gu["scales"], "gu_z": gu["zeros"],
             "dn_q": dn["qweight"], "dn_s": dn["scales"], "dn_z": dn["zeros"]}
 
@@ -165,7 +167,8 @@ MOE_PREFILL = dict(name="moe_deepseekv3_shape_prefill", seed=4, H=7168, I=2048, 
 
 # ---- algorithmic bytes (measurement bookkeeping, not the method) ------------------
 
-def packed_weight_bytes(n_weights: int, group: int = GROUP) -> float:
-    """Algorithmic bytes of int4 weights: per group of `group` weights, group/2 bytes
-    of codes, a 2-byte binary16 scale and a 4-bit zero point."""
-    return n_weights * (group / 2 + 2 + 0.5) / group
+def packed_weight_bytes(n_weights: int, group: int = GROUP, bits: int = 4) -> float:
+    """Algorithmic bytes of quantized weights: per group of `group` weights,
+    group * bits / 8 bytes of codes, a 2-byte binary16 scale and a bits-wide zero
+    point."""
+    return n_weights * (group * bits / 8 + 2 + bits / 8) / group
