@@ -124,7 +124,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-linear measurements")
     ap.add_argument("--no-groups", action="store_true",
-                    help="skip the decode step with other group sizes")
+                    help="skip the decode step with other group sizes and 8-bit codes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     return ap.parse_args()
@@ -145,22 +145,23 @@ def build_layer(c, layer, q, torch):
     return mw
 
 
-def build_layer_quantized(c, layer, q, torch, group):
-    """A layer of the same shape for another group size: seeded random bf16
-    weights (N(0, 0.02^2)) quantized on the GPU with that group size and packed,
-    expert by expert (fast to build; the values feed timing only)."""
+def build_layer_quantized(c, layer, q, torch, group, fmt=0):
+    """A layer of the same shape for another group size or code width (fmt
+    QI4_INT8: 8-bit codes): seeded random bf16 weights (N(0, 0.02^2)) quantized
+    on the GPU and packed, expert by expert (fast to build; the values feed
+    timing only)."""
     E, H, I = c["E"], c["H"], c["I"]
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(1000 * c["seed"] + 17 * layer + group)
+    gen.manual_seed(1000 * c["seed"] + 17 * layer + group + 7 * fmt)
 
     def one(N, K, flags, out):
         w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32)
         w = w.mul_(0.02).to(torch.bfloat16)
-        qw, sc, zr = q.quantize(w, group=group)
-        return q.pack(qw, sc, zr, N, K, flags, out=out, group=group)
+        qw, sc, zr = q.quantize(w, group=group, flags=fmt)
+        return q.pack(qw, sc, zr, N, K, flags | fmt, out=out, group=group)
 
-    gu_b = q.packed_bytes(2 * I, H, q.QI4_PACK_GATEUP, group)
-    dn_b = q.packed_bytes(H, I, 0, group)
+    gu_b = q.packed_bytes(2 * I, H, q.QI4_PACK_GATEUP | fmt, group)
+    dn_b = q.packed_bytes(H, I, fmt, group)
     w_gu = torch.empty(E * gu_b, dtype=torch.uint8, device="cuda")
     w_dn = torch.empty(E * dn_b, dtype=torch.uint8, device="cuda")
     for e in range(E):
@@ -169,17 +170,19 @@ def build_layer_quantized(c, layer, q, torch, group):
     sgu = one(2 * I, H, q.QI4_PACK_GATEUP, None)
     sdn = one(H, I, 0, None)
     torch.cuda.synchronize()
-    return q.MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn, group)
+    return q.MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn, group, fmt)
 
 
 def run_group_variants(q, torch, c, T, steps, warmup):
-    """The decode step at batch T with 64-wide groups and with one group per row
-    (group_size 0), two layers each, as the main measurement."""
+    """The decode step at batch T with 64-wide groups, with one group per row
+    (group_size 0) and with 8-bit codes (groups of 128), two layers each, as the
+    main measurement."""
     res = []
-    for group in (64, 0):
-        layers = [build_layer_quantized(c, l, q, torch, group) for l in range(2)]
+    for group, fmt in ((64, 0), (0, 0), (128, q.QI4_INT8)):
+        layers = [build_layer_quantized(c, l, q, torch, group, fmt) for l in range(2)]
         r = run_batch(q, torch, layers, c, T, steps, warmup)
-        res.append({"group_size": group, "T": T, "tokens_per_s": r["tokens_per_s"],
+        res.append({"group_size": group, "bits": 8 if fmt else 4, "T": T,
+                    "tokens_per_s": r["tokens_per_s"],
                     "ms_per_step": r["ms_per_step"], "gate_up_GBps": r["gate_up_GBps"],
                     "gate_up_hbm_frac": r["gate_up_GBps"] / HBM_PEAK_GBPS,
                     "down_GBps": r["down_GBps"], "step_GBps": r["step_GBps"]})
@@ -282,9 +285,9 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     H, I = c["H"], c["I"]
     # bytes per weight of the gate/up (groups along H) and down (along I) matrices
-    g = layers[0].group
-    pw_gu = workloads.packed_weight_bytes(1, g or H)
-    pw_dn = workloads.packed_weight_bytes(1, g or I)
+    g, bits = layers[0].group, 8 if layers[0].flags & q.QI4_INT8 else 4
+    pw_gu = workloads.packed_weight_bytes(1, g or H, bits)
+    pw_dn = workloads.packed_weight_bytes(1, g or I, bits)
     gu_w, dn_w = 2 * I * H, H * I
     # algorithmic bytes per step: weights of the touched experts + the shared one,
     # activations in, outputs out, router logits in
@@ -428,10 +431,32 @@ def run_dense(q, torch, reps=20):
                           "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
                           "tokens_per_s": T / t})
         del pw
+    # the same shapes with 8-bit codes (groups of 128), quantized on the GPU
+    # from N(0, 0.02^2) bf16 weights
+    sweep8 = []
+    per_w8 = workloads.packed_weight_bytes(1, 128, 8)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    for i, (K, N) in enumerate(c2["shapes"]):
+        wf = (torch.randn((N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+        qw, sc, zr = q.quantize(wf, flags=q.QI4_INT8)
+        pw = q.pack(qw, sc, zr, N, K, q.QI4_INT8)
+        del wf, qw, sc, zr
+        for T in (1, 8, 32):
+            x = q_bf16(torch, workloads.activations(c2["seed"], 20 + 10 * i + T, T, K, "bf16",
+                                                    c2["x_scale"]))
+            y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+            t = timed(lambda: q.qlinear(x, pw, N, flags=q.QI4_INT8, out=y))
+            b = N * K * per_w8 + T * K * 2 + T * N * 2
+            sweep8.append({"K": K, "N": N, "T": T, "us": t * 1e6,
+                           "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
+                           "tokens_per_s": T / t})
+        del pw
     del rd
     torch.cuda.empty_cache()
     return {"protocol": "1 GiB read before each rep (outside the events); median of "
-                        f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep}
+                        f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep,
+            "skinny_sweep_int8": sweep8}
 
 
 def run_router(q, torch, reps=20):
@@ -571,7 +596,7 @@ def main():
     groups = None
     if not args.no_groups:
         groups = run_group_variants(q, torch, c, args.T, max(10, args.steps // 2), args.warmup)
-        log(f"group sizes: {json.dumps(groups)}")
+        log(f"format variants: {json.dumps(groups)}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -610,7 +635,7 @@ def main():
         "prefill": prefill,
         "dense": dense,
         "quantize": quant,
-        "group_sizes": groups,
+        "format_variants": groups,
         "router": router,
         "cpu_baseline": cpu,
     }

@@ -1,6 +1,6 @@
 """Python binding of libqi4: int4 group-quantized linear layer (groups of 128 by
-default; 64, multiples of 128, or one group per row) and routed MoE expert FFN
-for AMD MI355X (gfx950).
+default; 64, multiples of 128, or one group per row; 8-bit codes with the flag
+QI4_INT8) and routed MoE expert FFN for AMD MI355X (gfx950).
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``libqi4.so`` (sources in ``csrc/``, C ABI in ``include/qi4.h``);
@@ -20,7 +20,12 @@ QI4_OK = 0
 QI4_F32, QI4_BF16 = 0, 1
 QI4_EPI_NONE, QI4_EPI_SILU_MUL = 0, 1
 QI4_PACK_GATEUP = 1
+QI4_INT8 = 2         # format flag: 8-bit codes (qweight [N][K], zeros 0..255)
 GROUP = 128          # default group size; 0 means one group per row
+
+
+def _code_shape(N: int, K: int, flags: int):
+    return (N, K) if flags & QI4_INT8 else (N, K // 2)
 
 
 def _ngroups(K: int, group: int) -> int:
@@ -67,8 +72,10 @@ def lib():
             "qi4_unpack": (ci, [vp, i64, i64, ci, ci, vp, vp, vp, vp]),
             "qi4_dequant_f32": (ci, [vp, i64, i64, ci, ci, vp, vp]),
             "qi4_quantize": (ci, [vp, ci, i64, i64, ci, vp, vp, vp, vp]),
+            "qi4_quantize_int8": (ci, [vp, ci, i64, i64, ci, vp, vp, vp, vp]),
             "qlinear_int4_g128": (ci, [vp, ci, i64, i64, vp, i64, ci, vp, ci, ci, vp]),
             "qlinear_int4": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
+            "qlinear_int8": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
             "moe_route_sort": (ci, [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]),
             "moe_router_topk": (ci, [vp, i64, i64, vp, i64, i32, vp, vp, vp, vp]),
@@ -88,7 +95,8 @@ def lib():
 
 # declared in include/qi4.h, in header order
 EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pack", "qi4_unpack",
-            "qi4_dequant_f32", "qi4_quantize", "qlinear_int4_g128", "qlinear_int4", "moe_route_topk",
+            "qi4_dequant_f32", "qi4_quantize", "qi4_quantize_int8", "qlinear_int4_g128",
+            "qlinear_int4", "qlinear_int8", "moe_route_topk",
             "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4"]
@@ -132,8 +140,9 @@ def packed_bytes(N: int, K: int, flags: int = 0, group: int = GROUP) -> int:
 
 def pack(qweight, scales, zeros, N: int, K: int, flags: int = 0, out=None, stream=None,
          group: int = GROUP):
-    """Canonical (uint8 [N][K/2], int16/uint16 binary16 bits [N][K/group], uint8
-    [N][K/group]) device tensors -> packed uint8 device tensor."""
+    """Canonical (uint8 [N][K/2] -- [N][K] with QI4_INT8 --, int16/uint16 binary16
+    bits [N][K/group], uint8 [N][K/group]) device tensors -> packed uint8 device
+    tensor."""
     import torch
     _need(qweight, torch.uint8, "qweight")
     _need(zeros, torch.uint8, "zeros")
@@ -149,7 +158,7 @@ def unpack(packed, N: int, K: int, flags: int = 0, stream=None, group: int = GRO
     import torch
     dev = packed.device
     ng = _ngroups(K, group)
-    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    qw = torch.empty(_code_shape(N, K, flags), dtype=torch.uint8, device=dev)
     sc = torch.empty((N, ng), dtype=torch.int16, device=dev)
     zr = torch.empty((N, ng), dtype=torch.uint8, device=dev)
     _check(lib().qi4_unpack(_ptr(packed), N, K, group, flags, _ptr(qw), _ptr(sc), _ptr(zr),
@@ -165,9 +174,10 @@ def dequant_f32(packed, N: int, K: int, flags: int = 0, stream=None, group: int 
     return w
 
 
-def quantize(w, stream=None, group: int = GROUP):
+def quantize(w, stream=None, group: int = GROUP, flags: int = 0):
     """float32 or bfloat16 device weights [N][K] -> canonical (qweight uint8 [N][K/2],
-    scales int16 binary16 bits [N][K/group], zeros uint8 [N][K/group]) device tensors."""
+    scales int16 binary16 bits [N][K/group], zeros uint8 [N][K/group]) device tensors;
+    8-bit codes (qweight [N][K]) with flags QI4_INT8."""
     import torch
     if w.dtype == torch.float32:
         wd = QI4_F32
@@ -179,11 +189,12 @@ def quantize(w, stream=None, group: int = GROUP):
         raise ValueError("w must be a contiguous 2-D device tensor")
     N, K = w.shape
     ng = _ngroups(K, group)
-    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    qw = torch.empty(_code_shape(N, K, flags), dtype=torch.uint8, device=w.device)
     sc = torch.empty((N, ng), dtype=torch.int16, device=w.device)
     zr = torch.empty((N, ng), dtype=torch.uint8, device=w.device)
-    _check(lib().qi4_quantize(_ptr(w), wd, N, K, group, _ptr(qw), _ptr(sc), _ptr(zr),
-                              _stream(stream)), "qi4_quantize")
+    fn = lib().qi4_quantize_int8 if flags & QI4_INT8 else lib().qi4_quantize
+    _check(fn(_ptr(w), wd, N, K, group, _ptr(qw), _ptr(sc), _ptr(zr), _stream(stream)),
+           "qi4_quantize")
     return qw, sc, zr
 
 
@@ -207,7 +218,10 @@ def qlinear(x, packed, N: int, flags: int = 0, out_dtype=None, epilogue: int = Q
     if out is None:
         out = torch.empty((T, n_out), dtype=out_dtype, device=x.device)
     yd = QI4_BF16 if out.dtype == torch.bfloat16 else QI4_F32
-    if group == GROUP:
+    if flags & QI4_INT8:
+        _check(lib().qlinear_int8(_ptr(x), xd, T, K, _ptr(packed), N, group, flags, _ptr(out), yd,
+                                  epilogue, _stream(stream)), "qlinear_int8")
+    elif group == GROUP:
         _check(lib().qlinear_int4_g128(_ptr(x), xd, T, K, _ptr(packed), N, flags, _ptr(out), yd,
                                        epilogue, _stream(stream)), "qlinear_int4_g128")
     else:
@@ -230,14 +244,15 @@ class MoeWeights:
     shared_gate_up: object = None
     shared_down: object = None
     group: int = GROUP
+    flags: int = 0       # QI4_INT8: 8-bit experts
 
     def desc(self, top_k: int) -> _MoeDesc:
         return _MoeDesc(self.E, self.H, self.I, top_k, self.group,
-                        1 if self.shared_gate_up is not None else 0, 0)
+                        1 if self.shared_gate_up is not None else 0, self.flags)
 
 
 def pack_moe(experts: dict, shared: dict | None, E: int, H: int, I: int, device="cuda",
-             stream=None, group: int = GROUP) -> MoeWeights:
+             stream=None, group: int = GROUP, flags: int = 0) -> MoeWeights:
     """Pack canonical expert weights (numpy or torch; see workloads.moe_experts) expert by
     expert on the device."""
     import numpy as np
@@ -250,24 +265,25 @@ def pack_moe(experts: dict, shared: dict | None, E: int, H: int, I: int, device=
             a = torch.from_numpy(np.ascontiguousarray(a))
         return a.to(device)
 
-    gu_b, dn_b = packed_bytes(2 * I, H, QI4_PACK_GATEUP, group), packed_bytes(H, I, 0, group)
+    fg, fd = QI4_PACK_GATEUP | flags, flags
+    gu_b, dn_b = packed_bytes(2 * I, H, fg, group), packed_bytes(H, I, fd, group)
     w_gu = torch.empty(E * gu_b, dtype=torch.uint8, device=device)
     w_dn = torch.empty(E * dn_b, dtype=torch.uint8, device=device)
     for e in range(E):
         pack(dev(experts["gu_q"][e], torch.uint8), dev(experts["gu_s"][e], torch.int16),
-             dev(experts["gu_z"][e], torch.uint8), 2 * I, H, QI4_PACK_GATEUP,
+             dev(experts["gu_z"][e], torch.uint8), 2 * I, H, fg,
              out=w_gu[e * gu_b:(e + 1) * gu_b], stream=stream, group=group)
         pack(dev(experts["dn_q"][e], torch.uint8), dev(experts["dn_s"][e], torch.int16),
-             dev(experts["dn_z"][e], torch.uint8), H, I, 0,
+             dev(experts["dn_z"][e], torch.uint8), H, I, fd,
              out=w_dn[e * dn_b:(e + 1) * dn_b], stream=stream, group=group)
     sgu = sdn = None
     if shared is not None:
         sgu = pack(dev(shared["gu_q"], torch.uint8), dev(shared["gu_s"], torch.int16),
-                   dev(shared["gu_z"], torch.uint8), 2 * I, H, QI4_PACK_GATEUP, stream=stream,
+                   dev(shared["gu_z"], torch.uint8), 2 * I, H, fg, stream=stream,
                    group=group)
         sdn = pack(dev(shared["dn_q"], torch.uint8), dev(shared["dn_s"], torch.int16),
-                   dev(shared["dn_z"], torch.uint8), H, I, 0, stream=stream, group=group)
-    return MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn, group)
+                   dev(shared["dn_z"], torch.uint8), H, I, fd, stream=stream, group=group)
+    return MoeWeights(E, H, I, w_gu, w_dn, sgu, sdn, group, flags)
 
 
 def moe_route_topk(logits, top_k: int, stream=None):

@@ -40,7 +40,7 @@ const char *qi4_status_string(int status) {
         case QI4_ERR_NULL: return "a required pointer is NULL";
         case QI4_ERR_SHAPE: return "a size is out of range, K is not a multiple of 128, or a pointer is misaligned";
         case QI4_ERR_DTYPE: return "unknown dtype or epilogue";
-        case QI4_ERR_GROUP: return "group_size must be 128";
+        case QI4_ERR_GROUP: return "group_size must be 0, 64 or a multiple of 128";
         case QI4_ERR_WORKSPACE: return "workspace too small";
         case QI4_ERR_ALIAS: return "an output overlaps an input";
         case QI4_ERR_UNSUPPORTED: return "unsupported device (needs gfx950) or flag combination";
@@ -52,7 +52,8 @@ const char *qi4_status_string(int status) {
 int64_t qi4_packed_bytes(int64_t N, int64_t K, int group_size, int flags) {
     int rc = qi4::check_matrix(N, K, group_size, flags);
     if (rc != QI4_OK) return rc;
-    return qi4::PackedLayout(N, K, flags, (int)qi4::effective_group(group_size, K)).bytes;
+    return qi4::PackedLayout(N, qi4::packed_k(K, flags), flags,
+                             (int)qi4::effective_group(group_size, K)).bytes;
 }
 
 }  // extern "C"

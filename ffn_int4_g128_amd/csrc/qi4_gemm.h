@@ -16,7 +16,7 @@ struct GemmArgs {
     const uint8_t *w;          // dense matrix, or routed expert 0 (each matrix < 2^31 bytes)
     int64_t w_stride;          // bytes between routed experts
     const uint8_t *w_shared;   // shared expert (moe) or nullptr
-    int64_t N, K;              // rows and reduction length of each matrix
+    int64_t N, K;              // rows and packed reduction length of each matrix
     int flags;                 // QI4_PACK_GATEUP or 0
     int group_size;            // quantization group size (64, or a multiple of 128)
     // activations
@@ -25,6 +25,8 @@ struct GemmArgs {
     int64_t a_bytes;           // bytes of the whole A buffer (< 2^31)
     int a_f32;                 // float32 rows, split into 4 bf16 terms in registers
     int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
+    int a_shift;               // weight block b reads activation block b >> a_shift
+                               // (1: an 8-bit matrix, two 4-bit planes per block)
     // problems
     int moe;                   // 0: one dense problem with T slots
     int64_t T;                 // tokens

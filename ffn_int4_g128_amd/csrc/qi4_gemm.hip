@@ -166,13 +166,14 @@ qgemm_kernel(const GemmArgs args) {
         int lr = 0, li = 0;
         uint32_t loc = 0, los = 0, loz = 0, loa = 0;
         int lnt = 0;   // tiles of block lr inside the matrix (0..NB)
+        const int ash = args.a_shift;
         auto rebase = [&]() {
             const int64_t tile = tile0 + (int64_t)lr * NB;
             const uint32_t slot = (uint32_t)(tile & (kQuadTiles - 1));
             loc = (uint32_t)((tile * G + gb) * kTileGroupBytes);
             los = (uint32_t)L.scale_rec(tile, gb) + 2u * slot;
             loz = (uint32_t)L.zero_rec(tile, gb) + (slot >> 1);
-            loa = (uint32_t)gb * 128u * ES;
+            loa = (uint32_t)(gb >> ash) * 128u * ES;
             lnt = lr < nblk ? (int)(nt - tile < NB ? nt - tile : NB) : 0;
         };
         auto load_w = [&](Stage<NB, MT, AF32, H> &q) {
@@ -200,7 +201,9 @@ qgemm_kernel(const GemmArgs args) {
             loc += kTileGroupBytes;
             los += H * kQuadScaleBytes;
             loz += H * kQuadZeroBytes;
-            loa += 128u * ES;
+            // the next block reads the next activation block (8-bit planes:
+            // after each odd block)
+            if (((gb + li) | (ash ^ 1)) & 1) loa += 128u * ES;
             if (++li == ngp) {
                 li = 0;
                 ++lr;
@@ -514,15 +517,18 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
 
 using namespace qi4;
 
-extern "C" int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
-                            const void *packed_w, int64_t N, int group_size, int flags, void *y,
-                            int y_dtype, int epilogue, void *stream) {
+namespace {
+
+// qlinear_int4 / qlinear_int8 (flags holds QI4_INT8 for the latter).
+int qlinear_impl(const void *x, int x_dtype, int64_t T, int64_t K, const void *packed_w,
+                 int64_t N, int group_size, int flags, void *y, int y_dtype, int epilogue,
+                 void *stream) {
     int rc = check_matrix(N, K, group_size, flags);
     if (rc) return rc;
     if (x_dtype != QI4_F32 && x_dtype != QI4_BF16) return QI4_ERR_DTYPE;
     if (y_dtype != QI4_F32 && y_dtype != QI4_BF16) return QI4_ERR_DTYPE;
     if (epilogue != QI4_EPI_NONE && epilogue != QI4_EPI_SILU_MUL) return QI4_ERR_DTYPE;
-    if (epilogue == QI4_EPI_SILU_MUL && flags != QI4_PACK_GATEUP) return QI4_ERR_UNSUPPORTED;
+    if (epilogue == QI4_EPI_SILU_MUL && !(flags & QI4_PACK_GATEUP)) return QI4_ERR_UNSUPPORTED;
     if (T < 0 || T > (int64_t(1) << 31)) return QI4_ERR_SHAPE;
     if (T == 0) return QI4_OK;
     if (!x || !packed_w || !y) return QI4_ERR_NULL;
@@ -531,7 +537,8 @@ extern "C" int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
     const int64_t xb = T * K * (x_dtype == QI4_F32 ? 4 : 2);
     const int64_t yb = T * n_out * (y_dtype == QI4_F32 ? 4 : 2);
     const int gs = (int)effective_group(group_size, K);
-    const int64_t wb = PackedLayout(N, K, flags, gs).bytes;
+    const int64_t Kp = packed_k(K, flags);
+    const int64_t wb = PackedLayout(N, Kp, flags, gs).bytes;
     if (wb >= (int64_t(1) << 31) || xb >= (int64_t(1) << 31)) return QI4_ERR_SHAPE;
     if (overlaps(y, yb, x, xb) || overlaps(y, yb, packed_w, wb)) return QI4_ERR_ALIAS;
     if ((rc = check_device())) return rc;
@@ -539,11 +546,12 @@ extern "C" int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
     GemmArgs a = {};
     a.w = static_cast<const uint8_t *>(packed_w);
     a.N = N;
-    a.K = K;
+    a.K = Kp;
     a.flags = flags;
     a.group_size = gs;
     a.a = x;
     a.lda = K;
+    a.a_shift = (flags & QI4_INT8) ? 1 : 0;
     a.a_bytes = xb;
     a.a_f32 = x_dtype == QI4_F32;
     a.P = a.a_f32 ? 4 : 1;
@@ -555,6 +563,23 @@ extern "C" int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
     a.epi = epilogue;
     a.n_out = n_out;
     return launch_qgemm(a, 1, T, as_stream(stream));
+}
+
+}  // namespace
+
+extern "C" int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
+                            const void *packed_w, int64_t N, int group_size, int flags, void *y,
+                            int y_dtype, int epilogue, void *stream) {
+    if (flags & QI4_INT8) return QI4_ERR_UNSUPPORTED;   // an 8-bit matrix: qlinear_int8
+    return qlinear_impl(x, x_dtype, T, K, packed_w, N, group_size, flags, y, y_dtype, epilogue,
+                        stream);
+}
+
+extern "C" int qlinear_int8(const void *x, int x_dtype, int64_t T, int64_t K,
+                            const void *packed_w, int64_t N, int group_size, int flags, void *y,
+                            int y_dtype, int epilogue, void *stream) {
+    return qlinear_impl(x, x_dtype, T, K, packed_w, N, group_size, flags | QI4_INT8, y, y_dtype,
+                        epilogue, stream);
 }
 
 extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,

@@ -22,16 +22,25 @@ inline bool aligned(const void *p, uintptr_t a) {
 // The group size a call means: 0 stands for one group per row (K).
 inline int64_t effective_group(int group_size, int64_t K) { return group_size == 0 ? K : group_size; }
 
+// K of the packed 4-bit matrix that holds an N x K matrix: an 8-bit matrix is
+// stored as two 4-bit planes, one 128-wide block of each per block of K.
+inline int64_t packed_k(int64_t K, int flags) { return (flags & QI4_INT8) ? 2 * K : K; }
+
+// Bytes of the canonical codes of an N x K matrix.
+inline int64_t code_bytes(int64_t N, int64_t K, int flags) {
+    return (flags & QI4_INT8) ? N * K : N * K / 2;
+}
+
 // Shape checks common to every call on a packed matrix.
 inline int check_matrix(int64_t N, int64_t K, int group_size, int flags) {
     // 64, or a multiple of 128 dividing K (0 or K: one group per row)
     const int64_t gs = effective_group(group_size, K);
     if (group_size < 0 || (gs != 64 && (gs < 128 || gs % 128 != 0))) return QI4_ERR_GROUP;
     if (gs > 64 && K % gs != 0) return QI4_ERR_SHAPE;
-    if (flags & ~QI4_PACK_GATEUP) return QI4_ERR_UNSUPPORTED;
+    if (flags & ~(QI4_PACK_GATEUP | QI4_INT8)) return QI4_ERR_UNSUPPORTED;
     if (N < 1 || K < 128 || (K % 128) != 0) return QI4_ERR_SHAPE;
     if ((flags & QI4_PACK_GATEUP) && (N % 2) != 0) return QI4_ERR_SHAPE;
-    if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return QI4_ERR_SHAPE;
+    if (N > (int64_t(1) << 31) || K > (int64_t(1) << 30)) return QI4_ERR_SHAPE;
     return QI4_OK;
 }
 

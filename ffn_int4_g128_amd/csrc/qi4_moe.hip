@@ -444,7 +444,8 @@ int check_desc(const qi4_moe_desc *d) {
     if (d->group_size < 0 || (d->group_size != 0 && d->group_size != 64 &&
                               (d->group_size < 128 || d->group_size % 128 != 0)))
         return QI4_ERR_GROUP;
-    if (d->flags != 0 || (d->has_shared != 0 && d->has_shared != 1)) return QI4_ERR_UNSUPPORTED;
+    if ((d->flags & ~QI4_INT8) || (d->has_shared != 0 && d->has_shared != 1))
+        return QI4_ERR_UNSUPPORTED;
     if (d->num_experts < 1 || d->num_experts > kMaxExperts) return QI4_ERR_SHAPE;
     if (d->hidden < 128 || d->hidden % 128 || d->inter < 128 || d->inter % 128) return QI4_ERR_SHAPE;
     if (d->hidden > (1 << 20) || d->inter > (1 << 20)) return QI4_ERR_SHAPE;
@@ -459,11 +460,17 @@ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 // Group sizes of the gate/up (groups along hidden) and down (along inter) matrices.
 inline int gs_gate_up(const qi4_moe_desc *d) { return (int)effective_group(d->group_size, d->hidden); }
 inline int gs_down(const qi4_moe_desc *d) { return (int)effective_group(d->group_size, d->inter); }
+// Pack flags of the two matrices (QI4_INT8: 8-bit experts, stored as two 4-bit
+// planes of twice the width, each block reading one activation block).
+inline int gate_up_flags(const qi4_moe_desc *d) { return QI4_PACK_GATEUP | (d->flags & QI4_INT8); }
+inline int down_flags(const qi4_moe_desc *d) { return d->flags & QI4_INT8; }
+inline int a_shift_of(const qi4_moe_desc *d) { return (d->flags & QI4_INT8) ? 1 : 0; }
 inline int64_t gate_up_bytes(const qi4_moe_desc *d) {
-    return PackedLayout(2 * d->inter, d->hidden, QI4_PACK_GATEUP, gs_gate_up(d)).bytes;
+    return PackedLayout(2 * d->inter, packed_k(d->hidden, d->flags), gate_up_flags(d),
+                        gs_gate_up(d)).bytes;
 }
 inline int64_t down_bytes(const qi4_moe_desc *d) {
-    return PackedLayout(d->hidden, d->inter, 0, gs_down(d)).bytes;
+    return PackedLayout(d->hidden, packed_k(d->inter, d->flags), down_flags(d), gs_down(d)).bytes;
 }
 
 // Batches of at least this many tokens run the prefill GEMM (fp16 MFMA on
@@ -565,11 +572,12 @@ GemmArgs gate_up_args(const qi4_moe_desc *d, const void *x, int64_t T, const int
     a.w_stride = gate_up_bytes(d);
     a.w_shared = static_cast<const uint8_t *>(sh_gu);
     a.N = 2 * d->inter;
-    a.K = d->hidden;
-    a.flags = QI4_PACK_GATEUP;
+    a.K = packed_k(d->hidden, d->flags);
+    a.flags = gate_up_flags(d);
     a.group_size = gs_gate_up(d);
     a.a = x;
     a.lda = d->hidden;
+    a.a_shift = a_shift_of(d);
     a.a_bytes = T * d->hidden * 2;
     a.a_f32 = 0;
     a.P = 1;
@@ -596,11 +604,12 @@ GemmArgs down_args(const qi4_moe_desc *d, const void *h, int64_t T, const int32_
     a.w_stride = down_bytes(d);
     a.w_shared = static_cast<const uint8_t *>(sh_dn);
     a.N = d->hidden;
-    a.K = d->inter;
-    a.flags = 0;
+    a.K = packed_k(d->inter, d->flags);
+    a.flags = down_flags(d);
     a.group_size = gs_down(d);
     a.a = h;
     a.lda = d->inter;
+    a.a_shift = a_shift_of(d);
     a.a_bytes = (T * d->top_k + (d->has_shared ? T : 0)) * 2 * d->inter * 2;
     a.a_f32 = 0;
     a.P = 2;
@@ -634,8 +643,9 @@ PrefillArgs prefill_args(const qi4_moe_desc *d, int64_t T, bool gate_up, const i
     a.w = static_cast<const uint8_t *>(w);
     a.w_shared = static_cast<const uint8_t *>(w_shared);
     a.N = gate_up ? 2 * I : H;
-    a.K = gate_up ? H : I;
-    a.flags = gate_up ? QI4_PACK_GATEUP : 0;
+    a.K = packed_k(gate_up ? H : I, d->flags);
+    a.a_shift = a_shift_of(d);
+    a.flags = gate_up ? gate_up_flags(d) : down_flags(d);
     a.group_size = gate_up ? gs_gate_up(d) : gs_down(d);
     a.w_stride = PackedLayout(a.N, a.K, a.flags, a.group_size).bytes;
     a.a16 = a16;

@@ -12,10 +12,13 @@ struct PrefillArgs {
     const uint8_t *w;          // routed expert 0 (packed), stride w_stride
     int64_t w_stride;
     const uint8_t *w_shared;   // shared expert or nullptr
-    int64_t N, K;
+    int64_t N, K;              // rows and packed reduction length of each matrix
+    int a_shift;               // weight block b reads activation block b >> a_shift
+                               // (1: 8-bit matrices, two 4-bit planes per block)
     int flags;
     int group_size;            // quantization group size (64, or a multiple of 128)
-    const uint16_t *a16;       // fp16 activation rows [a_rows][K]; value = a16 * 2^a_exp[row]
+    const uint16_t *a16;       // fp16 activation rows [a_rows][K >> a_shift];
+                               // value = a16 * 2^a_exp[row]
     int64_t a_rows;
     const int32_t *a_exp;
     int gather_tokens;         // rows of a16 are tokens (gate/up) or slots (down)

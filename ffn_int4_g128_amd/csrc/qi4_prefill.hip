@@ -264,7 +264,8 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     const int64_t nt = L.nt, G = L.G;
     const int64_t tile0 = bx * (kRowsPerWG / 16) + wave * NBW;
     const __amdgpu_buffer_rsrc_t wr = rsrc(w, (uint32_t)L.bytes);
-    const __amdgpu_buffer_rsrc_t ar = rsrc(args.a16, (uint32_t)(args.a_rows * args.K * 2));
+    const int64_t KA = args.K >> args.a_shift;   // activation row length
+    const __amdgpu_buffer_rsrc_t ar = rsrc(args.a16, (uint32_t)(args.a_rows * KA * 2));
 
     // Weight offsets: the lane part is the same for every tile and group; the
     // tile and group part is wave-uniform and goes in soffset (scalar registers).
@@ -295,7 +296,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
         const bool ok = slot < n;
         const int64_t slot_c = ok ? slot : 0;
         const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
-        aoff[h] = ok ? (uint32_t)((src * args.K + 8 * cchunk) * 2) : kOob;
+        aoff[h] = ok ? (uint32_t)((src * KA + 8 * cchunk) * 2) : kOob;
     }
     // MFMA operand lane (row r16, chunk j) finds its chunk at this LDS offset
     const uint32_t rdoff = 16u * (uint32_t)(4 * r16 + ((j + rot(r16)) & 3));
@@ -308,7 +309,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     // wave exactly kReqs requests.
     auto fill = [&](int stage, int g) {
         const bool in = g < G;
-        const uint32_t so = in ? (uint32_t)g * 256u : 0u;
+        const uint32_t so = in ? (uint32_t)(g >> args.a_shift) * 256u : 0u;
         uint8_t *buf = lds + stage * SH::kStageBytes;
 #pragma unroll
         for (int i = 0; i < FPW; ++i) {

@@ -1,15 +1,18 @@
-// Load-time int4 quantizer: float32 or bf16 weights -> canonical codes, scales
-// and zero points for groups of 64, 128, 256, ... (up to a whole row) along K.
+// Load-time quantizer: float32 or bf16 weights -> canonical 4-bit (or 8-bit)
+// codes, scales and zero points for groups of 64, 128, 256, ... (up to a whole
+// row) along K.
 //
 // The fastllm README (gittoolsai.com), section "model export", notes that
 // loading a model with an int4 dtype quantizes it online at every load, which is
 // slow.  This kernel does that step on the GPU.  Per group of weights w of one
 // row (asymmetric min/max, with 0 always inside the range):
 //   lo = min(0, min w), hi = max(0, max w)
-//   scale = (hi - lo) / 15 rounded to binary16 (nearest, ties to even);
+//   scale = (hi - lo) / L rounded to binary16 (nearest, ties to even);
 //           1.0 when that rounds to 0
-//   zero  = clamp(rint(-lo / scale), 0, 15)
-//   q     = clamp(rint(w / scale) + zero, 0, 15)         rint: half to even
+//   zero  = clamp(rint(-lo / scale), 0, L)
+//   q     = clamp(rint(w / scale) + zero, 0, L)          rint: half to even
+// with L = 15 levels for 4-bit codes and 255 for 8-bit ones (the --quant-bit 8
+// option of the FastLLM page, section 4.2).
 // The decisions are those of the formula evaluated in binary64 (float32 and
 // bf16 widen exactly; divisions are correctly rounded); the per-weight quotient
 // is formed in float32 and checked against the rounding boundaries (below).
@@ -44,7 +47,11 @@ __device__ inline uint32_t f64_to_f16_bits_rne(double v) {
     return ((uint32_t)be << 10) | ((uint32_t)m - 1024u);
 }
 
-__device__ inline double clamp15(double v) { return v < 0.0 ? 0.0 : (v > 15.0 ? 15.0 : v); }
+template <int BITS>
+__device__ inline double clampL(double v) {
+    constexpr double L = (double)((1 << BITS) - 1);
+    return v < 0.0 ? 0.0 : (v > L ? L : v);
+}
 
 // Eight consecutive weights (float32 or bf16) at element offset off.
 template <bool F32>
@@ -66,33 +73,46 @@ __device__ inline void load8(const void *w, int64_t off, float (&v)[8]) {
 }
 
 // Scale (binary16 bits and value) and zero of a group with range [lo, hi].
+template <int BITS>
 __device__ inline void scale_zero(float lo, float hi, uint32_t &sb, double &s, double &z) {
-    sb = f64_to_f16_bits_rne(((double)hi - (double)lo) / 15.0);
+    sb = f64_to_f16_bits_rne(((double)hi - (double)lo) / (double)((1 << BITS) - 1));
     s = (double)__builtin_bit_cast(_Float16, (uint16_t)sb);
     if (s == 0.0) {
         sb = 0x3C00u;   // binary16 1.0
         s = 1.0;
     }
-    z = clamp15(rint(-(double)lo / s));
+    z = clampL<BITS>(rint(-(double)lo / s));
 }
 
-// Codes of eight weights, even k in the low nibble.  rint(w / s) is formed
-// from x = w * (1/s) in float32 (w and s are exact in float32; two roundings:
-// |x - w/s| <= |x| 2^-23 <= 4e-6 for |x| <= 32).  Away from the half-integers
-// x rounds like w/s; within 1e-4 of one the decision is taken on the binary64
-// quotient.  Beyond 32 both clamp alike (z <= 15).
-__device__ inline uint32_t codes8(const float (&v)[8], double s, double z) {
+// Codes of eight weights: 4-bit codes packed even k in the low nibble (low 32
+// bits), 8-bit codes one per byte.  rint(w / s) is formed from x = w * (1/s)
+// in float32 (w and s are exact in float32; two roundings: |x - w/s| <= |x| 2^-23,
+// at most 6.2e-5 for |x| <= 2 (L + 1)).  Away from the half-integers x rounds
+// like w/s; within 1e-4 of one the decision is taken on the binary64 quotient.
+// Beyond 2 (L + 1) both clamp alike (z <= L).
+template <int BITS>
+__device__ inline uint64_t codes8(const float (&v)[8], double s, double z) {
+    constexpr float XMAX = 2.0f * (1 << BITS);
     const float rs = 1.0f / (float)s;
-    uint32_t codes = 0;
+    uint64_t codes = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = v[e] * rs;
         const float r = rintf(x);
-        const double qf = (fabsf(x) > 32.0f || fabsf(fabsf(x - r) - 0.5f) > 1e-4f)
+        const double qf = (fabsf(x) > XMAX || fabsf(fabsf(x - r) - 0.5f) > 1e-4f)
                               ? (double)r : rint((double)v[e] / s);
-        codes |= (uint32_t)clamp15(qf + z) << (4 * e);
+        codes |= (uint64_t)clampL<BITS>(qf + z) << (BITS * e);
     }
     return codes;
+}
+
+// Store the codes of eight weights starting at weight k of row n.
+template <int BITS>
+__device__ inline void store_codes(uint8_t *qweight, int64_t n, int64_t K, int64_t k, uint64_t c) {
+    if constexpr (BITS == 8)
+        *reinterpret_cast<uint2 *>(qweight + n * K + k) = make_uint2((uint32_t)c, (uint32_t)(c >> 32));
+    else
+        *reinterpret_cast<uint32_t *>(qweight + n * (K / 2) + k / 2) = (uint32_t)c;
 }
 
 // Groups of 8 * SEG weights (SEG = 8, 16, 32 or 64 lanes): each SEG-lane
@@ -100,7 +120,7 @@ __device__ inline uint32_t codes8(const float (&v)[8], double s, double z) {
 // weights 8j .. 8j+7 (one 16- or 32-byte load, one 4-byte code store).  A wave
 // takes kQuantPasses * (64 / SEG) consecutive groups (row-major order), with
 // every pass's loads issued before any is used.
-template <bool F32, int SEG>
+template <bool F32, int SEG, int BITS>
 __global__ void __launch_bounds__(kQuantWaves * 64)
 quantize_kernel(const void *__restrict__ w, int64_t N, int64_t K, uint8_t *__restrict__ qweight,
                 uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros) {
@@ -138,8 +158,8 @@ quantize_kernel(const void *__restrict__ w, int64_t N, int64_t K, uint8_t *__res
         const int64_t n = grp / G, g = grp - n * G;
         uint32_t sb;
         double sd, z;
-        scale_zero(lo, hi, sb, sd, z);
-        *reinterpret_cast<uint32_t *>(qweight + n * (K / 2) + g * (GS / 2) + 4 * j) = codes8(v[p], sd, z);
+        scale_zero<BITS>(lo, hi, sb, sd, z);
+        store_codes<BITS>(qweight, n, K, g * GS + 8 * j, codes8<BITS>(v[p], sd, z));
         if (j == 0) {
             scales[n * G + g] = (uint16_t)sb;
             zeros[n * G + g] = (uint8_t)z;
@@ -150,7 +170,7 @@ quantize_kernel(const void *__restrict__ w, int64_t N, int64_t K, uint8_t *__res
 // Other group sizes (multiples of 128 other than 128, 256, 512, up to a whole
 // row): one wave per group, two passes over it (range, then codes), 512
 // weights per wave step.
-template <bool F32>
+template <bool F32, int BITS>
 __global__ void __launch_bounds__(kQuantWaves * 64)
 quantize_long_kernel(const void *__restrict__ w, int64_t N, int64_t K, int64_t GS,
                      uint8_t *__restrict__ qweight, uint16_t *__restrict__ scales,
@@ -177,11 +197,11 @@ quantize_long_kernel(const void *__restrict__ w, int64_t N, int64_t K, int64_t G
     }
     uint32_t sb;
     double sd, z;
-    scale_zero(lo, hi, sb, sd, z);
+    scale_zero<BITS>(lo, hi, sb, sd, z);
     for (int64_t i = 8 * lane; i < GS; i += 512) {
         float v[8];
         load8<F32>(w, base + i, v);
-        *reinterpret_cast<uint32_t *>(qweight + n * (K / 2) + (g * GS + i) / 2) = codes8(v, sd, z);
+        store_codes<BITS>(qweight, n, K, g * GS + i, codes8<BITS>(v, sd, z));
     }
     if (lane == 0) {
         scales[n * G + g] = (uint16_t)sb;
@@ -189,7 +209,7 @@ quantize_long_kernel(const void *__restrict__ w, int64_t N, int64_t K, int64_t G
     }
 }
 
-template <bool F32>
+template <bool F32, int BITS>
 int launch_quantize(const void *w, int64_t N, int64_t K, int64_t gs, uint8_t *qweight,
                     uint16_t *scales, uint8_t *zeros, hipStream_t st) {
     const int64_t groups = N * (K / gs);
@@ -197,7 +217,7 @@ int launch_quantize(const void *w, int64_t N, int64_t K, int64_t gs, uint8_t *qw
     if (gs != 64 && gs != 128 && gs != 256 && gs != 512) {
         const int64_t blocks = ceil_div(groups, kQuantWaves);
         if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
-        quantize_long_kernel<F32><<<(unsigned)blocks, threads, 0, st>>>(w, N, K, gs, qweight, scales, zeros);
+        quantize_long_kernel<F32, BITS><<<(unsigned)blocks, threads, 0, st>>>(w, N, K, gs, qweight, scales, zeros);
         return launch_status();
     }
     const int seg = (int)(gs / 8);
@@ -205,10 +225,10 @@ int launch_quantize(const void *w, int64_t N, int64_t K, int64_t gs, uint8_t *qw
     if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
     const dim3 g((unsigned)blocks);
     switch (seg) {
-    case 8: quantize_kernel<F32, 8><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
-    case 16: quantize_kernel<F32, 16><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
-    case 32: quantize_kernel<F32, 32><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
-    case 64: quantize_kernel<F32, 64><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 8: quantize_kernel<F32, 8, BITS><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 16: quantize_kernel<F32, 16, BITS><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 32: quantize_kernel<F32, 32, BITS><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
+    case 64: quantize_kernel<F32, 64, BITS><<<g, threads, 0, st>>>(w, N, K, qweight, scales, zeros); break;
     default: return QI4_ERR_GROUP;
     }
     return launch_status();
@@ -219,22 +239,40 @@ int launch_quantize(const void *w, int64_t N, int64_t K, int64_t gs, uint8_t *qw
 
 using namespace qi4;
 
-extern "C" int qi4_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
-                            uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream) {
+namespace {
+
+template <int BITS>
+int quantize_entry(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
+                   uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream) {
     if (!w || !qweight || !scales || !zeros) return QI4_ERR_NULL;
     if (w_dtype != QI4_F32 && w_dtype != QI4_BF16) return QI4_ERR_DTYPE;
-    int rc = check_matrix(N, K, group_size, 0);
+    const int flags = BITS == 8 ? QI4_INT8 : 0;
+    int rc = check_matrix(N, K, group_size, flags);
     if (rc) return rc;
     const int64_t gs = effective_group(group_size, K);
     const int64_t es = w_dtype == QI4_F32 ? 4 : 2;
-    if (!aligned(w, 16) || !aligned(qweight, 4) || !aligned(scales, 2)) return QI4_ERR_SHAPE;
-    const int64_t G = K / gs;
-    if (overlaps(w, N * K * es, qweight, N * K / 2) || overlaps(w, N * K * es, scales, N * G * 2) ||
-        overlaps(w, N * K * es, zeros, N * G) || overlaps(qweight, N * K / 2, scales, N * G * 2) ||
-        overlaps(qweight, N * K / 2, zeros, N * G) || overlaps(scales, N * G * 2, zeros, N * G))
+    if (!aligned(w, 16) || !aligned(qweight, BITS == 8 ? 8 : 4) || !aligned(scales, 2))
+        return QI4_ERR_SHAPE;
+    const int64_t G = K / gs, cb = code_bytes(N, K, flags);
+    if (overlaps(w, N * K * es, qweight, cb) || overlaps(w, N * K * es, scales, N * G * 2) ||
+        overlaps(w, N * K * es, zeros, N * G) || overlaps(qweight, cb, scales, N * G * 2) ||
+        overlaps(qweight, cb, zeros, N * G) || overlaps(scales, N * G * 2, zeros, N * G))
         return QI4_ERR_ALIAS;
     if ((rc = check_device())) return rc;
     hipStream_t st = as_stream(stream);
-    return w_dtype == QI4_F32 ? launch_quantize<true>(w, N, K, gs, qweight, scales, zeros, st)
-                              : launch_quantize<false>(w, N, K, gs, qweight, scales, zeros, st);
+    return w_dtype == QI4_F32 ? launch_quantize<true, BITS>(w, N, K, gs, qweight, scales, zeros, st)
+                              : launch_quantize<false, BITS>(w, N, K, gs, qweight, scales, zeros, st);
+}
+
+}  // namespace
+
+extern "C" int qi4_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
+                            uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream) {
+    return quantize_entry<4>(w, w_dtype, N, K, group_size, qweight, scales, zeros, stream);
+}
+
+extern "C" int qi4_quantize_int8(const void *w, int w_dtype, int64_t N, int64_t K,
+                                 int group_size, uint8_t *qweight, uint16_t *scales,
+                                 uint8_t *zeros, void *stream) {
+    return quantize_entry<8>(w, w_dtype, N, K, group_size, qweight, scales, zeros, stream);
 }

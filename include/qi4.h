@@ -11,11 +11,12 @@
  *    runs "read 4-bit weight -> dequantize -> multiply" with no extra pass;
  *    section 2.3: the matrix multiply is a core operator below the model layer.
  *    Section 4.2 "model conversion and format": the group size defaults to 128;
- *    64 and 256 are allowed.
+ *    64 and 256 are allowed; codes are 4 or 8 bits wide (--quant-bit).
  *  - fastllm README (gittoolsai.com), "other parameters": --moe_experts sets
  *    how many routed experts each token uses; --cuda_se runs the shared expert
  *    on the GPU.  "Inference precision": int4g is the grouped int4 type, int4
- *    the plain one (read here as one scale and zero per row: group_size 0).
+ *    the plain one (read here as one scale and zero per row: group_size 0),
+ *    int8 the 8-bit type (flag QI4_INT8 below).
  *  - FastLLM notes (wmrh.cn), part 1: a MoE layer holds many experts but each
  *    token activates only a few of them.
  * Dequantization is w = scale * (q - zero).  Expert FFN is
@@ -50,6 +51,10 @@
  *    scales  uint16 [N][K/Gs]   IEEE binary16 bit patterns
  *    zeros   uint8  [N][K/Gs]   zero point, 0..15
  * A [gate; up] matrix of an FFN has N = 2*I rows: rows [0, I) gate, [I, 2I) up.
+ * With the flag QI4_INT8 (8-bit codes) the canonical format is instead
+ *    qweight uint8  [N][K]      one code 0..255 per byte
+ *    zeros   uint8  [N][K/Gs]   zero point, 0..255
+ * (scales as above), and w = scale * (q - zero) likewise.
  *
  * Packed (device) format, produced by qi4_pack: rows are cut into 16-row tiles
  * (with QI4_PACK_GATEUP, tile 2m holds gate rows 16m.. and tile 2m+1 the up rows
@@ -66,8 +71,15 @@
  * Lane 16*j + r of a tile/block holds row r's codes for k in
  * 128*g + 32*s + 8*j + [0, 8) in its dword s (s = 0..3), so one 16-byte load per
  * lane brings a wave exactly one block of 16 rows.  Missing rows (N not a multiple
- * of 16) are packed as zeros.  The layout is private to this library: only
- * qi4_pack writes it and only the calls below read it.
+ * of 16) are packed as zeros.  An 8-bit matrix (QI4_INT8) is stored as the
+ * 4-bit packed matrix of width 2K whose block 2b holds the high nibbles q >> 4
+ * of block b with zero z >> 4 and scale binary16(16 * scale), and block 2b + 1
+ * the low nibbles q & 15 with zero z & 15 and the scale itself:
+ * 16 s (q_hi - z_hi) + s (q_lo - z_lo) = s (q - z) exactly, and every GEMM
+ * reads the activations of block b for both.  16 * scale must be a binary16,
+ * so 8-bit scales need |scale| <= 4094 (a larger one gives an infinite product).
+ * The layout is private to this library: only qi4_pack writes it and only the
+ * calls below read it.
  */
 #ifndef QI4_H
 #define QI4_H
@@ -94,7 +106,8 @@ enum {
 
 enum { QI4_F32 = 0, QI4_BF16 = 1 };          /* activation / output element types */
 enum { QI4_EPI_NONE = 0, QI4_EPI_SILU_MUL = 1 };
-enum { QI4_PACK_GATEUP = 1 };                 /* pack flag: pair gate/up tiles      */
+enum { QI4_PACK_GATEUP = 1,                  /* pack flag: pair gate/up tiles      */
+       QI4_INT8 = 2 };                        /* format flag: 8-bit codes           */
 
 /* ABI version of the loaded library (QI4_ABI_VERSION). */
 int qi4_abi_version(void);
@@ -113,14 +126,14 @@ int64_t qi4_packed_bytes(int64_t N, int64_t K, int group_size, int flags);
 int qi4_pack(const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
              int64_t N, int64_t K, int group_size, int flags, void *packed, void *stream);
 
-/* Packed -> canonical; the exact inverse of qi4_pack (zero values beyond 15
-   cannot occur). */
+/* Packed -> canonical; the exact inverse of qi4_pack (4-bit zero values beyond
+   15 cannot occur). */
 int qi4_unpack(const void *packed, int64_t N, int64_t K, int group_size, int flags,
                uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream);
 
 /* Dequantize a packed matrix to float32 w [N][K] in canonical row order:
    w = float(scale) * (q - zero).  Exact (the product of a binary16 scale and an
-   integer in [-15, 15] is representable in binary32). */
+   integer in [-255, 255] is representable in binary32). */
 int qi4_dequant_f32(const void *packed, int64_t N, int64_t K, int group_size, int flags,
                     float *w, void *stream);
 
@@ -138,6 +151,12 @@ int qi4_dequant_f32(const void *packed, int64_t N, int64_t K, int group_size, in
  * Outputs must not overlap w or each other (QI4_ERR_ALIAS). */
 int qi4_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
                  uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream);
+
+/* The same quantizer with 8-bit codes (the --quant-bit 8 option of the FastLLM
+ * page, section 4.2): 255 in place of 15 in every formula above, output in the
+ * QI4_INT8 canonical format (qweight [N][K], 8-byte aligned; zeros 0..255). */
+int qi4_quantize_int8(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
+                      uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream);
 
 /* The linear layer: y[t][n'] = epilogue( sum_k x[t][k] * dequant(W)[n][k] ).
  *   x        [T][K] of x_dtype (QI4_BF16 or QI4_F32), row-major, contiguous
@@ -160,11 +179,18 @@ int qlinear_int4(const void *x, int x_dtype, int64_t T, int64_t K,
                  const void *packed_w, int64_t N, int group_size, int flags,
                  void *y, int y_dtype, int epilogue, void *stream);
 
+/* The same linear layer for an 8-bit matrix (packed with QI4_INT8 in flags; the
+ * flag may be given or left out here).  The fastllm README lists int8 among the
+ * weight types; the FastLLM page (section 4.2) converts with --quant-bit 8. */
+int qlinear_int8(const void *x, int x_dtype, int64_t T, int64_t K,
+                 const void *packed_w, int64_t N, int group_size, int flags,
+                 void *y, int y_dtype, int epilogue, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Routed mixture-of-experts FFN (decode and prefill).
  * Routed expert e uses packed gate/up block w_gate_up + e * qi4_packed_bytes(2I, H,
- * group_size, QI4_PACK_GATEUP) and packed down block w_down + e *
- * qi4_packed_bytes(H, I, group_size, 0).  The shared expert (has_shared != 0) has the same two shapes and is
+ * group_size, QI4_PACK_GATEUP | flags) and packed down block w_down + e *
+ * qi4_packed_bytes(H, I, group_size, flags), flags = desc.flags.  The shared expert (has_shared != 0) has the same two shapes and is
  * added with weight 1.
  * ------------------------------------------------------------------------- */
 typedef struct {
@@ -174,7 +200,7 @@ typedef struct {
     int32_t top_k;         /* routed experts per token (1..min(E, 32))           */
     int32_t group_size;    /* 64, a multiple of 128 dividing H and I, or 0      */
     int32_t has_shared;    /* 0 or 1                                            */
-    int32_t flags;         /* must be 0                                         */
+    int32_t flags;         /* 0 (4-bit experts) or QI4_INT8 (8-bit experts)      */
 } qi4_moe_desc;            /* host struct                                       */
 
 /* Router: for each token the top_k largest logits in descending order (ties to

@@ -103,6 +103,19 @@ def test_argument_errors_return_before_any_launch(q):
                              ctypes.c_void_p(0x100000 + 512), ctypes.c_void_p(0x300000),
                              ctypes.c_void_p(0x400000), None) == -6
     assert L.moe_sort_tokens(None, 4, 8, 256, p, p, p, None, None) == -1
+    # 8-bit format: packed size is that of the 4-bit matrix of twice the width;
+    # unknown flag bits; qlinear_int4 refuses an 8-bit matrix; quantizer alignment
+    assert L.qi4_packed_bytes(48, 512, 128, 2) == L.qi4_packed_bytes(48, 1024, 128, 0)
+    assert L.qi4_packed_bytes(48, 512, 64, 3) == L.qi4_packed_bytes(48, 1024, 64, 1)
+    assert L.qi4_packed_bytes(48, 512, 0, 2) > L.qi4_packed_bytes(48, 512, 0, 0)
+    assert L.qi4_packed_bytes(48, 512, 128, 4) == -7
+    assert L.qlinear_int4(p, 1, 1, 128, p, 16, 128, 2, p, 1, 0, None) == -7
+    assert L.qlinear_int8(p, 1, 1, 100, p, 16, 128, 0, p, 1, 0, None) == -2
+    assert L.qlinear_int8(None, 1, 1, 128, p, 16, 128, 0, p, 1, 0, None) == -1
+    assert L.qlinear_int8(p, 1, 0, 128, p, 16, 128, 0, p, 1, 0, None) == 0
+    assert L.qi4_quantize_int8(p, 1, 16, 128, 128, ctypes.c_void_p(0x1004), p, p, None) == -2
+    assert L.qi4_quantize_int8(None, 1, 16, 128, 128, p, p, p, None) == -1
+    assert L.qi4_pack(p, p, p, 16, 128, 128, 2, ctypes.c_void_p(0x2004), None) == -2
     # fused routing + permutation: shape, NULL, aliasing, T == 0
     assert L.moe_route_sort(p, 4, 8, 9, p, p, p, p, p, p, None) == -2
     assert L.moe_route_sort(p, 4, 2000, 8, p, p, p, p, p, p, None) == -2
@@ -134,6 +147,10 @@ def test_moe_descriptor_errors(q):
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7000, 2048, 8, 128, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(4, 7168, 2048, 8, 128, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 2, 0)), 1) == -7
+    # flags: QI4_INT8 (8-bit experts) is accepted, other bits are not
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 1, 2)), 32) > 0
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 1, 1)), 1) == -7
+    assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 1, 4)), 1) == -7
     p = ctypes.c_void_p(0x1000)
     small = ctypes.c_void_p(0x10000000)
     # workspace too small
