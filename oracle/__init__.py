@@ -32,6 +32,7 @@ _fp = ctypes.POINTER(ctypes.c_float)
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_i8p = ctypes.POINTER(ctypes.c_int8)
 _i64 = ctypes.c_int64
 
 
@@ -67,10 +68,13 @@ def lib():
                                + [_u8p, _u16p, _u8p] * 4
                                + [_i64, ci, ctypes.c_double, ctypes.c_double, _dp, _dp, ci])
         L.qi4o_quantize.argtypes = [_dp, _i64, _i64, _i64, ci, _u8p, _u16p, _u8p]
+        L.qi4o_quantize_act.argtypes = [_fp, _i64, ctypes.c_float, _i8p]
+        L.qi4o_dequant_act.argtypes = [_i8p, _i64, ctypes.c_float, _dp]
         for f in ("qi4o_unpack", "qi4o_dequant", "qi4o_linear", "qi4o_gate_up_silu",
-                  "qi4o_topk_softmax", "qi4o_sort", "qi4o_moe", "qi4o_quantize"):
+                  "qi4o_topk_softmax", "qi4o_sort", "qi4o_moe", "qi4o_quantize",
+                  "qi4o_quantize_act", "qi4o_dequant_act"):
             getattr(L, f).restype = ctypes.c_int
-        if L.qi4o_abi_version() != 2:
+        if L.qi4o_abi_version() != 3:
             raise RuntimeError("stale oracle library: rebuild it (oracle.build())")
         _lib = L
     return _lib
@@ -169,6 +173,40 @@ def linear(x64: np.ndarray, qweight, scales, zeros, N: int, K: int, group: int =
                              _ptr(zeros, _u8p), N, group, bits, _ptr(y, _dp), _ptr(S, _dp),
                              threads or default_threads()), "linear")
     return y, S
+
+
+# ---- W4A8: int8 activations with a static per-tensor scale (R30) -----------
+
+def act_reciprocal(x_scale: float) -> np.float32:
+    """r = float32(1 / s_x), the float32 quotient of the float32 scale."""
+    return np.float32(1.0) / np.float32(x_scale)
+
+
+def quantize_act(x32: np.ndarray, x_scale: float) -> np.ndarray:
+    """int8 activations a = clamp(rint(float32(x * r)), -127, 127), same shape as x32
+    (float32 values; bf16 inputs widen exactly)."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    a = np.empty(x32.shape, dtype=np.int8)
+    _check(lib().qi4o_quantize_act(_ptr(x32, _fp), x32.size, act_reciprocal(x_scale),
+                                   _ptr(a, _i8p)), "quantize_act")
+    return a
+
+
+def dequant_act(a: np.ndarray, x_scale: float) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.int8)
+    xh = np.empty(a.shape, dtype=np.float64)
+    _check(lib().qi4o_dequant_act(_ptr(a, _i8p), a.size, np.float32(x_scale), _ptr(xh, _dp)),
+           "dequant_act")
+    return xh
+
+
+def linear_w4a8(x32: np.ndarray, x_scale: float, qweight, scales, zeros, N: int, K: int,
+                group: int = 128, threads: int | None = None):
+    """W4A8 linear: (y, S, a) with y = xhat . dequant(W)^T for xhat = a * s_x, the
+    int8 activations a of quantize_act, and S = sum_k |xhat * w|."""
+    a = quantize_act(x32, x_scale)
+    y, S = linear(dequant_act(a, x_scale), qweight, scales, zeros, N, K, group, threads)
+    return y, S, a
 
 
 def gate_up_silu(x64: np.ndarray, qweight, scales, zeros, I: int, K: int, group: int = 128,

@@ -31,6 +31,12 @@
  *   R19 reference quantizer: asymmetric min/max with 0 inside the range;
  *   R29 8-bit weights (--quant-bit 8): one byte per code, q in 0..255, same
  *       groups, binary16 scale and a zero in 0..255, w = scale * (q - zero).
+ *   R30 W4A8 (FastDeploy page, x-techcon: "W4A8 static quantization"): the
+ *       activations are quantized to int8 with one static (caller-given) scale
+ *       s_x per tensor, symmetric: a = clamp(rint(x * r), -127, 127) with
+ *       r = float32(1 / s_x) and the product rounded to float32 (the decision
+ *       is taken in float32), rint half to even; the layer then computes
+ *       y = sum_k (a_k * s_x) * w_k with the weights as before.
  *
  * `bits` (4 or 8) selects the code width everywhere: 4-bit codes pack two per
  * byte (qweight [N][K/2]), 8-bit codes one per byte (qweight [N][K]).
@@ -46,7 +52,7 @@
 #include <string.h>
 #include <math.h>
 
-#define ORACLE_ABI 2
+#define ORACLE_ABI 3
 int qi4o_abi_version(void) { return ORACLE_ABI; }
 
 /* ---- IEEE binary16 <-> double ----------------------------------------- */
@@ -184,6 +190,31 @@ int qi4o_linear(const double *x, int64_t T, int64_t K,
             if (S) S[t * N + n] = mag;
         }
     }
+    return 0;
+}
+
+/* ---- W4A8: int8 activations (R30) ---------------------------------------- */
+
+/* a[t][k] = clamp(rint(x[t][k] * r), -127, 127): the product is a float32
+   product (one rounding), rint rounds half to even; NaN gives -127. */
+int qi4o_quantize_act(const float *x, int64_t n, float r, int8_t *a)
+{
+    if (n < 0) return -2;
+    for (int64_t i = 0; i < n; i++) {
+        volatile float p = x[i] * r;   /* float32 product, not widened */
+        float q = rintf(p);
+        if (!(q >= -127.0f)) q = -127.0f;
+        if (q > 127.0f) q = 127.0f;
+        a[i] = (int8_t)q;
+    }
+    return 0;
+}
+
+/* xhat[i] = a[i] * s_x in double (exact: an 8-bit integer times a float32). */
+int qi4o_dequant_act(const int8_t *a, int64_t n, float s_x, double *xhat)
+{
+    if (n < 0) return -2;
+    for (int64_t i = 0; i < n; i++) xhat[i] = (double)a[i] * (double)s_x;
     return 0;
 }
 
