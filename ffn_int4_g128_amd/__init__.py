@@ -76,6 +76,9 @@ def lib():
             "qlinear_int4_g128": (ci, [vp, ci, i64, i64, vp, i64, ci, vp, ci, ci, vp]),
             "qlinear_int4": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
             "qlinear_int8": (ci, [vp, ci, i64, i64, vp, i64, ci, ci, vp, ci, ci, vp]),
+            "qlinear_w4a8_workspace_bytes": (i64, [i64, i64]),
+            "qlinear_w4a8": (ci, [vp, ci, ctypes.c_float, i64, i64, vp, i64, ci, ci, vp, ci, ci,
+                                  vp, i64, vp]),
             "moe_route_topk": (ci, [vp, i64, i64, i32, vp, vp, vp]),
             "moe_route_sort": (ci, [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]),
             "moe_router_topk": (ci, [vp, i64, i64, vp, i64, i32, vp, vp, vp, vp]),
@@ -96,7 +99,8 @@ def lib():
 # declared in include/qi4.h, in header order
 EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pack", "qi4_unpack",
             "qi4_dequant_f32", "qi4_quantize", "qi4_quantize_int8", "qlinear_int4_g128",
-            "qlinear_int4", "qlinear_int8", "moe_route_topk",
+            "qlinear_int4", "qlinear_int8", "qlinear_w4a8_workspace_bytes", "qlinear_w4a8",
+            "moe_route_topk",
             "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4"]
@@ -227,6 +231,36 @@ def qlinear(x, packed, N: int, flags: int = 0, out_dtype=None, epilogue: int = Q
     else:
         _check(lib().qlinear_int4(_ptr(x), xd, T, K, _ptr(packed), N, group, flags, _ptr(out), yd,
                                   epilogue, _stream(stream)), "qlinear_int4")
+    return out
+
+
+def qlinear_w4a8(x, x_scale: float, packed, N: int, flags: int = 0, out_dtype=None,
+                 epilogue: int = QI4_EPI_NONE, out=None, workspace=None, stream=None,
+                 group: int = GROUP):
+    """W4A8: y = epilogue(x_scale * a . dequant(W)^T) with the int8 activations
+    a = clamp(rint(x * float32(1 / x_scale)), -127, 127); x bfloat16 or float32 [T][K]."""
+    import torch
+    if x.dtype == torch.bfloat16:
+        xd = QI4_BF16
+    elif x.dtype == torch.float32:
+        xd = QI4_F32
+    else:
+        raise ValueError(f"x must be bfloat16 or float32, got {x.dtype}")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    T, K = x.shape
+    out_dtype = out_dtype or x.dtype
+    n_out = N // 2 if epilogue == QI4_EPI_SILU_MUL else N
+    if out is None:
+        out = torch.empty((T, n_out), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        nb = lib().qlinear_w4a8_workspace_bytes(T, K)
+        _check(int(nb) if nb < 0 else 0, "qlinear_w4a8_workspace_bytes")
+        workspace = torch.empty(max(int(nb), 1), dtype=torch.uint8, device=x.device)
+    yd = QI4_BF16 if out.dtype == torch.bfloat16 else QI4_F32
+    _check(lib().qlinear_w4a8(_ptr(x), xd, float(x_scale), T, K, _ptr(packed), N, group, flags,
+                              _ptr(out), yd, epilogue, _ptr(workspace), workspace.numel(),
+                              _stream(stream)), "qlinear_w4a8")
     return out
 
 

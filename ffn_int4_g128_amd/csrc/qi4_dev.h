@@ -141,6 +141,15 @@ __device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// int8 x int8 -> int32, 16x16 outputs, 64-deep: lane 16 j + r supplies 16 bytes
+// of row r of A (and of column r of B) for the j-th quarter of the k range; the
+// same (lane group, byte) position of A and B holds the same k.
+__device__ inline i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
 // Four codes pairs of one dword -> four dwords of bf16 pairs holding 128 + q.
 // bf16 0x4300 is 128.0 and its last mantissa bit weighs 1, so OR-ing a code
 // q <= 15 into the low mantissa bits gives exactly 128 + q.

@@ -24,6 +24,8 @@ struct GemmArgs {
     int64_t lda;               // elements per A source row
     int64_t a_bytes;           // bytes of the whole A buffer (< 2^31)
     int a_f32;                 // float32 rows, split into 4 bf16 terms in registers
+    int a_i8;                  // int8 rows in MFMA operand order (W4A8), lda in bytes
+    float a_scale;             // W4A8: the activations' scale, applied at the store
     int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
     int a_shift;               // weight block b reads activation block b >> a_shift
                                // (1: an 8-bit matrix, two 4-bit planes per block)

@@ -57,26 +57,29 @@ __device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
 // Loads of one 128-wide group: the codes, scale and zero byte of NB tiles and
 // the raw activation fragments of MT M tiles (bf16: one 16-byte load per k
 // step; float32: two).
-template <int NB, int MT, bool AF32, int H>
+// AM: activation mode -- 0 bf16 rows, 1 float32 rows (split into bf16 terms),
+// 2 int8 rows in operand order (W4A8; 32 bytes per lane per block).
+template <int NB, int MT, int AM, int H>
 struct Stage {
     uint4 cw[NB];
     uint32_t sc[H][(NB + 1) / 2];   // per half: binary16 scales of tiles 2i, 2i+1 in dword i
     uint32_t zb[H];                 // per half: zero of tile nb in nibble nb (+ the slot offset)
-    uint4 af[MT][4][AF32 ? 2 : 1];
+    uint4 af[MT][AM == 2 ? 2 : 4][AM == 1 ? 2 : 1];
 };
 
 
 
 // Waves per SIMD the register allocation must allow: the grouped gate/up GEMM
 // sits one register above the four-wave limit without this.
-template <int NB, int MT, bool AF32, int EPI>
-constexpr int kMinWaves = (!AF32 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL) ? 4 : 1;
+template <int NB, int MT, int AM, int EPI>
+constexpr int kMinWaves = (AM == 0 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL) ? 4 : 1;
 
 // H = 2: 64-wide groups, two scales and zeros per 128-wide block.
-template <int NB, int MT, bool AF32, int S, int EPI, int H>
+template <int NB, int MT, int AM, int S, int EPI, int H>
 __global__ void __launch_bounds__(kMaxWaves * 64)
-__attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AF32, EPI>)))
+__attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI>)))
 qgemm_kernel(const GemmArgs args) {
+    constexpr bool AF32 = AM == 1, AI8 = AM == 2;
     __shared__ float red[kRedSlots * 256];
 
     const int lane = threadIdx.x & 63;
@@ -141,7 +144,7 @@ qgemm_kernel(const GemmArgs args) {
     const int spt = 16 / P;                 // slots per M tile
     const int64_t chunk = (int64_t)MT * spt;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    constexpr int ES = AF32 ? 4 : 2;        // bytes per activation element
+    constexpr int ES = AF32 ? 4 : AI8 ? 1 : 2;   // bytes per activation element
 
     for (int64_t c0 = 0; c0 < n; c0 += chunk) {
         // M tiles of this chunk that hold at least one slot (uniform per workgroup)
@@ -155,7 +158,7 @@ qgemm_kernel(const GemmArgs args) {
 
         // S register stages: while one step is multiplied, the loads of the
         // next S - 1 steps are in flight.
-        Stage<NB, MT, AF32, H> st[S];
+        Stage<NB, MT, AM, H> st[S];
         uint32_t abase[MT];
         int apart[MT];
         // Load cursor (wave-uniform): block lr, step li of that block, and the
@@ -176,7 +179,7 @@ qgemm_kernel(const GemmArgs args) {
             loa = (uint32_t)(gb >> ash) * 128u * ES;
             lnt = lr < nblk ? (int)(nt - tile < NB ? nt - tile : NB) : 0;
         };
-        auto load_w = [&](Stage<NB, MT, AF32, H> &q) {
+        auto load_w = [&](Stage<NB, MT, AM, H> &q) {
             const bool in = lnt > 0 && gb + li < ge;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -186,16 +189,22 @@ qgemm_kernel(const GemmArgs args) {
                 load_meta<NB>(wr, vs, vz, in ? los + h * kQuadScaleBytes : kOobS,
                               in ? loz + h * kQuadZeroBytes : kOobS, q.sc[h], q.zb[h]);
         };
-        auto load_a = [&](Stage<NB, MT, AF32, H> &q) {
+        auto load_a = [&](Stage<NB, MT, AM, H> &q) {
             const bool in = lnt > 0 && gb + li < ge;
             const uint32_t oa = in ? loa : kOobS;
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MT; ++m) {
+                if constexpr (AI8) {
+                    q.af[m][0][0] = buf_b128(ar, abase[m], oa);
+                    q.af[m][1][0] = buf_b128(ar, abase[m] + 16u, oa);
+                } else {
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    q.af[m][s4][0] = buf_b128(ar, abase[m] + 32u * s4 * ES, oa);
-                    if constexpr (AF32) q.af[m][s4][AF32 ? 1 : 0] = buf_b128(ar, abase[m] + 32u * s4 * ES + 16, oa);
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        q.af[m][s4][0] = buf_b128(ar, abase[m] + 32u * s4 * ES, oa);
+                        if constexpr (AF32) q.af[m][s4][AF32 ? 1 : 0] = buf_b128(ar, abase[m] + 32u * s4 * ES + 16, oa);
+                    }
                 }
+            }
         };
         auto advance = [&]() {
             loc += kTileGroupBytes;
@@ -210,7 +219,53 @@ qgemm_kernel(const GemmArgs args) {
                 rebase();
             }
         };
-        auto compute = [&](const Stage<NB, MT, AF32, H> &q, int zshift) {
+        auto compute = [&](const Stage<NB, MT, AM, H> &q, int zshift) {
+          if constexpr (AI8) {
+            // W4A8: codes as int8 operands (no offset), exact int32 sums per
+            // block; acc - xz = sum_k a * (q - zero) exactly, then the scale.
+            // The k order inside a lane's 16 bytes is the one the activation
+            // quantizer writes: low nibbles of a dword (k offsets 0, 4, 1, 5),
+            // then its high nibbles (2, 6, 3, 7), dwords s = 2kk, 2kk + 1.
+            const i32x4 zero_i = {0, 0, 0, 0};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const uint4 d = q.cw[nb];
+                const uint32_t mk = 0x0F0F0F0Fu;
+                const i32x4 b0 = {(int)(d.x & mk), (int)((d.x >> 4) & mk), (int)(d.y & mk),
+                                  (int)((d.y >> 4) & mk)};
+                const i32x4 b1 = {(int)(d.z & mk), (int)((d.z >> 4) & mk), (int)(d.w & mk),
+                                  (int)((d.w >> 4) & mk)};
+                i32x4 bz[H];
+                float sc[H];
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    const int zz = (int)(((q.zb[h] >> (zshift + 4 * nb)) & 15u) * 0x01010101u);
+                    bz[h] = i32x4{zz, zz, zz, zz};
+                    sc[h] = f16_bits_to_f32((uint16_t)(q.sc[h][nb >> 1] >> (16 * (nb & 1))));
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m >= m_used) break;
+                    const i32x4 a0 = __builtin_bit_cast(i32x4, q.af[m][0][0]);
+                    const i32x4 a1 = __builtin_bit_cast(i32x4, q.af[m][1][0]);
+                    if constexpr (H == 1) {
+                        i32x4 acc = mfma_i8(a0, b0, zero_i);
+                        i32x4 xz = mfma_i8(a0, bz[0], zero_i);
+                        acc = mfma_i8(a1, b1, acc);
+                        xz = mfma_i8(a1, bz[0], xz);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) res[m][nb][v] += sc[0] * (float)(acc[v] - xz[v]);
+                    } else {
+                        const i32x4 acc0 = mfma_i8(a0, b0, zero_i), xz0 = mfma_i8(a0, bz[0], zero_i);
+                        const i32x4 acc1 = mfma_i8(a1, b1, zero_i), xz1 = mfma_i8(a1, bz[H - 1], zero_i);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            res[m][nb][v] += sc[0] * (float)(acc0[v] - xz0[v]) +
+                                             sc[H - 1] * (float)(acc1[v] - xz1[v]);
+                    }
+                }
+            }
+          } else {
             bf16x8 a[MT][4];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -266,6 +321,7 @@ qgemm_kernel(const GemmArgs args) {
                     }
                 }
             }
+          }
         };
 
         // ---- reduction of the waves' partial sums of block r in a fixed
@@ -283,6 +339,10 @@ qgemm_kernel(const GemmArgs args) {
             const int64_t tile_b = tile0 + (int64_t)r * NB;
             const int pairs = EPI == QI4_EPI_SILU_MUL ? NB / 2 : NB;
             auto store = [&](int64_t slot, int64_t oc, float val, float uval) {
+                if constexpr (AI8) {   // the activations' scale
+                    val *= args.a_scale;
+                    uval *= args.a_scale;
+                }
                 if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
                 const int64_t dst = row0 + slot;
                 if (args.out_mode == OUT_F32) {
@@ -398,7 +458,8 @@ qgemm_kernel(const GemmArgs args) {
             const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
             const int64_t row = AF32 ? src : src * P + part;
             apart[m] = part;
-            abase[m] = ok ? (uint32_t)((row * args.lda + 8 * j) * ES) : kOob;
+            // (int8 rows: a lane's 32 bytes of a block sit at 32 j)
+            abase[m] = ok ? (uint32_t)(row * args.lda * ES + (AI8 ? 32 * j : 8 * j * ES)) : kOob;
         }
         lr = 0;
         li = 0;
@@ -434,17 +495,21 @@ template <int NB, int MT, int S, int H>
 int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
     if (a.epi == QI4_EPI_SILU_MUL) {
         if constexpr (NB % 2 == 0) {
-            if (a.a_f32)
-                qgemm_kernel<NB, MT, true, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+            if (a.a_i8)
+                qgemm_kernel<NB, MT, 2, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+            else if (a.a_f32)
+                qgemm_kernel<NB, MT, 1, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
             else
-                qgemm_kernel<NB, MT, false, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+                qgemm_kernel<NB, MT, 0, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
         } else {
             return QI4_ERR_UNSUPPORTED;
         }
+    } else if (a.a_i8) {
+        qgemm_kernel<NB, MT, 2, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     } else if (a.a_f32) {
-        qgemm_kernel<NB, MT, true, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
+        qgemm_kernel<NB, MT, 1, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     } else {
-        qgemm_kernel<NB, MT, false, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
+        qgemm_kernel<NB, MT, 0, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     }
     return launch_status();
 }
@@ -519,10 +584,58 @@ using namespace qi4;
 
 namespace {
 
-// qlinear_int4 / qlinear_int8 (flags holds QI4_INT8 for the latter).
+// W4A8 activations: one thread per 8 consecutive values of a row, k0 = 128 b +
+// 32 s + 8 j.  a = clamp(rint(x * r), -127, 127) with the float32 product (ties
+// to even; NaN gives -127), stored at row * K + 128 b + 32 j + 8 s in the order
+// of the weight operand's bytes: k0 + 0, 4, 1, 5, 2, 6, 3, 7.
+template <bool F32>
+__global__ void __launch_bounds__(256)
+quantize_act_kernel(const void *__restrict__ x, int64_t T, int64_t K, float r,
+                    uint8_t *__restrict__ out) {
+    const int64_t chunks = T * K / 8, cpr = K / 8;
+    for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
+        const int64_t row = c / cpr, k0 = 8 * (c - row * cpr);
+        float v[8];
+        if constexpr (F32) {
+            const float4 u0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row * K + k0);
+            const float4 u1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row * K + k0 + 4);
+            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+        } else {
+            const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row * K + k0);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+                v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+            }
+        }
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q = fminf(fmaxf(rintf(v[e] * r), -127.0f), 127.0f);
+            b[e] = (uint32_t)(int)q & 0xFFu;
+        }
+        const uint32_t lo = b[0] | (b[4] << 8) | (b[1] << 16) | (b[5] << 24);
+        const uint32_t hi = b[2] | (b[6] << 8) | (b[3] << 16) | (b[7] << 24);
+        const int64_t kb = k0 & ~int64_t(127), s = (k0 >> 5) & 3, j = (k0 >> 3) & 3;
+        *reinterpret_cast<uint2 *>(out + row * K + kb + 32 * j + 8 * s) = make_uint2(lo, hi);
+    }
+}
+
+// W4A8 extras of a linear call: the activations' scale and the workspace that
+// receives the int8 activations.
+struct W4A8 {
+    float scale;
+    void *ws;
+    int64_t ws_bytes;
+};
+
+// qlinear_int4 / qlinear_int8 (flags holds QI4_INT8 for the latter) /
+// qlinear_w4a8 (w4a8 given).
 int qlinear_impl(const void *x, int x_dtype, int64_t T, int64_t K, const void *packed_w,
                  int64_t N, int group_size, int flags, void *y, int y_dtype, int epilogue,
-                 void *stream) {
+                 void *stream, const W4A8 *w4a8 = nullptr) {
     int rc = check_matrix(N, K, group_size, flags);
     if (rc) return rc;
     if (x_dtype != QI4_F32 && x_dtype != QI4_BF16) return QI4_ERR_DTYPE;
@@ -541,7 +654,30 @@ int qlinear_impl(const void *x, int x_dtype, int64_t T, int64_t K, const void *p
     const int64_t wb = PackedLayout(N, Kp, flags, gs).bytes;
     if (wb >= (int64_t(1) << 31) || xb >= (int64_t(1) << 31)) return QI4_ERR_SHAPE;
     if (overlaps(y, yb, x, xb) || overlaps(y, yb, packed_w, wb)) return QI4_ERR_ALIAS;
+    float r = 0.f;
+    if (w4a8) {
+        const float sx = w4a8->scale;
+        r = 1.0f / sx;
+        if (!(sx > 0.f) || !(sx < INFINITY) || !(r < INFINITY))   // finite, positive, finite 1/s
+            return QI4_ERR_SHAPE;
+        if (!w4a8->ws) return QI4_ERR_NULL;
+        if (w4a8->ws_bytes < T * K) return QI4_ERR_WORKSPACE;
+        if (!aligned(w4a8->ws, 16)) return QI4_ERR_SHAPE;
+        if (overlaps(w4a8->ws, T * K, x, xb) || overlaps(w4a8->ws, T * K, y, yb) ||
+            overlaps(w4a8->ws, T * K, packed_w, wb))
+            return QI4_ERR_ALIAS;
+    }
     if ((rc = check_device())) return rc;
+    if (w4a8) {
+        const int64_t chunks = T * K / 8;
+        const unsigned g = (unsigned)(chunks / 256 + 1 < 65536 ? chunks / 256 + 1 : 65536);
+        uint8_t *a8 = static_cast<uint8_t *>(w4a8->ws);
+        if (x_dtype == QI4_F32)
+            quantize_act_kernel<true><<<g, 256, 0, as_stream(stream)>>>(x, T, K, r, a8);
+        else
+            quantize_act_kernel<false><<<g, 256, 0, as_stream(stream)>>>(x, T, K, r, a8);
+        if ((rc = launch_status())) return rc;
+    }
 
     GemmArgs a = {};
     a.w = static_cast<const uint8_t *>(packed_w);
@@ -555,6 +691,14 @@ int qlinear_impl(const void *x, int x_dtype, int64_t T, int64_t K, const void *p
     a.a_bytes = xb;
     a.a_f32 = x_dtype == QI4_F32;
     a.P = a.a_f32 ? 4 : 1;
+    if (w4a8) {   // the GEMM reads the int8 rows
+        a.a = w4a8->ws;
+        a.a_bytes = T * K;
+        a.a_f32 = 0;
+        a.a_i8 = 1;
+        a.a_scale = w4a8->scale;
+        a.P = 1;
+    }
     a.moe = 0;
     a.T = T;
     a.out = y;
@@ -580,6 +724,22 @@ extern "C" int qlinear_int8(const void *x, int x_dtype, int64_t T, int64_t K,
                             int y_dtype, int epilogue, void *stream) {
     return qlinear_impl(x, x_dtype, T, K, packed_w, N, group_size, flags | QI4_INT8, y, y_dtype,
                         epilogue, stream);
+}
+
+extern "C" int64_t qlinear_w4a8_workspace_bytes(int64_t T, int64_t K) {
+    if (T < 0 || K < 128 || K % 128 || T > (int64_t(1) << 31) || K > (int64_t(1) << 30))
+        return QI4_ERR_SHAPE;
+    return (T * K + 255) & ~int64_t(255);
+}
+
+extern "C" int qlinear_w4a8(const void *x, int x_dtype, float x_scale, int64_t T, int64_t K,
+                            const void *packed_w, int64_t N, int group_size, int flags, void *y,
+                            int y_dtype, int epilogue, void *workspace, int64_t ws_bytes,
+                            void *stream) {
+    if (flags & QI4_INT8) return QI4_ERR_UNSUPPORTED;   // 4-bit weights only
+    const W4A8 w{x_scale, workspace, ws_bytes};
+    return qlinear_impl(x, x_dtype, T, K, packed_w, N, group_size, flags, y, y_dtype, epilogue,
+                        stream, &w);
 }
 
 extern "C" int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,

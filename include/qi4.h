@@ -186,6 +186,26 @@ int qlinear_int8(const void *x, int x_dtype, int64_t T, int64_t K,
                  const void *packed_w, int64_t N, int group_size, int flags,
                  void *y, int y_dtype, int epilogue, void *stream);
 
+/* W4A8: the linear layer with int8 activations (the FastDeploy page,
+ * x-techcon, names W4A8 static quantization: 4-bit weights, 8-bit activations
+ * with a scale fixed ahead of time).  One static scale x_scale per tensor
+ * (finite, > 0, with a finite float32 reciprocal, else QI4_ERR_SHAPE):
+ *   r = float32(1 / x_scale)   (computed on the host in float32)
+ *   a = clamp(rint(x * r), -127, 127)   float32 product, ties to even, NaN -> -127
+ *   y = epilogue( x_scale * sum_k a_k * dequant(W)[n][k] )
+ * The inner sums run on int8 MFMA in exact int32 per 128-wide block (the zero
+ * point subtracted exactly), then the binary16 scale in float32.
+ *   workspace  device, >= qlinear_w4a8_workspace_bytes(T, K) bytes, 16-byte
+ *              aligned; receives the int8 activations (QI4_ERR_WORKSPACE if
+ *              smaller); must not overlap x, y or packed_w.
+ * 4-bit matrices only (QI4_INT8 in flags is QI4_ERR_UNSUPPORTED); other
+ * arguments as qlinear_int4. */
+int64_t qlinear_w4a8_workspace_bytes(int64_t T, int64_t K);
+int qlinear_w4a8(const void *x, int x_dtype, float x_scale, int64_t T, int64_t K,
+                 const void *packed_w, int64_t N, int group_size, int flags,
+                 void *y, int y_dtype, int epilogue, void *workspace, int64_t ws_bytes,
+                 void *stream);
+
 /* ---------------------------------------------------------------------------
  * Routed mixture-of-experts FFN (decode and prefill).
  * Routed expert e uses packed gate/up block w_gate_up + e * qi4_packed_bytes(2I, H,

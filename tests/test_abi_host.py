@@ -116,6 +116,19 @@ def test_argument_errors_return_before_any_launch(q):
     assert L.qi4_quantize_int8(p, 1, 16, 128, 128, ctypes.c_void_p(0x1004), p, p, None) == -2
     assert L.qi4_quantize_int8(None, 1, 16, 128, 128, p, p, p, None) == -1
     assert L.qi4_pack(p, p, p, 16, 128, 128, 2, ctypes.c_void_p(0x2004), None) == -2
+    # W4A8: scale, workspace, 8-bit weights refused
+    inf, nan = float("inf"), float("nan")
+    assert L.qlinear_w4a8_workspace_bytes(3, 256) == 768
+    assert L.qlinear_w4a8_workspace_bytes(3, 100) == -2
+    xs, ys, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    for bad in (0.0, -1.0, inf, nan, 1e-39):
+        assert L.qlinear_w4a8(xs, 1, bad, 1, 128, p, 16, 128, 0, ys, 1, 0, ws, 128, None) == -2
+    assert L.qlinear_w4a8(p, 1, 0.1, 2, 128, p, 16, 128, 0, ctypes.c_void_p(0x200000), 1, 0,
+                          ctypes.c_void_p(0x300000), 255, None) == -5
+    assert L.qlinear_w4a8(p, 1, 0.1, 2, 128, p, 16, 128, 0, ctypes.c_void_p(0x200000), 1, 0,
+                          None, 256, None) == -1
+    assert L.qlinear_w4a8(xs, 1, 0.1, 1, 128, p, 16, 128, 2, ys, 1, 0, ws, 128, None) == -7
+    assert L.qlinear_w4a8(p, 1, 0.1, 0, 128, p, 16, 128, 0, p, 1, 0, None, 0, None) == 0
     # fused routing + permutation: shape, NULL, aliasing, T == 0
     assert L.moe_route_sort(p, 4, 8, 9, p, p, p, p, p, p, None) == -2
     assert L.moe_route_sort(p, 4, 2000, 8, p, p, p, p, p, p, None) == -2

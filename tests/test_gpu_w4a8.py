@@ -1,0 +1,104 @@
+"""GPU parity of W4A8 (int8 activations with a static per-tensor scale, the
+FastDeploy page's "W4A8 static quantization", on int8 MFMA): the int8
+activations bit for bit against the oracle's float32 decision, and
+qlinear_w4a8 within 2e-3 * sum|w * xhat| of the oracle fed the same int8
+activations (xhat = a * x_scale), over bf16 and float32 inputs, group sizes,
+ragged shapes, clamped activations and the SiLU(gate)*up epilogue."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests._gpu import assert_within, bf16_dev, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack(w, flags, group):
+    import ffn_int4_g128_amd as q
+    return q.pack(to_dev(w["qweight"]), to_dev(w["scales"]), to_dev(w["zeros"]), w["N"], w["K"],
+                  flags, group=group)
+
+
+def _x(seed, T, K, xd):
+    x = workloads.activations(seed, K + T, T, K, xd)
+    x32 = workloads.bf16_bits_to_f32(x) if xd == "bf16" else x
+    return (bf16_dev(x) if xd == "bf16" else to_dev(x)), x32
+
+
+def _unpermute(ws: np.ndarray, T: int, K: int) -> np.ndarray:
+    """The workspace's operand order back to [T][K]: bytes 128 b + 32 j + 8 s + i
+    of a row hold k = 128 b + 32 s + 8 j + (0, 4, 1, 5, 2, 6, 3, 7)[i]."""
+    a = ws[:T * K].view(np.int8).reshape(T, K // 128, 4, 4, 8)     # [t][b][j][s][i]
+    order = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+    out = np.empty((T, K // 128, 4, 4, 8), dtype=np.int8)          # [t][b][s][j][e]
+    out[..., order] = a.transpose(0, 1, 3, 2, 4)
+    return out.reshape(T, K)
+
+
+@pytest.mark.parametrize("xd", ["bf16", "f32"])
+@pytest.mark.parametrize("T,K,scale", [(1, 256, None), (7, 1024, None), (32, 384, 0.01),
+                                       (3, 512, 0.5)])
+def test_int8_activations_bit_exact(xd, T, K, scale):
+    import torch
+    import ffn_int4_g128_amd as q
+    N = 32
+    w = workloads.weights(101, T, N, K, 0.005, 0.02)
+    xt, x32 = _x(101, T, K, xd)
+    s = scale or float(np.abs(x32).max()) / 127.0
+    ws = torch.zeros(q.lib().qlinear_w4a8_workspace_bytes(T, K), dtype=torch.uint8, device="cuda")
+    q.qlinear_w4a8(xt, s, _pack(w, 0, 128), N, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    a = _unpermute(ws.cpu().numpy(), T, K)
+    assert np.array_equal(a, oracle.quantize_act(x32, s))
+
+
+@pytest.mark.parametrize("group", [128, 64, 0])
+@pytest.mark.parametrize("T,N,K,xd", [(1, 130, 768, "bf16"), (5, 64, 1024, "f32"),
+                                      (16, 48, 512, "bf16"), (17, 80, 512, "bf16"),
+                                      (32, 1000, 2048, "bf16"), (100, 40, 384, "f32"),
+                                      (1, 4096, 4096, "bf16")])
+def test_qlinear_w4a8(group, T, N, K, xd):
+    import torch
+    import ffn_int4_g128_amd as q
+    if group and K % group:
+        pytest.skip("group does not divide K")
+    w = workloads.weights(102, T * 7 + N + group, N, K, 0.005, 0.02, group=group)
+    xt, x32 = _x(102, T, K, xd)
+    s = float(np.abs(x32).max()) / 127.0
+    y = q.qlinear_w4a8(xt, s, _pack(w, 0, group), N, out_dtype=torch.float32, group=group)
+    torch.cuda.synchronize()
+    ref, S, _ = oracle.linear_w4a8(x32, s, w["qweight"], w["scales"], w["zeros"], N, K,
+                                   group=group or K)
+    assert_within(to_f64(y), ref, oracle.C_TOL * S, f"w4a8 group {group} T{T} N{N} K{K} {xd}")
+
+
+def test_qlinear_w4a8_clamped_and_large():
+    # a scale that clamps many activations, a 5120 x 13824 matrix, bf16 output
+    import torch
+    import ffn_int4_g128_amd as q
+    T, N, K = 3, 5120, 13824
+    w = workloads.weights(103, 0, N, K, 0.002, 0.01)
+    xt, x32 = _x(103, T, K, "bf16")
+    s = 0.01
+    y = q.qlinear_w4a8(xt, s, _pack(w, 0, 128), N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, S, a = oracle.linear_w4a8(x32, s, w["qweight"], w["scales"], w["zeros"], N, K)
+    assert (np.abs(a) == 127).mean() > 0.15   # |x| > 1.27: about a fifth of N(0,1)
+    assert_within(to_f64(y), ref, oracle.C_TOL * S, "w4a8 clamped 5120x13824")
+
+
+@pytest.mark.parametrize("group", [128, 64])
+def test_qlinear_w4a8_silu_mul(group):
+    import torch
+    import ffn_int4_g128_amd as q
+    T, I, K = 6, 40, 512
+    w = workloads.weights(104, group, 2 * I, K, 0.005, 0.02, group=group)
+    xt, x32 = _x(104, T, K, "bf16")
+    s = float(np.abs(x32).max()) / 127.0
+    y = q.qlinear_w4a8(xt, s, _pack(w, q.QI4_PACK_GATEUP, group), 2 * I, flags=q.QI4_PACK_GATEUP,
+                       out_dtype=torch.float32, epilogue=q.QI4_EPI_SILU_MUL, group=group)
+    torch.cuda.synchronize()
+    xh = oracle.dequant_act(oracle.quantize_act(x32, s), s)
+    h, tol = oracle.gate_up_silu(xh, w["qweight"], w["scales"], w["zeros"], I, K, group=group)
+    assert_within(to_f64(y), h, tol, f"w4a8 silu_mul group {group}")
