@@ -452,11 +452,30 @@ def run_dense(q, torch, reps=20):
                            "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
                            "tokens_per_s": T / t})
         del pw
+    # W4A8: the 4-bit matrices of the sweep with int8 activations (static
+    # scale max|x| / 127); the time includes the activation-quantizing launch
+    sweep_w4a8 = []
+    for i, (K, N) in enumerate(c2["shapes"]):
+        w = workloads.weights(c2["seed"], 10 + i, N, K, *c2["scale"])
+        pw = _dense_pack(q, torch, w)
+        for T in (1, 8, 32):
+            xb = workloads.activations(c2["seed"], 20 + 10 * i + T, T, K, "bf16", c2["x_scale"])
+            sx = float(abs(workloads.bf16_bits_to_f32(xb)).max()) / 127.0
+            x = q_bf16(torch, xb)
+            y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(q.lib().qlinear_w4a8_workspace_bytes(T, K), dtype=torch.uint8,
+                             device="cuda")
+            t = timed(lambda: q.qlinear_w4a8(x, sx, pw, N, out=y, workspace=ws))
+            b = N * K * per_w + T * K * 2 + T * N * 2
+            sweep_w4a8.append({"K": K, "N": N, "T": T, "us": t * 1e6,
+                               "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
+                               "tokens_per_s": T / t})
+        del pw
     del rd
     torch.cuda.empty_cache()
     return {"protocol": "1 GiB read before each rep (outside the events); median of "
                         f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep,
-            "skinny_sweep_int8": sweep8}
+            "skinny_sweep_int8": sweep8, "skinny_sweep_w4a8": sweep_w4a8}
 
 
 def run_router(q, torch, reps=20):
