@@ -69,12 +69,16 @@ def lib():
                                + [_i64, ci, ctypes.c_double, ctypes.c_double, _dp, _dp, ci])
         L.qi4o_quantize.argtypes = [_dp, _i64, _i64, _i64, ci, _u8p, _u16p, _u8p]
         L.qi4o_quantize_act.argtypes = [_fp, _i64, ctypes.c_float, _i8p]
+        L.qi4o_moe_w4a8.argtypes = ([_fp, _i64, _i64, _i64, _i64, ctypes.c_int, _i32p, _dp]
+                                    + [_u8p, _u16p, _u8p] * 4
+                                    + [_i64, ctypes.c_float, ctypes.c_float, ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_double, _dp, _dp, ci])
         L.qi4o_dequant_act.argtypes = [_i8p, _i64, ctypes.c_float, _dp]
         for f in ("qi4o_unpack", "qi4o_dequant", "qi4o_linear", "qi4o_gate_up_silu",
                   "qi4o_topk_softmax", "qi4o_sort", "qi4o_moe", "qi4o_quantize",
-                  "qi4o_quantize_act", "qi4o_dequant_act"):
+                  "qi4o_quantize_act", "qi4o_dequant_act", "qi4o_moe_w4a8"):
             getattr(L, f).restype = ctypes.c_int
-        if L.qi4o_abi_version() != 3:
+        if L.qi4o_abi_version() != 4:
             raise RuntimeError("stale oracle library: rebuild it (oracle.build())")
         _lib = L
     return _lib
@@ -299,6 +303,48 @@ def moe(x64: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: dict, shared: 
                           *[_ptr(a, t) for a, t in zip(sa, types)],
                           group, bits, c, eps_p, _ptr(out, _dp), _ptr(tol, _dp),
                           threads or default_threads()), "moe")
+    return out, tol
+
+
+#: relative bound on the W4A8 GPU path's error in g and u (exact int32 sums; a few
+#: float32 roundings), used only to find the int8 h decisions that may differ
+C_AMB_W4A8 = 1e-4
+
+
+def moe_w4a8(x32: np.ndarray, x_scale: float, h_scale: float, ids: np.ndarray, p: np.ndarray,
+             experts: dict, shared: dict | None, H: int, I: int, E: int, group: int = 128,
+             c: float = C_TOL, c_amb: float = C_AMB_W4A8, eps_p: float = EPS_P,
+             threads: int | None = None):
+    """W4A8 MoE layer: (out, tol), both [T][H] float64.  x32 float32 [T][H] (bf16
+    inputs widen exactly); int8 activations with static scales x_scale (layer
+    input) and h_scale (the down projection's input); 4-bit expert weights as in
+    moe()."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32).reshape(-1, H)
+    T = x32.shape[0]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    k = ids.shape[1]
+    out = np.empty((T, H), dtype=np.float64)
+    tol = np.empty((T, H), dtype=np.float64)
+
+    def arrs(d):
+        if d is None:
+            return [None] * 6
+        return [np.ascontiguousarray(d["gu_q"], dtype=np.uint8),
+                np.ascontiguousarray(d["gu_s"], dtype=np.uint16),
+                np.ascontiguousarray(d["gu_z"], dtype=np.uint8),
+                np.ascontiguousarray(d["dn_q"], dtype=np.uint8),
+                np.ascontiguousarray(d["dn_s"], dtype=np.uint16),
+                np.ascontiguousarray(d["dn_z"], dtype=np.uint8)]
+
+    ea, sa = arrs(experts), arrs(shared)
+    types = [_u8p, _u16p, _u8p] * 2
+    _check(lib().qi4o_moe_w4a8(_ptr(x32, _fp), T, H, I, E, k, _ptr(ids, _i32p), _ptr(p, _dp),
+                               *[_ptr(a, t) for a, t in zip(ea, types)],
+                               *[_ptr(a, t) for a, t in zip(sa, types)],
+                               group, np.float32(x_scale), np.float32(h_scale), c, c_amb, eps_p,
+                               _ptr(out, _dp), _ptr(tol, _dp), threads or default_threads()),
+           "moe_w4a8")
     return out, tol
 
 

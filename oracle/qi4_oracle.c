@@ -52,7 +52,7 @@
 #include <string.h>
 #include <math.h>
 
-#define ORACLE_ABI 3
+#define ORACLE_ABI 4
 int qi4o_abi_version(void) { return ORACLE_ABI; }
 
 /* ---- IEEE binary16 <-> double ----------------------------------------- */
@@ -404,6 +404,118 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
         }
     }
     free(y); free(A); free(h); free(th);
+    return rc;
+}
+
+/* ---- W4A8 MoE (R30 applied to both projections) -------------------------- */
+
+/* One expert with int8 activations: h = SiLU(g) * u from xhat (already the
+   dequantized int8 input); the decision a_h = clamp(rint(float32(float32(h) * r_h)),
+   -127, 127) with r_h = float32(1 / s_h), hhat = a_h * s_h; y = hhat . W_d^T.
+   A[n] = sum_k |W_d[n][k] * hhat_k| (for the per-linear factor c) and
+   B[n] = s_h * sum_k |W_d[n][k]| over the k whose decision is not certain: the
+   range h +- amb_k (amb = the first-order effect of a relative error c_amb in g
+   and u, plus the float32 roundings of h and of h * r_h) maps to two different
+   clamped codes. */
+static int expert_ffn_w4a8(const double *xhat, int64_t H, int64_t I, int64_t Ggu, int64_t Gdn,
+                           float s_h, double c_amb, const uint8_t *gq, const uint16_t *gs,
+                           const uint8_t *gz, const uint8_t *dq, const uint16_t *ds,
+                           const uint8_t *dz, double *y, double *A, double *B, double *h,
+                           double *amb, double *hq, int *unsure, int threads)
+{
+    int rc = qi4o_gate_up_silu(xhat, 1, H, gq, gs, gz, I, Ggu, 4, c_amb, h, amb, threads);
+    if (rc) return rc;
+    const float r = 1.0f / s_h;
+    for (int64_t i = 0; i < I; i++) {
+        volatile float hf = (float)h[i];
+        volatile float pr = hf * r;
+        float q = rintf(pr);
+        if (!(q >= -127.0f)) q = -127.0f;
+        if (q > 127.0f) q = 127.0f;
+        hq[i] = (double)q * (double)s_h;
+        const double m = amb[i] + fabs(h[i]) * ldexp(1.0, -22);
+        double lo = rint((h[i] - m) * (double)r), hi = rint((h[i] + m) * (double)r);
+        lo = lo < -127 ? -127 : (lo > 127 ? 127 : lo);
+        hi = hi < -127 ? -127 : (hi > 127 ? 127 : hi);
+        unsure[i] = lo != hi;
+    }
+#pragma omp parallel for num_threads(threads) schedule(static)
+    for (int64_t n = 0; n < H; n++) {
+        double acc = 0.0, a = 0.0, b = 0.0;
+        for (int64_t i = 0; i < I; i++) {
+            double w = w_at(dq, ds, dz, I, Gdn, 4, n, i);
+            acc += w * hq[i];
+            a += fabs(w * hq[i]);
+            if (unsure[i]) b += fabs(w) * (double)s_h;
+        }
+        y[n] = acc;
+        A[n] = a;
+        B[n] = b;
+    }
+    return 0;
+}
+
+/* out[t] = sum_j p[t][j] * FFN8_{ids[t][j]}(xhat_t) + FFN8_shared(xhat_t) with
+   xhat = the int8 activations of x (scale s_x, qi4o_quantize_act) times s_x and
+   FFN8 the expert above; 4-bit weights as in qi4o_moe.  tol = sum_j p_j
+   (c A_j + B_j) + c A_sh + B_sh + eps_p sum_j |y_j|: the per-linear factor on the
+   down projection and the uncertain h decisions (the gate/up error enters only
+   through those, bounded by c_amb). */
+int qi4o_moe_w4a8(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                  const int32_t *ids, const double *p,
+                  const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *gu_z,
+                  const uint8_t *dn_q, const uint16_t *dn_s, const uint8_t *dn_z,
+                  const uint8_t *sh_gu_q, const uint16_t *sh_gu_s, const uint8_t *sh_gu_z,
+                  const uint8_t *sh_dn_q, const uint16_t *sh_dn_s, const uint8_t *sh_dn_z,
+                  int64_t G, float s_x, float s_h, double c, double c_amb, double eps_p,
+                  double *out, double *tol, int threads)
+{
+    const int64_t Ggu = G ? G : H, Gdn = G ? G : I;
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || G < 0 || H % Ggu || I % Gdn) return -2;
+    if (!(s_x > 0.0f) || !(s_h > 0.0f)) return -2;
+    if (threads < 1) threads = 1;
+    const int64_t gu_qb = code_bytes(2 * I, H, 4), gu_mb = 2 * I * (H / Ggu);
+    const int64_t dn_qb = code_bytes(H, I, 4), dn_mb = H * (I / Gdn);
+    double *xh = (double *)malloc(sizeof(double) * (size_t)H);
+    int8_t *ax = (int8_t *)malloc((size_t)H);
+    double *y = (double *)malloc(sizeof(double) * (size_t)H);
+    double *A = (double *)malloc(sizeof(double) * (size_t)H);
+    double *B = (double *)malloc(sizeof(double) * (size_t)H);
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    double *amb = (double *)malloc(sizeof(double) * (size_t)I);
+    double *hq = (double *)malloc(sizeof(double) * (size_t)I);
+    int *un = (int *)malloc(sizeof(int) * (size_t)I);
+    int rc = 0;
+    if (!xh || !ax || !y || !A || !B || !h || !amb || !hq || !un) rc = -9;
+    for (int64_t t = 0; t < T && rc == 0; t++) {
+        qi4o_quantize_act(x + t * H, H, 1.0f / s_x, ax);
+        qi4o_dequant_act(ax, H, s_x, xh);
+        double *ot = out + t * H;
+        double *tt = tol ? tol + t * H : NULL;
+        for (int64_t n = 0; n < H; n++) { ot[n] = 0.0; if (tt) tt[n] = 0.0; }
+        for (int j = 0; j < k && rc == 0; j++) {
+            int64_t e = ids[t * k + j];
+            if (e < 0 || e >= E) { rc = -3; break; }
+            double pj = p[t * k + j];
+            rc = expert_ffn_w4a8(xh, H, I, Ggu, Gdn, s_h, c_amb,
+                                 gu_q + e * gu_qb, gu_s + e * gu_mb, gu_z + e * gu_mb,
+                                 dn_q + e * dn_qb, dn_s + e * dn_mb, dn_z + e * dn_mb,
+                                 y, A, B, h, amb, hq, un, threads);
+            for (int64_t n = 0; n < H; n++) {
+                ot[n] += pj * y[n];
+                if (tt) tt[n] += pj * (c * A[n] + B[n]) + eps_p * fabs(y[n]);
+            }
+        }
+        if (rc == 0 && sh_gu_q) {
+            rc = expert_ffn_w4a8(xh, H, I, Ggu, Gdn, s_h, c_amb, sh_gu_q, sh_gu_s, sh_gu_z,
+                                 sh_dn_q, sh_dn_s, sh_dn_z, y, A, B, h, amb, hq, un, threads);
+            for (int64_t n = 0; n < H; n++) {
+                ot[n] += y[n];
+                if (tt) tt[n] += c * A[n] + B[n];
+            }
+        }
+    }
+    free(xh); free(ax); free(y); free(A); free(B); free(h); free(amb); free(hq); free(un);
     return rc;
 }
 

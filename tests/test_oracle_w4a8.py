@@ -60,3 +60,66 @@ def test_quantization_error_bound():
     assert np.all(np.abs(a.astype(np.float64) * np.float32(s) - x) <= s * (0.5 + 1e-5))
     assert np.all(np.abs(y - y0) <= (s * (0.5 + 1e-5)) * wabs[None, :])
     assert np.abs(a).max() == 127 and np.abs(y - y0).max() > 0
+
+
+# ---- the W4A8 MoE layer ----------------------------------------------------------
+
+def _small_moe(seed, E=4, H=256, I=128):
+    ex = workloads.moe_experts(seed, 0, E, H, I, 0.005, 0.02)
+    sh = workloads.moe_shared(seed, 0, H, I, 0.005, 0.02)
+    x = workloads.bf16_bits_to_f32(workloads.activations(seed, 1, 3, H, "bf16"))
+    return ex, sh, x, E, H, I
+
+
+def test_moe_w4a8_top1_is_the_chain_of_pinned_pieces():
+    # one expert with weight 1, no shared one: xhat from the activation quantizer,
+    # h = SiLU(g) * u (pinned gate_up_silu), h quantized the same way, then the
+    # pinned linear layer
+    ex, _, x, E, H, I = _small_moe(41)
+    sx, shh = float(np.abs(x).max()) / 127.0, 0.05
+    ids = np.array([[2], [0], [3]], dtype=np.int32)
+    out, tol = oracle.moe_w4a8(x, sx, shh, ids, np.ones((3, 1)), ex, None, H, I, E)
+    xh = oracle.dequant_act(oracle.quantize_act(x, sx), sx)
+    for t in range(3):
+        e = ids[t, 0]
+        h, _ = oracle.gate_up_silu(xh[t:t + 1], ex["gu_q"][e], ex["gu_s"][e], ex["gu_z"][e], I, H)
+        hh = oracle.dequant_act(oracle.quantize_act(h.astype(np.float32), shh), shh)
+        y, S = oracle.linear(hh, ex["dn_q"][e], ex["dn_s"][e], ex["dn_z"][e], H, I)
+        assert np.array_equal(out[t], y[0])
+        assert np.all(tol[t] >= oracle.C_TOL * S[0] * (1 - 1e-12))
+
+
+def test_moe_w4a8_fine_h_grid_approaches_the_plain_layer_on_xhat():
+    # with a fine h grid the int8 h step vanishes: |out - moe(xhat)| <= s_h / 2 *
+    # sum of |W_d| over the selected experts and the shared one (clamping off:
+    # s_h * 127 above every |h|)
+    ex, sh, x, E, H, I = _small_moe(42)
+    sx = float(np.abs(x).max()) / 127.0
+    ids = np.array([[1, 3], [0, 2], [3, 0]], dtype=np.int32)
+    pw = np.array([[0.75, 0.25], [0.5, 0.5], [0.1, 0.9]])
+    xh = oracle.dequant_act(oracle.quantize_act(x, sx), sx)
+    ref, _ = oracle.moe(xh, ids, pw, ex, sh, H, I, E)
+    hmax = 0.0
+    for e in range(E):
+        h, _ = oracle.gate_up_silu(xh, ex["gu_q"][e], ex["gu_s"][e], ex["gu_z"][e], I, H)
+        hmax = max(hmax, float(np.abs(h).max()))
+    hs, _ = oracle.gate_up_silu(xh, sh["gu_q"], sh["gu_s"], sh["gu_z"], I, H)
+    hmax = max(hmax, float(np.abs(hs).max()))
+    shh = hmax / 127.0
+    out, _ = oracle.moe_w4a8(x, sx, shh, ids, pw, ex, sh, H, I, E)
+    wd = [np.abs(oracle.dequant(ex["dn_q"][e], ex["dn_s"][e], ex["dn_z"][e], H, I)).sum(axis=1)
+          for e in range(E)]
+    wsh = np.abs(oracle.dequant(sh["dn_q"], sh["dn_s"], sh["dn_z"], H, I)).sum(axis=1)
+    for t in range(3):
+        bound = shh * (0.5 + 1e-5) * (sum(pw[t, j] * wd[ids[t, j]] for j in range(2)) + wsh)
+        assert np.all(np.abs(out[t] - ref[t]) <= bound)
+    assert np.abs(out - ref).max() > 0
+
+
+def test_moe_w4a8_zero_weights_leave_the_shared_expert():
+    ex, sh, x, E, H, I = _small_moe(43)
+    sx, shh = float(np.abs(x).max()) / 127.0, 0.02
+    ids = np.array([[0, 1], [2, 3], [1, 2]], dtype=np.int32)
+    out, _ = oracle.moe_w4a8(x, sx, shh, ids, np.zeros((3, 2)), ex, sh, H, I, E)
+    only, _ = oracle.moe_w4a8(x, sx, shh, ids[:, :1], np.zeros((3, 1)), ex, sh, H, I, E)
+    assert np.array_equal(out, only) and np.abs(out).max() > 0
