@@ -88,6 +88,9 @@ def lib():
             "moe_expert_down": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, i64, vp]),
             "moe_combine": (ci, [dp, vp, vp, vp, i64, vp, vp]),
             "moe_ffn_int4": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+            "moe_ffn_w4a8_workspace_bytes": (i64, [dp, i64]),
+            "moe_ffn_w4a8": (ci, [dp, vp, ctypes.c_float, ctypes.c_float, i64, vp, vp, vp, vp, vp,
+                                  vp, vp, vp, vp, i64, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -103,7 +106,7 @@ EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pac
             "moe_route_topk",
             "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
-            "moe_combine", "moe_ffn_int4"]
+            "moe_combine", "moe_ffn_int4", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_w4a8"]
 
 
 def _check(rc: int, what: str):
@@ -411,6 +414,34 @@ def moe_ffn(x, w: MoeWeights, top_k: int, logits=None, ids=None, weights=None, w
                               _ptr(w.w_gate_up), _ptr(w.w_down), _ptr(w.shared_gate_up),
                               _ptr(w.shared_down), _ptr(out), _ptr(workspace),
                               workspace.numel(), _stream(stream)), "moe_ffn_int4")
+    if return_routing:
+        return out, ids, weights
+    return out
+
+
+def moe_ffn_w4a8(x, w: MoeWeights, top_k: int, x_scale: float, h_scale: float, logits=None,
+                 ids=None, weights=None, workspace=None, out=None, return_routing: bool = False,
+                 stream=None):
+    """W4A8 MoE layer: moe_ffn with int8 activations (static scales x_scale for x
+    and h_scale for h = SiLU(g) * u); x bf16 [T][H]."""
+    import torch
+    _need(x, torch.bfloat16, "x")
+    T = x.shape[0]
+    d = w.desc(top_k)
+    if workspace is None:
+        nb = lib().moe_ffn_w4a8_workspace_bytes(ctypes.byref(d), T)
+        _check(int(nb) if nb < 0 else 0, "moe_ffn_w4a8_workspace_bytes")
+        workspace = torch.empty(max(int(nb), 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, w.H), dtype=torch.bfloat16, device=x.device)
+    if logits is not None and return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+        weights = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_ffn_w4a8(ctypes.byref(d), _ptr(x), float(x_scale), float(h_scale), T,
+                              _ptr(logits), _ptr(ids), _ptr(weights), _ptr(w.w_gate_up),
+                              _ptr(w.w_down), _ptr(w.shared_gate_up), _ptr(w.shared_down),
+                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_ffn_w4a8")
     if return_routing:
         return out, ids, weights
     return out

@@ -6,7 +6,8 @@
 
 namespace qi4 {
 
-enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_SPLIT2 = 2 };
+// OUT_I8: int8 rows in MFMA operand order (W4A8 h), q = clamp(rint(v * out_r))
+enum OutMode { OUT_F32 = 0, OUT_BF16 = 1, OUT_SPLIT2 = 2, OUT_I8 = 3 };
 
 // One launch computes out[dst(s)][n] = epi(sum_k A[src(s)][k] * W[n][k]) for the
 // "slots" s of one or more problems (a problem = one weight matrix and the rows
@@ -42,6 +43,7 @@ struct GemmArgs {
     void *out;
     int64_t ldo;               // elements per output row
     int out_mode;              // OutMode
+    float out_r;               // OUT_I8: reciprocal of the output's int8 scale
     int epi;                   // QI4_EPI_NONE or QI4_EPI_SILU_MUL
     int64_t n_out;             // valid output columns
     // set by launch_qgemm
@@ -51,5 +53,10 @@ struct GemmArgs {
 // Launch the GEMM for `n_problems` problems (grid.y); `max_slots` bounds the
 // slots of any one problem and picks the M tiling.  Returns a QI4 status.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t stream);
+
+// W4A8 activations: rows x [T][K] (bf16, or float32 when x_f32) -> int8 rows in
+// the operand order the AM = 2 GEMM reads, a = clamp(rint(x * r), -127, 127).
+int launch_quantize_act(const void *x, int x_f32, int64_t T, int64_t K, float r, uint8_t *out,
+                        hipStream_t stream);
 
 }  // namespace qi4

@@ -349,6 +349,13 @@ qgemm_kernel(const GemmArgs args) {
                     static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
                 } else if (args.out_mode == OUT_BF16) {
                     static_cast<uint16_t *>(args.out)[dst * args.ldo + oc] = (uint16_t)f32_to_bf16_rne(val);
+                } else if (args.out_mode == OUT_I8) {
+                    // the activation quantizer's decision and byte order (k offset e
+                    // of a dword at 2 (e & 3) + (e >> 2))
+                    const float qv = fminf(fmaxf(rintf(val * args.out_r), -127.0f), 127.0f);
+                    const int64_t pos = (oc & ~int64_t(127)) + 32 * ((oc >> 3) & 3) +
+                                        8 * ((oc >> 5) & 3) + 2 * (oc & 3) + ((oc >> 2) & 1);
+                    static_cast<int8_t *>(args.out)[dst * args.ldo + pos] = (int8_t)(int)qv;
                 } else {
                     const uint32_t hi = f32_to_bf16_rne(val);
                     const uint32_t lo = f32_to_bf16_rne(val - bf16_to_f32(hi));
@@ -669,14 +676,9 @@ int qlinear_impl(const void *x, int x_dtype, int64_t T, int64_t K, const void *p
     }
     if ((rc = check_device())) return rc;
     if (w4a8) {
-        const int64_t chunks = T * K / 8;
-        const unsigned g = (unsigned)(chunks / 256 + 1 < 65536 ? chunks / 256 + 1 : 65536);
-        uint8_t *a8 = static_cast<uint8_t *>(w4a8->ws);
-        if (x_dtype == QI4_F32)
-            quantize_act_kernel<true><<<g, 256, 0, as_stream(stream)>>>(x, T, K, r, a8);
-        else
-            quantize_act_kernel<false><<<g, 256, 0, as_stream(stream)>>>(x, T, K, r, a8);
-        if ((rc = launch_status())) return rc;
+        if ((rc = launch_quantize_act(x, x_dtype == QI4_F32, T, K, r,
+                                      static_cast<uint8_t *>(w4a8->ws), as_stream(stream))))
+            return rc;
     }
 
     GemmArgs a = {};
@@ -724,6 +726,16 @@ extern "C" int qlinear_int8(const void *x, int x_dtype, int64_t T, int64_t K,
                             int y_dtype, int epilogue, void *stream) {
     return qlinear_impl(x, x_dtype, T, K, packed_w, N, group_size, flags | QI4_INT8, y, y_dtype,
                         epilogue, stream);
+}
+
+int qi4::launch_quantize_act(const void *x, int x_f32, int64_t T, int64_t K, float r,
+                             uint8_t *out, hipStream_t st) {
+    const int64_t chunks = T * K / 8;
+    if (chunks <= 0) return QI4_OK;
+    const unsigned g = (unsigned)(chunks / 256 + 1 < 65536 ? chunks / 256 + 1 : 65536);
+    if (x_f32) quantize_act_kernel<true><<<g, 256, 0, st>>>(x, T, K, r, out);
+    else quantize_act_kernel<false><<<g, 256, 0, st>>>(x, T, K, r, out);
+    return launch_status();
 }
 
 extern "C" int64_t qlinear_w4a8_workspace_bytes(int64_t T, int64_t K) {

@@ -484,13 +484,15 @@ int64_t prefill_deferred_capacity(const qi4_moe_desc *d, const PrefillTiles &mt)
     return a > b ? a : b;
 }
 
+// Workspace regions.  W4A8 (w4a8): h holds int8 rows and x8 the int8 input,
+// and every batch runs the decode GEMMs (no prefill regions).
 struct MoeWorkspace {
     int64_t ids, wts, sorted, offsets, p2s, active, h, y, x16, ex, h16, eh, tiles, ntiles, deferred,
-        total;
-    MoeWorkspace(const qi4_moe_desc *d, int64_t T) {
+        x8, total;
+    MoeWorkspace(const qi4_moe_desc *d, int64_t T, bool w4a8 = false) {
         const int64_t P = T * d->top_k;
         const int64_t R = P + (d->has_shared ? T : 0);
-        const bool pf = T >= kPrefillMinT;
+        const bool pf = !w4a8 && T >= kPrefillMinT;
         int64_t o = 0;
         ids = o;     o += align256(P * 4);
         wts = o;     o += align256(P * 4);
@@ -498,7 +500,7 @@ struct MoeWorkspace {
         offsets = o; o += align256((d->num_experts + 1) * 4);
         p2s = o;     o += align256(P * 4);
         active = o;  o += align256((d->num_experts + 1) * 4);
-        h = o;       o += align256(R * 2 * d->inter * 2);
+        h = o;       o += align256(w4a8 ? R * d->inter : R * 2 * d->inter * 2);
         y = o;       o += align256(R * d->hidden * 4);
         // prefill only: fp16 rows with exponents and the tile list
         x16 = o;     o += pf ? align256(T * d->hidden * 2) : 0;
@@ -509,6 +511,7 @@ struct MoeWorkspace {
         tiles = o;   o += pf ? align256((mt.big + 3 * mt.small) * 8) : 0;
         ntiles = o;  o += pf ? 256 : 0;
         deferred = o; o += pf ? align256(prefill_deferred_capacity(d, mt) * 16) : 0;
+        x8 = o;      o += w4a8 ? align256(T * d->hidden) : 0;
         total = o;
     }
 };
@@ -880,10 +883,18 @@ int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights
     return launch_combine(d, y, topk_weights, pair_to_sorted, T, out, as_stream(stream));
 }
 
-int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *router_logits,
+}  // extern "C"
+
+namespace {
+
+// Static int8 scale: finite, positive, with a finite float32 reciprocal.
+bool good_scale(float s) { return s > 0.f && s < INFINITY && 1.0f / s < INFINITY; }
+
+// moe_ffn_int4 and moe_ffn_w4a8 (scales given).
+int moe_ffn_impl(const qi4_moe_desc *d, const void *x, int64_t T, const float *router_logits,
                  int32_t *topk_ids, float *topk_weights, const void *w_gate_up, const void *w_down,
                  const void *shared_gate_up, const void *shared_down, void *out, void *workspace,
-                 int64_t ws_bytes, void *stream) {
+                 int64_t ws_bytes, void *stream, const float *w4a8_scales) {
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_T(T, d))) return rc;
@@ -897,7 +908,12 @@ int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
         !aligned(workspace, 256) || (shared_gate_up && !aligned(shared_gate_up, 16)) ||
         (shared_down && !aligned(shared_down, 16)))
         return QI4_ERR_SHAPE;
-    const MoeWorkspace L(d, T);
+    const bool w4a8 = w4a8_scales != nullptr;
+    if (w4a8) {
+        if (d->flags != 0) return QI4_ERR_UNSUPPORTED;   // 4-bit experts
+        if (!good_scale(w4a8_scales[0]) || !good_scale(w4a8_scales[1])) return QI4_ERR_SHAPE;
+    }
+    const MoeWorkspace L(d, T, w4a8);
     if (ws_bytes < L.total) return QI4_ERR_WORKSPACE;
     const int64_t H = d->hidden;
     if (overlaps(out, T * H * 2, x, T * H * 2) || overlaps(out, T * H * 2, workspace, ws_bytes) ||
@@ -924,10 +940,60 @@ int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
     } else if ((rc = launch_sort(ids, T * k, E, sorted, offsets, p2s, active, st))) {
         return rc;
     }
+    if (w4a8) {
+        // int8 x, then gate/up writing int8 h, then down on int8 h (decode GEMMs)
+        const int64_t R = T * k + (d->has_shared ? T : 0);
+        uint8_t *x8 = ws + L.x8;
+        if ((rc = launch_quantize_act(x, 0, T, H, 1.0f / w4a8_scales[0], x8, st))) return rc;
+        GemmArgs a = gate_up_args(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h);
+        a.a = x8;
+        a.a_bytes = T * H;
+        a.a_i8 = 1;
+        a.a_scale = w4a8_scales[0];
+        a.out_mode = OUT_I8;
+        a.out_r = 1.0f / w4a8_scales[1];
+        if ((rc = launch_qgemm(a, a.routed_slots + d->has_shared, T, st))) return rc;
+        GemmArgs b = down_args(d, h, T, offsets, active, w_down, shared_down, y);
+        b.a_bytes = R * d->inter;
+        b.a_i8 = 1;
+        b.a_scale = w4a8_scales[1];
+        b.P = 1;
+        if ((rc = launch_qgemm(b, b.routed_slots + d->has_shared, T, st))) return rc;
+        return launch_combine(d, y, wts, p2s, T, out, st);
+    }
     if ((rc = run_gate_up(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h, ws, st)))
         return rc;
     if ((rc = run_down(d, h, T, offsets, active, w_down, shared_down, y, ws, st))) return rc;
     return launch_combine(d, y, wts, p2s, T, out, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *router_logits,
+                 int32_t *topk_ids, float *topk_weights, const void *w_gate_up, const void *w_down,
+                 const void *shared_gate_up, const void *shared_down, void *out, void *workspace,
+                 int64_t ws_bytes, void *stream) {
+    return moe_ffn_impl(d, x, T, router_logits, topk_ids, topk_weights, w_gate_up, w_down,
+                        shared_gate_up, shared_down, out, workspace, ws_bytes, stream, nullptr);
+}
+
+int64_t moe_ffn_w4a8_workspace_bytes(const qi4_moe_desc *d, int64_t T) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    return MoeWorkspace(d, T, true).total;
+}
+
+int moe_ffn_w4a8(const qi4_moe_desc *d, const void *x, float x_scale, float h_scale, int64_t T,
+                 const float *router_logits, int32_t *topk_ids, float *topk_weights,
+                 const void *w_gate_up, const void *w_down, const void *shared_gate_up,
+                 const void *shared_down, void *out, void *workspace, int64_t ws_bytes,
+                 void *stream) {
+    const float sc[2] = {x_scale, h_scale};
+    return moe_ffn_impl(d, x, T, router_logits, topk_ids, topk_weights, w_gate_up, w_down,
+                        shared_gate_up, shared_down, out, workspace, ws_bytes, stream, sc);
 }
 
 }  // extern "C"

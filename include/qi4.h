@@ -311,6 +311,23 @@ int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T,
                  const void *shared_gate_up, const void *shared_down,
                  void *out, void *workspace, int64_t ws_bytes, void *stream);
 
+/* W4A8 MoE layer: moe_ffn_int4 with int8 activations in both projections (the
+ * FastDeploy page, x-techcon, applies W4A8 static quantization to MoE layers).
+ * Static scales, as in qlinear_w4a8: the layer input x is quantized with
+ * x_scale, and h = SiLU(g) * u (computed in float32 from the int8 x) with
+ * h_scale, a_h = clamp(rint(h * float32(1 / h_scale)), -127, 127), before the
+ * down projection; both scales finite, > 0, with finite float32 reciprocals
+ * (else QI4_ERR_SHAPE).  4-bit experts only (desc.flags 0, else
+ * QI4_ERR_UNSUPPORTED).  Every batch size runs the weight-streaming grouped
+ * GEMMs (int8 MFMA); workspace >= moe_ffn_w4a8_workspace_bytes(d, T).  Other
+ * arguments, outputs and errors as moe_ffn_int4. */
+int64_t moe_ffn_w4a8_workspace_bytes(const qi4_moe_desc *d, int64_t T);
+int moe_ffn_w4a8(const qi4_moe_desc *d, const void *x, float x_scale, float h_scale, int64_t T,
+                 const float *router_logits, int32_t *topk_ids, float *topk_weights,
+                 const void *w_gate_up, const void *w_down,
+                 const void *shared_gate_up, const void *shared_down,
+                 void *out, void *workspace, int64_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

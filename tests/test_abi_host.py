@@ -160,6 +160,19 @@ def test_moe_descriptor_errors(q):
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7000, 2048, 8, 128, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(4, 7168, 2048, 8, 128, 1, 0)), 1) == -2
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 2, 0)), 1) == -7
+    # W4A8 MoE: workspace size, scales, 8-bit experts refused
+    p = ctypes.c_void_p(0x1000)
+    assert L.moe_ffn_w4a8_workspace_bytes(ctypes.byref(ok), 32) > 0
+    assert L.moe_ffn_w4a8_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 96, 1, 0)), 1) == -4
+    xw, ow, ww = (ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
+                  ctypes.c_void_p(0x30000000))
+    for sx, sh_ in ((0.0, 0.1), (0.1, -1.0), (float("nan"), 0.1), (0.1, float("inf"))):
+        assert L.moe_ffn_w4a8(ctypes.byref(ok), xw, sx, sh_, 4, p, None, None, p, p, p, p, ow, ww,
+                              1 << 40, None) == -2
+    assert L.moe_ffn_w4a8(ctypes.byref(D(256, 7168, 2048, 8, 128, 1, 2)), xw, 0.1, 0.1, 4, p, None,
+                          None, p, p, p, p, ow, ww, 1 << 40, None) == -7
+    assert L.moe_ffn_w4a8(ctypes.byref(ok), xw, 0.1, 0.1, 4, p, None, None, p, p, p, p, ow, ww,
+                          256, None) == -5
     # flags: QI4_INT8 (8-bit experts) is accepted, other bits are not
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 1, 2)), 32) > 0
     assert L.moe_ffn_int4_workspace_bytes(ctypes.byref(D(256, 7168, 2048, 8, 128, 1, 1)), 1) == -7

@@ -102,3 +102,44 @@ def test_qlinear_w4a8_silu_mul(group):
     xh = oracle.dequant_act(oracle.quantize_act(x32, s), s)
     h, tol = oracle.gate_up_silu(xh, w["qweight"], w["scales"], w["zeros"], I, K, group=group)
     assert_within(to_f64(y), h, tol, f"w4a8 silu_mul group {group}")
+
+
+# ---- the W4A8 MoE layer ----------------------------------------------------------
+
+def _moe_w4a8_case(E, H, I, k, T, group, seed, h_scale, shared=True, ids_sel=None):
+    import torch
+    import ffn_int4_g128_amd as q
+    ex = workloads.moe_experts(seed, 0, E, H, I, 0.005, 0.02, group=group)
+    sh = workloads.moe_shared(seed, 0, H, I, 0.005, 0.02, group=group) if shared else None
+    xb = workloads.activations(seed + 1, T, T, H, "bf16")
+    x32 = workloads.bf16_bits_to_f32(xb)
+    sx = float(np.abs(x32).max()) / 127.0
+    logits = workloads.logits_normal(seed + 2, T, T, E)
+    mw = q.pack_moe(ex, sh, E, H, I, group=group)
+    out, ids, wts = q.moe_ffn_w4a8(bf16_dev(xb), mw, k, sx, h_scale, logits=to_dev(logits),
+                                   return_routing=True)
+    torch.cuda.synchronize()
+    oids, op = oracle.topk_softmax(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    sel = np.arange(T) if ids_sel is None else ids_sel
+    ref, tol = oracle.moe_w4a8(x32[sel], sx, h_scale, oids[sel], op[sel], ex, sh, H, I, E,
+                               group=group)
+    assert_within(to_f64(out)[sel], ref, tol, f"moe w4a8 E{E} H{H} I{I} T{T} group {group}")
+
+
+@pytest.mark.parametrize("group", [128, 64])
+@pytest.mark.parametrize("T", [1, 5, 33, 200])
+def test_moe_w4a8(group, T):
+    _moe_w4a8_case(8, 512, 256, 2, T, group, 110 + T, h_scale=0.05)
+
+
+def test_moe_w4a8_clamped_h_and_no_shared():
+    # a coarse-to-clamping h scale and no shared expert
+    _moe_w4a8_case(6, 256, 128, 3, 17, 128, 120, h_scale=0.004, shared=False)
+
+
+@pytest.mark.parametrize("T", [8, 32])
+def test_moe_w4a8_deepseek_expert_shape(T):
+    # hidden 7168, intermediate 2048, 16 experts, top-8; the oracle checks four tokens
+    _moe_w4a8_case(16, 7168, 2048, 8, T, 128, 130, h_scale=0.02,
+                   ids_sel=np.array([0, 1, T // 2, T - 1]))
