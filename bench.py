@@ -310,6 +310,50 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     }
 
 
+def run_w4a8_decode(q, torch, layers, c, Ts, steps, warmup, n_batches=4):
+    """The MoE decode step with W4A8 (moe_ffn_w4a8, one call per step: routing,
+    int8 x, gate/up writing int8 h, down, combine) on the same 4-bit layers.
+    Static scales: x_scale = max|x| / 127 of the batches; h_scale = max|h| / 127
+    of h from the bf16 path's gate/up on the first batch (calibration, outside
+    the timed region).  Fence-free events around each step."""
+    import ctypes
+    import workloads
+    k, E, H, I = c["top_k"], c["E"], c["H"], c["I"]
+    res = []
+    for T in Ts:
+        xs = [workloads.activations(c["seed"], 700 + 10 * b + T, T, H, "bf16") for b in range(n_batches)]
+        x_scale = max(float(abs(workloads.bf16_bits_to_f32(v)).max()) for v in xs) / 127.0
+        xt = [q_bf16(torch, v) for v in xs]
+        lg = [torch.from_numpy(workloads.logits_normal(c["seed"], 800 + 10 * b + T, T, E)).cuda()
+              for b in range(n_batches)]
+        ids, wts, sp, off, inv, act = q.moe_route_sort(lg[0], k)
+        h = q.moe_gate_up(xt[0], layers[0], k, sp, off, act).float()
+        h_scale = float((h[:, 0] + h[:, 1]).abs().max()) / 127.0
+        del h
+        ws = torch.empty(q.lib().moe_ffn_w4a8_workspace_bytes(ctypes.byref(layers[0].desc(k)), T),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+        def step(i):
+            b = (i // len(layers)) % n_batches
+            q.moe_ffn_w4a8(xt[b], layers[i % len(layers)], k, x_scale, h_scale, logits=lg[b],
+                           workspace=ws, out=out)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            step(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        med = us[len(us) // 2]
+        res.append({"T": T, "us_per_step": med, "tokens_per_s": T / (med * 1e-6),
+                    "x_scale": x_scale, "h_scale": h_scale})
+    return res
+
+
 def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
     """Prefill: T=2048 tokens of one layer, top-8 routing with Zipf(1.1) skew."""
     import workloads
@@ -612,6 +656,9 @@ def main():
     router = run_router(q, torch)
     log(f"router: {json.dumps(router)}")
 
+    w4a8 = run_w4a8_decode(q, torch, layers, c, [1, 8, 32], max(10, args.steps), args.warmup)
+    log(f"w4a8 decode: {json.dumps(w4a8)}")
+
     groups = None
     if not args.no_groups:
         groups = run_group_variants(q, torch, c, args.T, max(10, args.steps // 2), args.warmup)
@@ -655,6 +702,7 @@ def main():
         "dense": dense,
         "quantize": quant,
         "format_variants": groups,
+        "w4a8_moe_decode": w4a8,
         "router": router,
         "cpu_baseline": cpu,
     }
