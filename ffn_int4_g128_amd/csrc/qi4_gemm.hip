@@ -32,7 +32,12 @@ namespace qi4 {
 namespace {
 
 constexpr int kMaxWaves = 8;
-constexpr int kRedSlots = 16;   // (wave, m, nb) partial tiles the LDS buffer holds
+// (wave, m, nb) partial tiles the LDS reduction buffer holds: 16 (16 KiB), or
+// 32 for a quad of tiles over two M tiles (the only shape that needs more; the
+// others keep the smaller buffer so that LDS never caps their occupancy).
+template <int NB, int MT>
+constexpr int kRedSlotsFor = NB * MT >= 8 ? 32 : 16;
+__host__ __device__ constexpr int red_slots(int NB, int MT) { return NB * MT >= 8 ? 32 : 16; }
 
 // Part `part` of the exact split of v into bf16 terms v = hi + mid + lo.
 __device__ inline uint32_t split_part(float v, int part) {
@@ -80,7 +85,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI>)))
 qgemm_kernel(const GemmArgs args) {
     constexpr bool AF32 = AM == 1, AI8 = AM == 2;
-    __shared__ float red[kRedSlots * 256];
+    __shared__ float red[kRedSlotsFor<NB, MT> * 256];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -534,6 +539,9 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 //  * W waves split K; about ten 128-wide groups per wave for a single matrix;
 //  * a single matrix takes NB = 2 tiles per workgroup (the gate/up pair)
 //    unless it has fewer than 320 tiles and needs more workgroups (NB = 1);
+//    from 9 rows on, a whole quad (NB = 4) when that still gives >= 192
+//    workgroups: the activation fragments, re-read per block of tiles, are
+//    then shared by four tiles (5120 -> 13824 at T = 32: 30.4 -> 23.7 us);
 //    the grouped expert GEMMs take a whole quad (NB = 4), and the down
 //    projection two quads per workgroup (R = 2) once the grid is large;
 //  * one M tile per pass (16 activation rows), two for a single matrix with
@@ -566,10 +574,11 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
             W = 2;
         }
     } else {
+        if (max_slots > 8 && ceil_div(nt, 4) >= 192) NB = 4;
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
     }
-    while (W > 1 && W * MT * NB > kRedSlots) W /= 2;
+    while (W > 1 && W * MT * NB > red_slots(NB, MT)) W /= 2;
     GemmArgs a = args;
     a.blocks_per_wg = R;
     const int64_t gx = ceil_div(ceil_div(nt, NB), R);
@@ -581,6 +590,7 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
         if (NB == 2) return launch_cfg<2, 1, 2>(a, grid, threads, st);
         return launch_cfg<1, 1, 2>(a, grid, threads, st);
     }
+    if (NB == 4) return launch_cfg<4, 2, 2>(a, grid, threads, st);
     if (NB == 2) return launch_cfg<2, 2, 2>(a, grid, threads, st);
     return launch_cfg<1, 2, 2>(a, grid, threads, st);
 }
