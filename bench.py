@@ -123,6 +123,7 @@ def parse():
                     help="timed prefill steps (T=2048, Zipf-skewed routing); 0 to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-linear measurements")
+    ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 MoE decode step")
     ap.add_argument("--no-groups", action="store_true",
                     help="skip the decode step with other group sizes and 8-bit codes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -656,8 +657,10 @@ def main():
     router = run_router(q, torch)
     log(f"router: {json.dumps(router)}")
 
-    w4a8 = run_w4a8_decode(q, torch, layers, c, [1, 8, 32], max(10, args.steps), args.warmup)
-    log(f"w4a8 decode: {json.dumps(w4a8)}")
+    w4a8 = None
+    if not args.no_w4a8:
+        w4a8 = run_w4a8_decode(q, torch, layers, c, [1, 8, 32], max(10, args.steps), args.warmup)
+        log(f"w4a8 decode: {json.dumps(w4a8)}")
 
     groups = None
     if not args.no_groups:

@@ -75,14 +75,15 @@ struct Stage {
 
 
 // Waves per SIMD the register allocation must allow: the grouped gate/up GEMM
-// sits one register above the four-wave limit without this.
-template <int NB, int MT, int AM, int EPI>
-constexpr int kMinWaves = (AM == 0 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL) ? 4 : 1;
+// sits one register above the four-wave limit without this (with 64-wide
+// groups it needs more registers than four waves allow: no cap there).
+template <int NB, int MT, int AM, int EPI, int H>
+constexpr int kMinWaves = (AM == 0 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL && H == 1) ? 4 : 1;
 
 // H = 2: 64-wide groups, two scales and zeros per 128-wide block.
 template <int NB, int MT, int AM, int S, int EPI, int H>
 __global__ void __launch_bounds__(kMaxWaves * 64)
-__attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI>)))
+__attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI, H>)))
 qgemm_kernel(const GemmArgs args) {
     constexpr bool AF32 = AM == 1, AI8 = AM == 2;
     __shared__ float red[kRedSlotsFor<NB, MT> * 256];
@@ -354,7 +355,7 @@ qgemm_kernel(const GemmArgs args) {
                     static_cast<float *>(args.out)[dst * args.ldo + oc] = val;
                 } else if (args.out_mode == OUT_BF16) {
                     static_cast<uint16_t *>(args.out)[dst * args.ldo + oc] = (uint16_t)f32_to_bf16_rne(val);
-                } else if (args.out_mode == OUT_I8) {
+                } else if (AI8 && args.out_mode == OUT_I8) {   // (int8 rows only from W4A8)
                     // the activation quantizer's decision and byte order (k offset e
                     // of a dword at 2 (e & 3) + (e >> 2))
                     const float qv = fminf(fmaxf(rintf(val * args.out_r), -127.0f), 127.0f);
