@@ -74,11 +74,12 @@ struct Stage {
 
 
 
-// Waves per SIMD the register allocation must allow: the grouped gate/up GEMM
-// sits one register above the four-wave limit without this (with 64-wide
-// groups it needs more registers than four waves allow: no cap there).
+// Waves per SIMD the register allocation must allow: the grouped gate/up and
+// down GEMMs (a quad of tiles, one M tile) sit one register above the four-wave
+// limit without this (down at T = 32: +4.7 % GB/s with it).  With 64-wide
+// groups they need more registers than four waves allow: no cap there.
 template <int NB, int MT, int AM, int EPI, int H>
-constexpr int kMinWaves = (AM == 0 && MT == 1 && NB == 4 && EPI == QI4_EPI_SILU_MUL && H == 1) ? 4 : 1;
+constexpr int kMinWaves = (AM == 0 && MT == 1 && NB == 4 && H == 1) ? 4 : 1;
 
 // H = 2: 64-wide groups, two scales and zeros per 128-wide block.
 template <int NB, int MT, int AM, int S, int EPI, int H>

@@ -1,7 +1,7 @@
 """CPU check of the compiled kernels' resources (the compiler's
 kernel-resource-usage report written by the build): no kernel spills registers
-to scratch memory, and the decode step's dominant kernel, the grouped gate/up
-GEMM with SiLU*up, keeps four waves per SIMD."""
+to scratch memory, and the decode step's two grouped GEMMs (gate/up with SiLU*up,
+and down) keep four waves per SIMD."""
 import importlib
 import os
 
@@ -33,7 +33,10 @@ def test_no_kernel_spills(resources):
     assert not spills, spills
 
 
-def test_grouped_gate_up_keeps_four_waves(resources):
-    # qgemm_kernel<4 tiles, 1 M tile, bf16 activations, 2 stages, SiLU*up, 128-wide groups>
-    hot = [r for _, n, r in resources if "qgemm_kernelILi4ELi1ELi0ELi2ELi1ELi1E" in n]
+@pytest.mark.parametrize("epi", [1, 0])
+def test_grouped_decode_gemms_keep_four_waves(resources, epi):
+    # qgemm_kernel<4 tiles, 1 M tile, bf16 activations, 2 stages, SiLU*up (1) or
+    # none (0: down), 128-wide groups>
+    tag = f"qgemm_kernelILi4ELi1ELi0ELi2ELi{epi}ELi1E"
+    hot = [r for _, n, r in resources if tag in n]
     assert hot and all(r["occupancy"] >= 4 and r["vgprs"] <= 128 for r in hot), hot
