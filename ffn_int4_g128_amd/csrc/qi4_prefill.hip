@@ -245,6 +245,16 @@ struct Shape {
 };
 using BigShape = Shape<8, 4, 4, 2, 2>;
 using SmallShape = Shape<4, 2, 8, 4, 4>;
+// Small tiles of class C (<= 16 << C rows) stage only the 1 << C activation
+// subtiles they multiply, over 3 stages: 12 / 24 / 48 KiB of LDS for classes
+// 0 / 1 / 2 (class 0: 4 waves of 64 weight rows), so they leave room on each
+// CU for the big-tile kernel's workgroups beside them (measured: step 2.98 ->
+// 2.87-2.90 ms).  With 64-wide groups class 0 keeps the 4-stage 64-row shape
+// (the 4-wave one would spill).
+template <int C, int H>
+using SmallShapeC = std::conditional_t<
+    C == 0, std::conditional_t<H == 1, Shape<1, 4, 4, 3, 4>, SmallShape>,
+    std::conditional_t<C == 1, Shape<2, 2, 8, 3, 4>, Shape<4, 2, 8, 3, 4>>>;
 
 // s_waitcnt operand that waits until at most `vm` vector memory operations are
 // outstanding (expcnt and lgkmcnt left at their maxima).
@@ -557,9 +567,9 @@ prefill_big_kernel(const PrefillArgs args) {
 
 // Small tiles of class C: at most 16 << C rows, 1 << C subtiles multiplied.
 template <int EPI, int C, int H>
-__global__ void __launch_bounds__(SmallShape::W * 64, SmallShape::OCC)
+__global__ void __launch_bounds__((SmallShapeC<C, H>::W * 64), (SmallShapeC<C, H>::OCC))
 prefill_small_kernel(const PrefillArgs args) {
-    fast_pass<EPI, SmallShape, 1 << C, H>(args, args.tiles + args.max_big + C * args.max_small,
+    fast_pass<EPI, SmallShapeC<C, H>, 1 << C, H>(args, args.tiles + args.max_big + C * args.max_small,
                                       args.tile_count[1 + C]);
 }
 
@@ -661,7 +671,9 @@ int side_stream(SideStream **out) {
 
 template <int EPI, int H>
 int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsigned gs) {
-    const unsigned tb = BigShape::W * 64, ts = SmallShape::W * 64;
+    const unsigned tb = BigShape::W * 64;
+    const unsigned ts0 = SmallShapeC<0, H>::W * 64, ts1 = SmallShapeC<1, H>::W * 64,
+                   ts2 = SmallShapeC<2, H>::W * 64;
     SideStream *ss = nullptr;
     int rc;
     if ((rc = side_stream(&ss))) return rc;
@@ -670,9 +682,9 @@ int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsign
         if (hipEventRecord(ss->fork, st) != hipSuccess) return QI4_ERR_HIP;
         for (int i = 0; i < kSideStreams; ++i)
             if (hipStreamWaitEvent(ss->s[i], ss->fork, 0) != hipSuccess) return QI4_ERR_HIP;
-        prefill_small_kernel<EPI, 0, H><<<gs, ts, 0, ss->s[0]>>>(a);
-        prefill_small_kernel<EPI, 1, H><<<gs, ts, 0, ss->s[1]>>>(a);
-        prefill_small_kernel<EPI, 2, H><<<gs, ts, 0, ss->s[2]>>>(a);
+        prefill_small_kernel<EPI, 0, H><<<gs, ts0, 0, ss->s[0]>>>(a);
+        prefill_small_kernel<EPI, 1, H><<<gs, ts1, 0, ss->s[1]>>>(a);
+        prefill_small_kernel<EPI, 2, H><<<gs, ts2, 0, ss->s[2]>>>(a);
         if ((rc = launch_status())) return rc;
         prefill_big_kernel<EPI, H><<<gb, tb, 0, st>>>(a);
         if ((rc = launch_status())) return rc;
