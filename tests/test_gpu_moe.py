@@ -232,6 +232,22 @@ def test_dsv3_prefill_zipf(dsv3):
     _check_layer(c, ex, sh, mw, T, logits, x, "dsv3 prefill zipf", [0, 777, T - 1])
 
 
+@pytest.mark.parametrize("T", [32, 2048])
+def test_dsv3_layer_is_deterministic(dsv3, T):
+    """Two calls on the same inputs give bit-identical outputs on the decode path
+    and on the prefill path (every output element is reduced in a fixed order;
+    the prefill side streams change only when work runs, not what it adds)."""
+    import torch
+    import ffn_int4_g128_amd as q
+    c, ex, sh, mw = dsv3
+    logits = to_dev(workloads.logits_zipf(4, 9, T, c["E"], 1.1))
+    x = bf16_dev(workloads.activations(4, 8, T, c["H"], "bf16"))
+    a = q.moe_ffn(x, mw, c["top_k"], logits=logits)
+    b = q.moe_ffn(x, mw, c["top_k"], logits=logits)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("T,E,H,k", [(1, 256, 7168, 8), (32, 256, 7168, 8), (5, 64, 512, 4),
                                      (70, 300, 1024, 8), (2048, 256, 7168, 8), (3, 8, 32, 8)])
 def test_router_logits_and_topk(T, E, H, k):
