@@ -38,6 +38,8 @@ struct GemmArgs {
     const int32_t *offsets;       // moe: expert segment starts (E + 1)
     const int32_t *active;        // moe: [count, experts...]
     int routed_slots;             // moe: problem slots for routed experts in grid.y
+    int shared_rows;              // moe: slots of each shared-expert problem (those after
+                                  // the routed ones in grid.y); 0: all T in one
     int gather_tokens;            // moe: A rows are tokens (gate/up) rather than slots (down)
     // output
     void *out;

@@ -114,10 +114,14 @@ qgemm_kernel(const GemmArgs args) {
             if (args.gather_tokens) gather = args.sorted_pairs;
             else src0 = row0;
         } else {
+            // shared expert: problem py - routed_slots takes its shared_rows
+            // slots starting there
             w = args.w_shared;
-            row0 = args.T * args.top_k;
-            n = args.T;
-            src0 = args.gather_tokens ? 0 : row0;
+            const int64_t sr = args.shared_rows > 0 ? args.shared_rows : args.T;
+            const int64_t cs = (int64_t)(py - args.routed_slots) * sr;
+            row0 = args.T * args.top_k + cs;
+            n = args.T - cs < sr ? args.T - cs : sr;
+            src0 = args.gather_tokens ? cs : row0;
         }
     }
     if (n <= 0) return;

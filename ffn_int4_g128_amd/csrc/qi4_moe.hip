@@ -669,6 +669,17 @@ PrefillArgs prefill_args(const qi4_moe_desc *d, int64_t T, bool gate_up, const i
     return a;
 }
 
+// Problems of a grouped decode launch: the routed experts' slots, then the
+// shared expert split into one problem per M tile of slots (16 / P), so that
+// its workgroups stream its weights side by side, each in one pass (from the
+// cache after the first), rather than one workgroup per tile block looping
+// over the M tiles and finishing last.
+int grouped_problems(GemmArgs &a, const qi4_moe_desc *d, int64_t T) {
+    if (!d->has_shared) return a.routed_slots;
+    a.shared_rows = 16 / a.P;
+    return a.routed_slots + (int)ceil_div(T, (int64_t)a.shared_rows);
+}
+
 // The two projections of the expert FFN on either path.  `ws` is the moe_ffn_int4
 // workspace (only its prefill regions are used here).
 int run_gate_up(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *sorted,
@@ -677,7 +688,7 @@ int run_gate_up(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *
     int rc;
     if (T < kPrefillMinT) {
         GemmArgs a = gate_up_args(d, x, T, sorted, offsets, active, w_gu, sh_gu, h);
-        return launch_qgemm(a, a.routed_slots + d->has_shared, T, st);
+        return launch_qgemm(a, grouped_problems(a, d, T), T, st);
     }
     const MoeWorkspace L(d, T);
     uint16_t *x16 = reinterpret_cast<uint16_t *>(ws + L.x16);
@@ -698,7 +709,7 @@ int run_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *off
     int rc;
     if (T < kPrefillMinT) {
         GemmArgs a = down_args(d, h, T, offsets, active, w_dn, sh_dn, y);
-        return launch_qgemm(a, a.routed_slots + d->has_shared, T, st);
+        return launch_qgemm(a, grouped_problems(a, d, T), T, st);
     }
     const MoeWorkspace L(d, T);
     const int64_t R = T * d->top_k + (d->has_shared ? T : 0);
@@ -952,13 +963,13 @@ int moe_ffn_impl(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
         a.a_scale = w4a8_scales[0];
         a.out_mode = OUT_I8;
         a.out_r = 1.0f / w4a8_scales[1];
-        if ((rc = launch_qgemm(a, a.routed_slots + d->has_shared, T, st))) return rc;
+        if ((rc = launch_qgemm(a, grouped_problems(a, d, T), T, st))) return rc;
         GemmArgs b = down_args(d, h, T, offsets, active, w_down, shared_down, y);
         b.a_bytes = R * d->inter;
         b.a_i8 = 1;
         b.a_scale = w4a8_scales[1];
         b.P = 1;
-        if ((rc = launch_qgemm(b, b.routed_slots + d->has_shared, T, st))) return rc;
+        if ((rc = launch_qgemm(b, grouped_problems(b, d, T), T, st))) return rc;
         return launch_combine(d, y, wts, p2s, T, out, st);
     }
     if ((rc = run_gate_up(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h, ws, st)))
