@@ -616,6 +616,27 @@ def cpu_baseline(c, T, target_s):
             "seconds": dt}
 
 
+def run_copy(torch, mib=1024, reps=20):
+    """Context for the HBM roofline: a plain device-to-device copy (torch's copy
+    kernel, 1 GiB read + 1 GiB written per launch), bytes moved / time."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del a, b
+    return {"bytes_per_launch": 2 * n, "us": us, "GBps": 2 * n / (us * 1e-6) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -631,6 +652,8 @@ def main():
     layers = [build_layer(c, l, q, torch) for l in range(args.layers)]
     log(f"  done in {time.perf_counter() - t0:.1f} s")
 
+    copy = run_copy(torch)
+    log(f"copy: {json.dumps(copy)}")
     main_r = run_batch(q, torch, layers, c, args.T, args.steps, args.warmup)
     log(f"T={args.T}: {json.dumps(main_r)}")
     sweep = []
@@ -695,7 +718,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "moe grouped gate/up + SiLU (qgemm_kernel)",
                      "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gu_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
-                     "launch_us": main_r["gate_up_us"], "bytes_per_launch": main_r["gate_up_bytes"]},
+                     "launch_us": main_r["gate_up_us"], "bytes_per_launch": main_r["gate_up_bytes"],
+                     "copy_GBps": copy["GBps"], "frac_of_copy": gu_gbps / copy["GBps"]},
         "step_GBps": main_r["step_GBps"],
         "experts_touched_mean": main_r["experts_touched_mean"],
         "down_GBps": main_r["down_GBps"],
