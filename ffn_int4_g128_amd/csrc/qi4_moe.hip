@@ -7,9 +7,12 @@
 // expert that always runs (--cuda_se) (fastllm README, "other parameters").
 // Here the routed experts a batch touches are found on the device (sort), and
 // one launch per projection covers all of them: grid.y enumerates the touched
-// experts plus the shared one, grid.x the 16-row tiles of each expert's matrix.
+// experts, then the shared one split by M tiles of slots, grid.x the 16-row
+// tiles of each expert's matrix.
 // Only touched experts' weights are read.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "qi4_gemm.h"
 #include "qi4_host.h"
@@ -365,25 +368,27 @@ sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
 // waves, wave t routing token t, the ids passed through LDS.  Saves one launch
 // (measured 1.4 us of a 72 us step at T = 1); from two tokens per wave on, the
 // serialized routing eats the gain.
+// W waves (4 up to four tokens, else 16): fewer waves take less to zero the
+// tables and to pass the barriers.
 constexpr int kFusedWaves = 16;
 constexpr int kFusedPairs = kFusedWaves * kMaxTopK;
-template <int VPL>
-__global__ void __launch_bounds__(kFusedWaves * 64)
+template <int VPL, int W>
+__global__ void __launch_bounds__(W * 64)
 route_sort_kernel(const float *__restrict__ logits, int64_t T, int E, int k, int nbits,
                   int32_t *__restrict__ ids, float *__restrict__ wts,
                   int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ offsets,
                   int32_t *__restrict__ pair_to_sorted, int32_t *__restrict__ active) {
-    __shared__ int cnt[kFusedWaves][kMaxExperts];
+    __shared__ int cnt[W][kMaxExperts];
     __shared__ int off_s[kMaxExperts + 1];
     __shared__ int tot_s[kMaxExperts];
-    __shared__ int32_t ids_s[kFusedPairs];
+    __shared__ int32_t ids_s[W * kMaxTopK];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave < T)   // whole waves: fully active
         route_token<VPL>(logits, wave, E, k, lane, ids, wts, ids_s);
     __syncthreads();
-    sort_body<kFusedWaves>(ids_s, T * k, E, nbits, sorted_pairs, offsets, pair_to_sorted, active,
-                           cnt, off_s, tot_s);
+    sort_body<W>(ids_s, T * k, E, nbits, sorted_pairs, offsets, pair_to_sorted, active, cnt, off_s,
+                 tot_s);
 }
 
 // ---- combine: fixed order, slots then the shared expert -------------------------------
@@ -558,12 +563,17 @@ int launch_route_sort(const float *logits, int64_t T, int E, int k, int32_t *ids
         return launch_sort(ids, T * k, E, sorted, offsets, p2s, active, st);
     }
     const int vpl = (E + 63) / 64, nb = bits_for(E);
-    const unsigned tb = kFusedWaves * 64;
-    if (vpl <= 1) route_sort_kernel<1><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-    else if (vpl <= 2) route_sort_kernel<2><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-    else if (vpl <= 4) route_sort_kernel<4><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-    else if (vpl <= 8) route_sort_kernel<8><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-    else route_sort_kernel<16><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+    auto go = [&](auto w) {
+        constexpr int W = decltype(w)::value;
+        const unsigned tb = W * 64;
+        if (vpl <= 1) route_sort_kernel<1, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+        else if (vpl <= 2) route_sort_kernel<2, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+        else if (vpl <= 4) route_sort_kernel<4, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+        else if (vpl <= 8) route_sort_kernel<8, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+        else route_sort_kernel<16, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+    };
+    if (T <= 4) go(std::integral_constant<int, 4>());
+    else go(std::integral_constant<int, kFusedWaves>());
     return launch_status();
 }
 

@@ -63,12 +63,14 @@ def test_sort_tokens_bit_exact(T, E, k):
     assert a[0] == len(nonempty) and np.array_equal(a[1:1 + a[0]], nonempty)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (8, 256, 8), (16, 256, 8), (17, 256, 8),
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (4, 256, 8), (5, 256, 8), (4, 1024, 32),
+                                   (8, 256, 8), (16, 256, 8), (17, 256, 8),
                                    (32, 256, 8), (2048, 256, 8), (3, 1000, 32), (9, 8, 8),
                                    (16, 1024, 32), (17, 1024, 32), (70, 64, 1), (1, 1, 1)])
 def test_route_sort_bit_exact(T, E, k):
-    """The routing + permutation call (one fused workgroup up to 16 tokens,
-    else the two kernels) gives the oracle's ids and permutation bit for bit."""
+    """The routing + permutation call (one fused workgroup of 4 waves up to 4
+    tokens, of 16 up to 16 tokens, else the two kernels) gives the oracle's ids
+    and permutation bit for bit."""
     import ffn_int4_g128_amd as q
     logits = workloads.logits_normal(63, E + k, T, E)
     ids, wts, sp, off, inv, act = q.moe_route_sort(to_dev(logits), k)
