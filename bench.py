@@ -395,13 +395,14 @@ def _dense_pack(q, torch, w, flags=0):
     return q.pack(dev(w["qweight"]), dev(w["scales"]), dev(w["zeros"]), w["N"], w["K"], flags)
 
 
-def run_dense(q, torch, reps=20):
+def run_dense(q, torch, reps=100):
     """Dense int4-g128 linears, cold cache: before each timed rep 1 GiB is read
     (outside the event pair), so no weight is served from the 256 MB last-level
     cache.  A read, not a write: a 1 GiB write would leave that cache full of
     dirty lines whose write-back the next kernel's reads would pay for.  The
     events are enqueued while the flush runs, so the host adds no gaps.  Median
-    over reps.  Workloads: the Llama-7B-shaped decode stack at T=1 (QKV, O,
+    over reps, with the 10th and 90th percentiles, and beside it a warm number
+    (50 launches back to back, no flush, mean).  Workloads: the Llama-7B-shaped decode stack at T=1 (QKV, O,
     gate/up with SiLU*up, down: four launches back to back, and the same four
     replayed from a captured HIP graph) and the skinny sweep (5120->13824 and
     13824->5120 at T = 1..32, one launch per event pair).  The event pair is a
@@ -412,7 +413,11 @@ def run_dense(q, torch, reps=20):
     rd = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     acc = torch.empty((), dtype=torch.float32, device="cuda")
 
+    spread = {}
+
     def timed(fn):
+        """Cold median in seconds; its p10 / p90 and the warm mean (us) are kept
+        in spread[fn] for the caller's record."""
         ts = []
         for r in range(reps + 3):
             torch.sum(rd, dim=0, out=acc)
@@ -423,6 +428,17 @@ def run_dense(q, torch, reps=20):
             torch.cuda.synchronize()
             if r >= 3:
                 ts.append(e0.elapsed_time(e1) * 1e-3)
+        ts.sort()
+        w0, w1 = TimingEvent(), TimingEvent()
+        fn()
+        torch.cuda.synchronize()
+        w0.record()
+        for _ in range(50):
+            fn()
+        w1.record()
+        torch.cuda.synchronize()
+        spread[fn] = {"p10_us": ts[len(ts) // 10] * 1e6, "p90_us": ts[(9 * len(ts)) // 10] * 1e6,
+                      "warm_us": w0.elapsed_time(w1) * 1e3 / 50}
         return statistics.median(ts)
 
     c1 = workloads.LLAMA7B_STACK
@@ -446,20 +462,22 @@ def run_dense(q, torch, reps=20):
     with torch.cuda.graph(graph):
         stack()
     t_eager, t_graph = timed(stack), timed(graph.replay)
+    eager_spread, graph_spread = spread.pop(stack), spread.pop(graph.replay)
     stack_bytes, per = 0.0, []
     for (name, N, K, n_out, *_), f in zip(lin, calls):
         b = N * K * per_w + K * 2 + n_out * 2
         stack_bytes += b
         t = timed(f)
         per.append({"linear": name, "N": N, "K": K, "us": t * 1e6,
-                    "GBps": b / t / 1e9})
+                    "GBps": b / t / 1e9, **spread.pop(f)})
     del graph, lin, calls
     stack = {"workload": "llama7b_decode_stack_t1", "bytes": stack_bytes,
              "eager_us": t_eager * 1e6, "eager_tokens_per_s": 1.0 / t_eager,
              "eager_GBps": stack_bytes / t_eager / 1e9,
              "graph_us": t_graph * 1e6, "graph_tokens_per_s": 1.0 / t_graph,
              "graph_GBps": stack_bytes / t_graph / 1e9,
-             "graph_hbm_frac": stack_bytes / t_graph / 1e9 / HBM_PEAK_GBPS, "linears": per}
+             "graph_hbm_frac": stack_bytes / t_graph / 1e9 / HBM_PEAK_GBPS,
+             "eager_spread": eager_spread, "graph_spread": graph_spread, "linears": per}
 
     c2 = workloads.SKINNY_SWEEP
     sweep = []
@@ -470,11 +488,12 @@ def run_dense(q, torch, reps=20):
             x = q_bf16(torch, workloads.activations(c2["seed"], 20 + 10 * i + T, T, K, "bf16",
                                                     c2["x_scale"]))
             y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-            t = timed(lambda: q.qlinear(x, pw, N, out=y))
+            fn = lambda: q.qlinear(x, pw, N, out=y)
+            t = timed(fn)
             b = N * K * per_w + T * K * 2 + T * N * 2
             sweep.append({"K": K, "N": N, "T": T, "us": t * 1e6,
                           "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
-                          "tokens_per_s": T / t})
+                          "tokens_per_s": T / t, **spread.pop(fn)})
         del pw
     # the same shapes with 8-bit codes (groups of 128), quantized on the GPU
     # from N(0, 0.02^2) bf16 weights
@@ -491,11 +510,12 @@ def run_dense(q, torch, reps=20):
             x = q_bf16(torch, workloads.activations(c2["seed"], 20 + 10 * i + T, T, K, "bf16",
                                                     c2["x_scale"]))
             y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-            t = timed(lambda: q.qlinear(x, pw, N, flags=q.QI4_INT8, out=y))
+            fn = lambda: q.qlinear(x, pw, N, flags=q.QI4_INT8, out=y)
+            t = timed(fn)
             b = N * K * per_w8 + T * K * 2 + T * N * 2
             sweep8.append({"K": K, "N": N, "T": T, "us": t * 1e6,
                            "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
-                           "tokens_per_s": T / t})
+                           "tokens_per_s": T / t, **spread.pop(fn)})
         del pw
     # W4A8: the 4-bit matrices of the sweep with int8 activations (static
     # scale max|x| / 127); the time includes the activation-quantizing launch
@@ -510,16 +530,18 @@ def run_dense(q, torch, reps=20):
             y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
             ws = torch.empty(q.lib().qlinear_w4a8_workspace_bytes(T, K), dtype=torch.uint8,
                              device="cuda")
-            t = timed(lambda: q.qlinear_w4a8(x, sx, pw, N, out=y, workspace=ws))
+            fn = lambda: q.qlinear_w4a8(x, sx, pw, N, out=y, workspace=ws)
+            t = timed(fn)
             b = N * K * per_w + T * K * 2 + T * N * 2
             sweep_w4a8.append({"K": K, "N": N, "T": T, "us": t * 1e6,
                                "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
-                               "tokens_per_s": T / t})
+                               "tokens_per_s": T / t, **spread.pop(fn)})
         del pw
     del rd
     torch.cuda.empty_cache()
     return {"protocol": "1 GiB read before each rep (outside the events); median of "
-                        f"{reps} reps", "llama7b_stack": stack, "skinny_sweep": sweep,
+                        f"{reps} reps (us), with p10_us / p90_us; warm_us: mean of 50 launches "
+                        "back to back without the flush", "llama7b_stack": stack, "skinny_sweep": sweep,
             "skinny_sweep_int8": sweep8, "skinny_sweep_w4a8": sweep_w4a8}
 
 
