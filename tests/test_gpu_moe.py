@@ -96,7 +96,12 @@ def _small_layer(E, H, I, seed, shared=True):
                                               (33, 16, 384, 256, 4, True), (17, 6, 128, 128, 6, False),
                                               (64, 4, 256, 128, 1, True), (127, 8, 256, 128, 2, True),
                                               (128, 8, 256, 128, 2, True), (300, 16, 384, 256, 4, True),
-                                              (200, 6, 128, 384, 6, False), (513, 32, 512, 128, 8, True)])
+                                              (200, 6, 128, 384, 6, False), (513, 32, 512, 128, 8, True),
+                                              # the shared expert's problems per decode launch change
+                                              # at 8 / 9 tokens (down, 8-slot M tiles) and at 16 / 17
+                                              # (gate/up, 16 slots)
+                                              (8, 8, 256, 128, 2, True), (9, 8, 256, 128, 2, True),
+                                              (16, 8, 256, 128, 2, True), (17, 8, 256, 128, 2, True)])
 def test_moe_small_layers(T, E, H, I, k, shared):
     import torch
     import ffn_int4_g128_amd as q
