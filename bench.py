@@ -662,8 +662,8 @@ def run_copy(torch, mib=1024, reps=20):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
-              "multi-GPU path; see DESIGN.md for how the layer would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library has "
+              "no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
     import ffn_int4_g128_amd as q
