@@ -7,7 +7,9 @@ page passages they follow).  Only ``tests/``, ``__graft_entry__.smoke()`` and
 with the GPU library and never imports it.
 
 This module is a thin ctypes shim: it widens activations to float64, checks
-shapes and calls the C functions.  All arithmetic of the method is in C.
+shapes and calls the C functions, which hold the method's arithmetic.  One step
+is a library primitive instead: the router projection (``router_logits``) is a
+numpy fp64 matrix product.
 Every exported function is pinned by tests in ``tests/test_oracle_*.py``; a
 function whose pin is missing would say "parity unpinned" here (none does).
 """
@@ -78,7 +80,7 @@ def lib():
                   "qi4o_topk_softmax", "qi4o_sort", "qi4o_moe", "qi4o_quantize",
                   "qi4o_quantize_act", "qi4o_dequant_act", "qi4o_moe_w4a8"):
             getattr(L, f).restype = ctypes.c_int
-        if L.qi4o_abi_version() != 4:
+        if L.qi4o_abi_version() != 5:
             raise RuntimeError("stale oracle library: rebuild it (oracle.build())")
         _lib = L
     return _lib

@@ -52,7 +52,7 @@
 #include <string.h>
 #include <math.h>
 
-#define ORACLE_ABI 4
+#define ORACLE_ABI 5
 int qi4o_abi_version(void) { return ORACLE_ABI; }
 
 /* ---- IEEE binary16 <-> double ----------------------------------------- */
@@ -223,17 +223,50 @@ int qi4o_dequant_act(const int8_t *a, int64_t n, float s_x, double *xhat)
 /* SiLU(v) = v / (1 + exp(-v)), written the plain way in double. */
 double qi4o_silu(double v) { return v / (1.0 + exp(-v)); }
 
-/* Derivative of SiLU, used only for the first-order tolerance of h. */
-static double silu_prime(double v)
+/* SiLU has one minimum, at the root g* of its derivative
+   sigma(g) * (1 + g * (1 - sigma(g))) (about -1.2785): it decreases before g* and
+   increases after.  Found once by bisection on [-2, -1], where the derivative
+   changes sign. */
+static double silu_argmin(void)
 {
-    double sg = 1.0 / (1.0 + exp(-v));
-    return sg * (1.0 + v * (1.0 - sg));
+    static double gstar = 0.0;
+    if (gstar == 0.0) {
+        double lo = -2.0, hi = -1.0;
+        for (int it = 0; it < 200 && hi - lo > 0.0; it++) {
+            double mid = 0.5 * (lo + hi);
+            if (mid == lo || mid == hi) break;
+            double sg = 1.0 / (1.0 + exp(-mid));
+            double d = sg * (1.0 + mid * (1.0 - sg));
+            if (d < 0.0) lo = mid; else hi = mid;
+        }
+        gstar = 0.5 * (lo + hi);
+    }
+    return gstar;
+}
+
+/* The largest |SiLU(g + d) - SiLU(g)| over |d| <= a.  SiLU is unimodal, so on
+   [g - a, g + a] its extreme values sit at the two ends or at its minimum g*. */
+static double silu_dev(double g, double a)
+{
+    double s0 = qi4o_silu(g);
+    double d1 = fabs(qi4o_silu(g + a) - s0), d2 = fabs(qi4o_silu(g - a) - s0);
+    double d = d1 > d2 ? d1 : d2;
+    double gs = silu_argmin();
+    if (g - a <= gs && gs <= g + a) {
+        double d3 = fabs(s0 - qi4o_silu(gs));
+        if (d3 > d) d = d3;
+    }
+    return d;
 }
 
 /* h[t][i] = SiLU(g[t][i]) * u[t][i] where [g; u] = x . W_gu^T, W_gu rows
-   [0,I) = gate, [I,2I) = up (R8).  tol_h (may be NULL) is the first-order
-   propagation of the per-linear tolerance c*S through SiLU(g)*u:
-   tol_h = c * (|SiLU'(g)| * |u| * S_g + |SiLU(g)| * S_u). */
+   [0,I) = gate, [I,2I) = up (R8).  tol_h (may be NULL) bounds |h' - h| for any
+   g' = g + dg, u' = u + du with |dg| <= c*S_g and |du| <= c*S_u (the per-linear
+   tolerance of each projection, S = sum|w*x|):
+     h' - h = (SiLU(g') - SiLU(g)) * u' + SiLU(g) * du, so
+     tol_h = D * (|u| + c*S_u) + |SiLU(g)| * c*S_u
+   with D the largest |SiLU(g + d) - SiLU(g)| over |d| <= c*S_g (R14).  As c
+   shrinks this is c * (|SiLU'(g)| * |u| * S_g + |SiLU(g)| * S_u). */
 int qi4o_gate_up_silu(const double *x, int64_t T, int64_t K,
                       const uint8_t *qweight, const uint16_t *scales, const uint8_t *zeros,
                       int64_t I, int64_t G, int bits, double c, double *h, double *tol_h,
@@ -250,9 +283,10 @@ int qi4o_gate_up_silu(const double *x, int64_t T, int64_t K,
             for (int64_t i = 0; i < I; i++) {
                 double g = gu[t * N + i], u = gu[t * N + I + i];
                 h[t * I + i] = qi4o_silu(g) * u;
-                if (tol_h)
-                    tol_h[t * I + i] = c * (fabs(silu_prime(g)) * fabs(u) * S[t * N + i] +
-                                            fabs(qi4o_silu(g)) * S[t * N + I + i]);
+                if (tol_h) {
+                    double ag = c * S[t * N + i], au = c * S[t * N + I + i];
+                    tol_h[t * I + i] = silu_dev(g, ag) * (fabs(u) + au) + fabs(qi4o_silu(g)) * au;
+                }
             }
     }
     free(gu); free(S);
@@ -322,8 +356,9 @@ int qi4o_sort(const int32_t *ids, int64_t T, int k, int64_t E,
 /* ---- the MoE expert FFN -------------------------------------------------- */
 
 /* One expert on one token: h = SiLU(W_g x) * (W_u x), y = W_d h, in double.
-   A (may be NULL) receives the first-order tolerance of y:
-   A[n] = sum_i |W_d[n][i]| * (c*|h_i| + tol_h[i]). */
+   A (may be NULL) bounds |y' - y| when h is off by at most tol_h and the down
+   projection adds its own error of at most c * sum|W_d * h'| (h' the h it was
+   given): A[n] = sum_i |W_d[n][i]| * (tol_h[i] + c * (|h_i| + tol_h[i])). */
 static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t Ggu, int64_t Gdn,
                       int bits, double c, const uint8_t *gq, const uint16_t *gs, const uint8_t *gz,
                       const uint8_t *dq, const uint16_t *ds, const uint8_t *dz,
@@ -337,7 +372,7 @@ static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t Ggu, int64
         for (int64_t i = 0; i < I; i++) {
             double w = w_at(dq, ds, dz, I, Gdn, bits, n, i);
             acc += w * h[i];
-            a += fabs(w) * (c * fabs(h[i]) + tol_h[i]);
+            a += fabs(w) * (tol_h[i] + c * (fabs(h[i]) + tol_h[i]));
         }
         y[n] = acc;
         if (A) A[n] = a;
@@ -351,9 +386,10 @@ static int expert_ffn(const double *xt, int64_t H, int64_t I, int64_t Ggu, int64
  * block dn_*[e] (H x I, groups along I); G = 0 means one group per row of each
  * matrix (H for gate/up, I for down: the plain, per-channel int4 that the
  * fastllm README names beside the grouped int4g).  The shared expert (sh_*) is skipped
- * when sh_gu_q is NULL.  tol (may be NULL) is the first-order tolerance
- * sum_j p_j*A_{e_j} + A_shared + eps_p * sum_j |y_{e_j}| with c the per-linear
- * relative factor and eps_p a bound on the error of the combine weights.
+ * when sh_gu_q is NULL.  tol (may be NULL) bounds the output's error when every
+ * linear is off by at most c times its sum|w*x| and every combine weight by at
+ * most eps_p: sum_j (|p_j|*A_{e_j} + eps_p*(|y_{e_j}| + A_{e_j})) + A_shared
+ * (reading R14).
  * Tokens are processed one by one; threads split output rows of each linear. */
 int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
              const int32_t *ids, const double *p,
@@ -391,7 +427,7 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
                             y, A, h, th, threads);
             for (int64_t n = 0; n < H; n++) {
                 ot[n] += pj * y[n];
-                if (tt) tt[n] += pj * A[n] + eps_p * fabs(y[n]);
+                if (tt) tt[n] += fabs(pj) * A[n] + eps_p * (fabs(y[n]) + A[n]);
             }
         }
         if (rc == 0 && sh_gu_q) {
@@ -414,9 +450,9 @@ int qi4o_moe(const double *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
    -127, 127) with r_h = float32(1 / s_h), hhat = a_h * s_h; y = hhat . W_d^T.
    A[n] = sum_k |W_d[n][k] * hhat_k| (for the per-linear factor c) and
    B[n] = s_h * sum_k |W_d[n][k]| over the k whose decision is not certain: the
-   range h +- amb_k (amb = the first-order effect of a relative error c_amb in g
-   and u, plus the float32 roundings of h and of h * r_h) maps to two different
-   clamped codes. */
+   range h +- amb_k (amb = the bound on |h' - h| of qi4o_gate_up_silu for a
+   relative error c_amb in g and u, plus the float32 roundings of h and of
+   h * r_h) maps to two different clamped codes. */
 static int expert_ffn_w4a8(const double *xhat, int64_t H, int64_t I, int64_t Ggu, int64_t Gdn,
                            float s_h, double c_amb, const uint8_t *gq, const uint16_t *gs,
                            const uint8_t *gz, const uint8_t *dq, const uint16_t *ds,
@@ -457,10 +493,11 @@ static int expert_ffn_w4a8(const double *xhat, int64_t H, int64_t I, int64_t Ggu
 
 /* out[t] = sum_j p[t][j] * FFN8_{ids[t][j]}(xhat_t) + FFN8_shared(xhat_t) with
    xhat = the int8 activations of x (scale s_x, qi4o_quantize_act) times s_x and
-   FFN8 the expert above; 4-bit weights as in qi4o_moe.  tol = sum_j p_j
-   (c A_j + B_j) + c A_sh + B_sh + eps_p sum_j |y_j|: the per-linear factor on the
-   down projection and the uncertain h decisions (the gate/up error enters only
-   through those, bounded by c_amb). */
+   FFN8 the expert above; 4-bit weights as in qi4o_moe.  Per expert the error of
+   y is at most D = B + c * (A + B): the uncertain h decisions (one step each,
+   B; the gate/up error enters only through those, bounded by c_amb) and the
+   down projection's own c * sum|W_d * h'| for h' within one step of hhat on the
+   uncertain decisions.  tol = sum_j (|p_j| D_j + eps_p (|y_j| + D_j)) + D_sh. */
 int qi4o_moe_w4a8(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
                   const int32_t *ids, const double *p,
                   const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *gu_z,
@@ -502,8 +539,9 @@ int qi4o_moe_w4a8(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, in
                                  dn_q + e * dn_qb, dn_s + e * dn_mb, dn_z + e * dn_mb,
                                  y, A, B, h, amb, hq, un, threads);
             for (int64_t n = 0; n < H; n++) {
+                double D = B[n] + c * (A[n] + B[n]);
                 ot[n] += pj * y[n];
-                if (tt) tt[n] += pj * (c * A[n] + B[n]) + eps_p * fabs(y[n]);
+                if (tt) tt[n] += fabs(pj) * D + eps_p * (fabs(y[n]) + D);
             }
         }
         if (rc == 0 && sh_gu_q) {
@@ -511,7 +549,7 @@ int qi4o_moe_w4a8(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, in
                                  sh_dn_q, sh_dn_s, sh_dn_z, y, A, B, h, amb, hq, un, threads);
             for (int64_t n = 0; n < H; n++) {
                 ot[n] += y[n];
-                if (tt) tt[n] += c * A[n] + B[n];
+                if (tt) tt[n] += B[n] + c * (A[n] + B[n]);
             }
         }
     }
