@@ -150,17 +150,116 @@ __device__ inline i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Four codes pairs of one dword -> four dwords of bf16 pairs holding 128 + q.
-// bf16 0x4300 is 128.0 and its last mantissa bit weighs 1, so OR-ing a code
-// q <= 15 into the low mantissa bits gives exactly 128 + q.
-__device__ inline uint4 unpack_codes_bf16(uint32_t d) {
-    const uint32_t m = 0x000F000Fu, magic = 0x43004300u;
-    uint4 r;
-    r.x = (d & m) | magic;
-    r.y = ((d >> 4) & m) | magic;
-    r.z = ((d >> 8) & m) | magic;
-    r.w = ((d >> 12) & m) | magic;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// (a & m) | c in one VALU instruction (m in a scalar register, c in a vector
+// register: a three-operand VALU op takes no literal here).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
     return r;
+}
+
+// fp16 1024 in both halves, produced opaquely so that it stays in one vector
+// register instead of being rematerialized at every use.
+__device__ inline uint32_t f16_magic_pair() {
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+    return magic;
+}
+
+// Exact fp16 operands q - zero of the 8 codes of one packed dword, with the
+// elements at k-offsets 2, 3, 6 and 7 sixteen times larger.  Masking a code in
+// place under fp16 1024 (whose last mantissa bit weighs 1) gives 1024 + q for
+// codes at bits 0..3 of a half and 1024 + 16 q for codes at bits 4..7; adding
+// -(1024 + zero) or -(1024 + 16 zero) (packed fp16, exact) leaves q - zero or
+// 16 (q - zero).  negz / negz16 hold those negated constants in both halves.
+// One shift, four and-or and four packed adds per 8 codes.
+__device__ inline uint4 codes_minus_zero_f16(uint32_t d, uint32_t negz, uint32_t negz16,
+                                             uint32_t magic) {
+    const f16x2 nz = __builtin_bit_cast(f16x2, negz), nz16 = __builtin_bit_cast(f16x2, negz16);
+    const uint32_t t = d >> 8;
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(d, 0x000F000Fu, magic)) + nz);
+    r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(d, 0x00F000F0u, magic)) + nz16);
+    r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, 0x000F000Fu, magic)) + nz);
+    r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, and_or(t, 0x00F000F0u, magic)) + nz16);
+    return r;
+}
+
+// fp16 -(1024 + zero) and -(1024 + 16 zero) in both halves of a dword.
+__device__ inline uint32_t f16_negz(uint32_t z) { return (0xE400u | z) * 0x00010001u; }
+__device__ inline uint32_t f16_negz16(uint32_t z) { return (0xE400u | (z << 4)) * 0x00010001u; }
+
+// ---- bf16 activations as exact fp16 operands ---------------------------------
+//
+// A bf16 value 2^(e-127) (1 + m/128) (exponent field e, 7 mantissa bits m) is
+// an fp16 value times a power of two as long as it lands in fp16's range.  One
+// power of two per (operand row, 128-wide block) is taken from the largest
+// exponent field E of the row's 128 values: c = max(E - 29, 0), and the fp16
+// operand is x * 2^(112 - c) (x * 2^(108 - c) at k-offsets 2, 3, 6, 7, whose
+// weights are 16x).  Its bits are built from the bf16 bits with integer ops:
+// (|bits| - (c << 7)) saturated at 0, shifted left by 3, with the sign put
+// back.  Exponent fields e > c give exact fp16 normals (field e - c <= 29);
+// e == c reads as an fp16 subnormal and e < c saturates to 0, an error below
+// 2^-15 in the scaled units, i.e. below 2^-29 of the block's largest value.
+// The product of the block's integer sums with 2^(c - 112) undoes the scale.
+
+__device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+__device__ inline uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, a),
+                                                                      __builtin_bit_cast(u16x2, b)));
+}
+__device__ inline uint32_t pk_shl3_u16(uint32_t a) {
+    const u16x2 s = {3, 3};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) << s);
+}
+
+// Largest |bits| (sign cleared) of the 16 bf16 pairs of one lane, both halves.
+__device__ inline uint32_t bf16_absmax_bits(const uint4 (&v)[4]) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        mx = pk_max_u16(mx, v[s].x & 0x7FFF7FFFu);
+        mx = pk_max_u16(mx, v[s].y & 0x7FFF7FFFu);
+        mx = pk_max_u16(mx, v[s].z & 0x7FFF7FFFu);
+        mx = pk_max_u16(mx, v[s].w & 0x7FFF7FFFu);
+    }
+    const uint32_t lo = mx & 0xFFFFu, hi = mx >> 16;
+    return lo > hi ? lo : hi;
+}
+
+// The block exponent offset c of operand row r16 from this lane's |bits|
+// maximum: the row's 128 values sit in lanes r16, r16 + 16, r16 + 32, r16 + 48
+// (one per 16-lane row of the wave); the permlane swaps pair rows 0/1 and 2/3,
+// then the wave's halves.
+__device__ inline uint32_t row_block_offset(uint32_t mx) {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+    mx = s16[0] > s16[1] ? s16[0] : s16[1];
+    const auto s32 = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+    mx = s32[0] > s32[1] ? s32[0] : s32[1];
+    const uint32_t E = mx >> 7;
+    return E > 29u ? E - 29u : 0u;
+}
+
+// One lane's 8 bf16 values of a k step (4 dwords, k-offsets 0..7) -> fp16
+// operands; cc = (c << 7) and cc4 = ((c + 4) << 7) in both halves.
+__device__ inline f16x8 bf16_to_f16_scaled(uint4 v, uint32_t cc, uint32_t cc4) {
+    uint4 r;
+    r.x = (v.x & 0x80008000u) | pk_shl3_u16(pk_sub_sat_u16(v.x & 0x7FFF7FFFu, cc));
+    r.y = (v.y & 0x80008000u) | pk_shl3_u16(pk_sub_sat_u16(v.y & 0x7FFF7FFFu, cc4));
+    r.z = (v.z & 0x80008000u) | pk_shl3_u16(pk_sub_sat_u16(v.z & 0x7FFF7FFFu, cc));
+    r.w = (v.w & 0x80008000u) | pk_shl3_u16(pk_sub_sat_u16(v.w & 0x7FFF7FFFu, cc4));
+    return __builtin_bit_cast(f16x8, r);
 }
 
 }  // namespace qi4

@@ -26,6 +26,9 @@ struct GemmArgs {
     int64_t a_bytes;           // bytes of the whole A buffer (< 2^31)
     int a_f32;                 // float32 rows, split into 4 bf16 terms in registers
     int a_i8;                  // int8 rows in MFMA operand order (W4A8), lda in bytes
+    int a_f16;                 // fp16 rows from prep_rows: value = fp16 * 2^a_exp[row], with
+                               // k = 2, 3, 6, 7 (mod 8) stored times 2^-4
+    const int32_t *a_exp;      // a_f16: per-row exponent
     float a_scale;             // W4A8: the activations' scale, applied at the store
     int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
     int a_shift;               // weight block b reads activation block b >> a_shift
@@ -34,6 +37,7 @@ struct GemmArgs {
     int moe;                   // 0: one dense problem with T slots
     int64_t T;                 // tokens
     int top_k;
+    uint32_t topk_magic;       // set by launch_qgemm: pair / top_k = umulhi(pair, topk_magic)
     const int32_t *sorted_pairs;  // moe gate/up: slot -> pair -> token
     const int32_t *offsets;       // moe: expert segment starts (E + 1)
     const int32_t *active;        // moe: [count, experts...]

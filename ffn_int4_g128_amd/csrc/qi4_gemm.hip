@@ -1,21 +1,24 @@
 // int4-g128 weight-only GEMM for few rows of activations (decode, T <= 32 per
 // problem per pass), on bf16 MFMA with float32 accumulation.
 //
-// The pages' pipeline is "read 4-bit weight -> dequantize -> multiply" with no
-// separate dequantization pass ("FastLLM: zero-dependency CPU inference
-// framework", section 3.1), and decode time is set by how fast the weights are
-// read, not by arithmetic (same section: every token re-reads all weights).  On
-// CDNA4 that becomes:
+// The FastLLM page (section 3.1, 4-bit quantization and weight reordering)
+// has each 4-bit weight dequantized on the fly inside the matrix product, with
+// no separate dequantization pass, and decode time set by how fast the weights
+// are read rather than by arithmetic, since every token reads all of them again.
+// On CDNA4 that becomes:
 //  * one 16-byte load per lane per (16-row tile, 128-wide group): a contiguous
 //    kilobyte per wave, prepared by qi4_pack;
 //  * the codes become MFMA operands with one AND/OR per pair: bf16 with the
 //    bits 0x4300 | q is exactly 128 + q;
-//  * MFMA 16x16x32 bf16 multiplies the activations (as they are, bf16) with
-//    those operands, giving acc = sum_k x * (128 + q) per group; a second MFMA
-//    chain in the same order against a constant operand 128 + zero gives
-//    xz = sum_k x * (128 + zero), and the group adds scale * (acc - xz), which
-//    equals scale * sum_k x * (q - zero).  Both chains see identical operands
-//    where q == zero, so an all-zero group contributes exactly 0;
+//  * the codes become exact fp16 operands q - zero with one and-or and one
+//    packed add per pair (fp16 1024 | q is exactly 1024 + q);
+//  * the activation rows become exact fp16 operands too: one power of two per
+//    (row, 128-wide block) taken from the block's largest exponent, built from
+//    the bf16 bits with packed integer ops (qi4_dev.h), and undone on the
+//    block's sum;
+//  * MFMA 16x16x32 fp16 forms each block's sum of exact products in float32
+//    (a code on its zero point adds exactly 0, so no large offset is ever
+//    subtracted), and the block adds scale * 2^(c - 112) * sum per output;
 //  * the K range is split across the waves of a workgroup and reduced in LDS in
 //    a fixed order, so results are deterministic;
 //  * a workgroup may stream several consecutive tile blocks through one
@@ -24,7 +27,8 @@
 //  * the scales and zero points of a quad of four tiles arrive with one load
 //    each per group.
 // Activations in float32 are split exactly into three bf16 terms (hi + mid +
-// lo), each an MFMA row; the epilogue adds the rows of one token back together.
+// lo), each an MFMA row with its own block exponent; the epilogue adds the rows
+// of one token back together.
 #include "qi4_gemm.h"
 #include "qi4_host.h"
 
@@ -63,7 +67,8 @@ __device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
 // the raw activation fragments of MT M tiles (bf16: one 16-byte load per k
 // step; float32: two).
 // AM: activation mode -- 0 bf16 rows, 1 float32 rows (split into bf16 terms),
-// 2 int8 rows in operand order (W4A8; 32 bytes per lane per block).
+// 2 int8 rows in operand order (W4A8; 32 bytes per lane per block), 3 fp16
+// rows with a per-row power of two (prep_rows).
 template <int NB, int MT, int AM, int H>
 struct Stage {
     uint4 cw[NB];
@@ -74,19 +79,20 @@ struct Stage {
 
 
 
-// Waves per SIMD the register allocation must allow: the grouped gate/up and
-// down GEMMs (a quad of tiles, one M tile) sit one register above the four-wave
-// limit without this (down at T = 32: +4.7 % GB/s with it).  With 64-wide
-// groups they need more registers than four waves allow: no cap there.
+// Waves per SIMD the register allocation must allow: four for the grouped
+// gate/up and down GEMMs of the MoE decode (a quad of tiles, one M tile, fp16
+// rows from prep_rows).  With 64-wide groups, or with the bf16 rows converted in
+// registers, they need more registers than four waves allow: no cap there (a
+// cap made the converting kernel spill and run slower).
 template <int NB, int MT, int AM, int EPI, int H>
-constexpr int kMinWaves = (AM == 0 && MT == 1 && NB == 4 && H == 1) ? 4 : 1;
+constexpr int kMinWaves = (AM == 3 && MT == 1 && NB == 4 && H == 1) ? 4 : 1;
 
 // H = 2: 64-wide groups, two scales and zeros per 128-wide block.
 template <int NB, int MT, int AM, int S, int EPI, int H>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI, H>)))
 qgemm_kernel(const GemmArgs args) {
-    constexpr bool AF32 = AM == 1, AI8 = AM == 2;
+    constexpr bool AF32 = AM == 1, AI8 = AM == 2, AF16 = AM == 3;
     __shared__ float red[kRedSlotsFor<NB, MT> * 256];
 
     const int lane = threadIdx.x & 63;
@@ -151,15 +157,23 @@ qgemm_kernel(const GemmArgs args) {
     const int gb = (int)((G * wave) / W), ge = (int)((G * (wave + 1)) / W);
     const int ngp = (((int)((G + W - 1) / W) + S - 1) / S) * S;
     const int steps = nblk * ngp;
-    const int P = args.P;
-    const int spt = 16 / P;                 // slots per M tile
+    const int P = args.P;                   // 1, 2 or 4
+    const int plog = P == 4 ? 2 : P == 2 ? 1 : 0;
+    const int spt = 16 >> plog;             // slots per M tile
     const int64_t chunk = (int64_t)MT * spt;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     constexpr int ES = AF32 ? 4 : AI8 ? 1 : 2;   // bytes per activation element
+    // source row of A (a token when gathering, else a slot) of a problem slot
+    auto src_row = [&](int64_t slot) -> int64_t {
+        if (!gather) return src0 + slot;
+        const uint32_t pr = (uint32_t)gather[row0 + slot];
+        return args.top_k == 1 ? pr : __umulhi(pr, args.topk_magic);
+    };
 
     for (int64_t c0 = 0; c0 < n; c0 += chunk) {
         // M tiles of this chunk that hold at least one slot (uniform per workgroup)
-        const int m_used = (int)((n - c0 + spt - 1) / spt < MT ? (n - c0 + spt - 1) / spt : MT);
+        const int64_t mt_left = (n - c0 + spt - 1) >> (4 - plog);
+        const int m_used = (int)(mt_left < MT ? mt_left : MT);
 
         f32x4 res[MT][NB];
 #pragma unroll
@@ -277,58 +291,78 @@ qgemm_kernel(const GemmArgs args) {
                 }
             }
           } else {
-            bf16x8 a[MT][4];
+            // Exact operands: the codes as fp16 q - zero (16x at k-offsets 2, 3,
+            // 6, 7), the activation rows as fp16 times a power of two: one per
+            // (row, block) converted here from bf16 (qi4_dev.h), or one per row
+            // from prep_rows (AM 3, applied at the store).  The products are
+            // exact and a code on its zero point adds exactly 0.  One MFMA chain
+            // per tile and block (two with 64-wide groups), then the scale (times
+            // 2^(c - 112) for the blocks converted here) per output row.
+            const uint32_t magic = f16_magic_pair();
+            uint4 raw[MT][4];
+            uint32_t cc[MT], cc4[MT];
+            float f[MT][4];
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MT; ++m) {
+                if (AF16 || m >= m_used) break;
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    if constexpr (AF32)
-                        a[m][s4] = as_bf16x8(split_frag(q.af[m][s4][0], q.af[m][s4][AF32 ? 1 : 0], apart[m]));
-                    else
-                        a[m][s4] = as_bf16x8(q.af[m][s4][0]);
-                }
+                for (int s4 = 0; s4 < 4; ++s4)
+                    raw[m][s4] = AF32 ? split_frag(q.af[m][s4][0], q.af[m][s4][AF32 ? 1 : 0], apart[m])
+                                      : q.af[m][s4][0];
+                const uint32_t c = row_block_offset(bf16_absmax_bits(raw[m]));
+                cc[m] = (c << 7) * 0x00010001u;
+                cc4[m] = ((c + 4) << 7) * 0x00010001u;
+                // 2^(c - 112) of the rows this lane's results belong to: result
+                // register v of lane 16 j + col is operand row 4 j + v
+                const int fb = (int)((c + 15u) << 23);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) f[m][v] = __int_as_float(__shfl(fb, 4 * j + v));
+            }
+            // activation operands of the 4 k steps, shared by the tiles
+            f16x8 a[MT][4];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m >= m_used) break;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    a[m][s] = AF16 ? __builtin_bit_cast(f16x8, q.af[m][s][0])
+                                   : bf16_to_f16_scaled(raw[m][s], cc[m], cc4[m]);
+            }
+            // tile by tile: one accumulator (per M tile and half) live at a time
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const bf16x8 b0 = as_bf16x8(unpack_codes_bf16(q.cw[nb].x));
-                const bf16x8 b1 = as_bf16x8(unpack_codes_bf16(q.cw[nb].y));
-                const bf16x8 b2 = as_bf16x8(unpack_codes_bf16(q.cw[nb].z));
-                const bf16x8 b3 = as_bf16x8(unpack_codes_bf16(q.cw[nb].w));
-                bf16x8 bz[H];
-                float sc[H];
+                f32x4 acc[MT][H];
+                uint32_t negz[H], negz16[H];
 #pragma unroll
                 for (int h = 0; h < H; ++h) {
                     const uint32_t z = (q.zb[h] >> (zshift + 4 * nb)) & 15u;
-                    const uint32_t zz = (0x4300u | z) * 0x00010001u;   // bf16 pair (128+z, 128+z)
-                    bz[h] = as_bf16x8(make_uint4(zz, zz, zz, zz));
-                    sc[h] = f16_bits_to_f32((uint16_t)(q.sc[h][nb >> 1] >> (16 * (nb & 1))));
+                    negz[h] = f16_negz(z);
+                    negz16[h] = f16_negz16(z);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) acc[m][h] = zero4;
                 }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int h = H == 2 ? s >> 1 : 0;   // 64-wide groups: k steps 0, 1 / 2, 3
+                    const uint32_t d = s == 0 ? q.cw[nb].x : s == 1 ? q.cw[nb].y : s == 2 ? q.cw[nb].z : q.cw[nb].w;
+                    const f16x8 b = __builtin_bit_cast(f16x8, codes_minus_zero_f16(d, negz[h], negz16[h], magic));
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        if (m >= m_used) break;
+                        acc[m][h] = mfma16x16x32_f16(a[m][s], b, acc[m][h]);
+                    }
+                }
+                const float s0 = f16_bits_to_f32((uint16_t)(q.sc[0][nb >> 1] >> (16 * (nb & 1))));
+                const float s1 = f16_bits_to_f32((uint16_t)(q.sc[H - 1][nb >> 1] >> (16 * (nb & 1))));
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m >= m_used) break;
-                    if constexpr (H == 1) {
-                        f32x4 acc = mfma16x16x32(a[m][0], b0, zero4);
-                        f32x4 xz = mfma16x16x32(a[m][0], bz[0], zero4);
-                        acc = mfma16x16x32(a[m][1], b1, acc);
-                        xz = mfma16x16x32(a[m][1], bz[0], xz);
-                        acc = mfma16x16x32(a[m][2], b2, acc);
-                        xz = mfma16x16x32(a[m][2], bz[0], xz);
-                        acc = mfma16x16x32(a[m][3], b3, acc);
-                        xz = mfma16x16x32(a[m][3], bz[0], xz);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) res[m][nb][v] += sc[0] * (acc[v] - xz[v]);
-                    } else {
-                        // k-steps 0, 1 are the first 64-wide group, 2, 3 the second
-                        f32x4 acc0 = mfma16x16x32(a[m][0], b0, zero4);
-                        f32x4 xz0 = mfma16x16x32(a[m][0], bz[0], zero4);
-                        acc0 = mfma16x16x32(a[m][1], b1, acc0);
-                        xz0 = mfma16x16x32(a[m][1], bz[0], xz0);
-                        f32x4 acc1 = mfma16x16x32(a[m][2], b2, zero4);
-                        f32x4 xz1 = mfma16x16x32(a[m][2], bz[H - 1], zero4);
-                        acc1 = mfma16x16x32(a[m][3], b3, acc1);
-                        xz1 = mfma16x16x32(a[m][3], bz[H - 1], xz1);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            res[m][nb][v] += sc[0] * (acc0[v] - xz0[v]) + sc[H - 1] * (acc1[v] - xz1[v]);
+                    for (int v = 0; v < 4; ++v) {
+                        float g = s0 * acc[m][0][v];
+                        if constexpr (H == 2) g += s1 * acc[m][H - 1][v];
+                        if constexpr (AF16) res[m][nb][v] += g;
+                        else res[m][nb][v] += f[m][v] * g;
                     }
                 }
             }
@@ -353,6 +387,11 @@ qgemm_kernel(const GemmArgs args) {
                 if constexpr (AI8) {   // the activations' scale
                     val *= args.a_scale;
                     uval *= args.a_scale;
+                }
+                if constexpr (AF16) {   // the row's power of two
+                    const int e = args.a_exp[src_row(slot)];
+                    val = ldexpf(val, e);
+                    uval = ldexpf(uval, e);
                 }
                 if (EPI == QI4_EPI_SILU_MUL) val = val / (1.0f + expf(-val)) * uval;
                 const int64_t dst = row0 + slot;
@@ -405,9 +444,9 @@ qgemm_kernel(const GemmArgs args) {
                     // (static register indices: v0 and p are unrolled, P is 1, 2 or 4)
 #pragma unroll
                     for (int v0 = 0; v0 < 4; ++v0) {
-                        if (v0 % P != 0) continue;
-                        const int64_t slot = c0 + (int64_t)m * spt + (rbase + v0) / P;
-                        if ((rbase + v0) / P >= spt || slot >= n) continue;
+                        if ((v0 & (P - 1)) != 0) continue;
+                        const int64_t slot = c0 + (int64_t)m * spt + ((rbase + v0) >> plog);
+                        if (((rbase + v0) >> plog) >= spt || slot >= n) continue;
                         float val = 0.f, uval = 0.f;
 #pragma unroll
                         for (int p = 0; v0 + p < 4; ++p) {
@@ -426,8 +465,8 @@ qgemm_kernel(const GemmArgs args) {
             for (int it = threadIdx.x; it < items; it += blockDim.x) {
                 const int col = it & 15;
                 int rest = it >> 4;
-                const int sq = rest % spt;
-                rest /= spt;
+                const int sq = rest & (spt - 1);
+                rest >>= 4 - plog;
                 const int pi = rest % pairs;
                 const int m = rest / pairs;
                 const int64_t slot = c0 + (int64_t)m * spt + sq;
@@ -469,11 +508,11 @@ qgemm_kernel(const GemmArgs args) {
         // ---- byte offset of this lane's activation row (operand row r16 of each M tile)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const int64_t slot = c0 + (int64_t)m * spt + r16 / P;
-            const int part = r16 % P;
+            const int64_t slot = c0 + (int64_t)m * spt + (r16 >> plog);
+            const int part = r16 & (P - 1);
             const bool ok = (r16 < spt * P) && slot < n;
             const int64_t slot_c = ok ? slot : 0;
-            const int64_t src = gather ? (int64_t)(gather[row0 + slot_c] / args.top_k) : src0 + slot_c;
+            const int64_t src = src_row(slot_c);
             const int64_t row = AF32 ? src : src * P + part;
             apart[m] = part;
             // (int8 rows: a lane's 32 bytes of a block sit at 32 j)
@@ -495,6 +534,9 @@ qgemm_kernel(const GemmArgs args) {
 #pragma unroll
             for (int q = 0; q < S; ++q) {
                 compute(st[q], zshift);
+                // the refill of this stage is issued after its compute: hoisting
+                // the loads above it would keep both copies live
+                __builtin_amdgcn_sched_barrier(0);
                 load_w(st[q]);
                 load_a(st[q]);
                 advance();
@@ -509,14 +551,19 @@ qgemm_kernel(const GemmArgs args) {
     }
 }
 
+// float32 activations (split into bf16 parts in registers) run on blocks of
+// at most two tiles: their fragments take twice the registers.
 template <int NB, int MT, int S, int H>
 int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
+    if (a.a_f32 && NB > 2) return QI4_ERR_UNSUPPORTED;
     if (a.epi == QI4_EPI_SILU_MUL) {
         if constexpr (NB % 2 == 0) {
             if (a.a_i8)
                 qgemm_kernel<NB, MT, 2, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
-            else if (a.a_f32)
-                qgemm_kernel<NB, MT, 1, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+            else if (a.a_f16)
+                qgemm_kernel<NB, MT, 3, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+            else if (NB <= 2 && a.a_f32)
+                qgemm_kernel<NB <= 2 ? NB : 2, MT, 1, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
             else
                 qgemm_kernel<NB, MT, 0, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
         } else {
@@ -524,8 +571,10 @@ int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
         }
     } else if (a.a_i8) {
         qgemm_kernel<NB, MT, 2, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
-    } else if (a.a_f32) {
-        qgemm_kernel<NB, MT, 1, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
+    } else if (a.a_f16) {
+        qgemm_kernel<NB, MT, 3, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
+    } else if (NB <= 2 && a.a_f32) {
+        qgemm_kernel<NB <= 2 ? NB : 2, MT, 1, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     } else {
         qgemm_kernel<NB, MT, 0, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     }
@@ -580,13 +629,17 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
             W = 2;
         }
     } else {
-        if (max_slots > 8 && ceil_div(nt, 4) >= 192) NB = 4;
+        if (max_slots > 8 && ceil_div(nt, 4) >= 192 && !args.a_f32) NB = 4;
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
     }
     while (W > 1 && W * MT * NB > red_slots(NB, MT)) W /= 2;
     GemmArgs a = args;
     a.blocks_per_wg = R;
+    // pair / top_k as a multiply-high: with m = floor((2^32 - 1) / k) + 1,
+    // floor(p * m / 2^32) = floor(p / k) whenever p * k < 2^32 (pairs are below
+    // 2^31 / 32 and top_k is at most 32); k = 1 (m = 2^32) is taken apart
+    a.topk_magic = a.top_k > 1 ? (uint32_t)(0xFFFFFFFFull / (uint32_t)a.top_k + 1ull) : 0u;
     const int64_t gx = ceil_div(ceil_div(nt, NB), R);
     if (gx > 0x7fffffff || n_problems > 65535) return QI4_ERR_SHAPE;
     dim3 grid((unsigned)gx, (unsigned)n_problems);

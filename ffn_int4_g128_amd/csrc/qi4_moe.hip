@@ -507,11 +507,12 @@ struct MoeWorkspace {
         active = o;  o += align256((d->num_experts + 1) * 4);
         h = o;       o += align256(w4a8 ? R * d->inter : R * 2 * d->inter * 2);
         y = o;       o += align256(R * d->hidden * 4);
-        // prefill only: fp16 rows with exponents and the tile list
-        x16 = o;     o += pf ? align256(T * d->hidden * 2) : 0;
-        ex = o;      o += pf ? align256(T * 4) : 0;
-        h16 = o;     o += pf ? align256(R * d->inter * 2) : 0;
-        eh = o;      o += pf ? align256(R * 4) : 0;
+        // fp16 rows with per-row exponents (both GEMM paths; not W4A8), then,
+        // for the prefill only, the tile list
+        x16 = o;     o += !w4a8 ? align256(T * d->hidden * 2) : 0;
+        ex = o;      o += !w4a8 ? align256(T * 4) : 0;
+        h16 = o;     o += !w4a8 ? align256(R * d->inter * 2) : 0;
+        eh = o;      o += !w4a8 ? align256(R * 4) : 0;
         const PrefillTiles mt = prefill_max_tiles(T, d->top_k, d->num_experts, d->has_shared);
         tiles = o;   o += pf ? align256((mt.big + 3 * mt.small) * 8) : 0;
         ntiles = o;  o += pf ? 256 : 0;
@@ -696,16 +697,20 @@ int run_gate_up(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *
                 const int32_t *offsets, const int32_t *active, const void *w_gu, const void *sh_gu,
                 void *h, uint8_t *ws, hipStream_t st) {
     int rc;
-    if (T < kPrefillMinT) {
-        GemmArgs a = gate_up_args(d, x, T, sorted, offsets, active, w_gu, sh_gu, h);
-        return launch_qgemm(a, grouped_problems(a, d, T), T, st);
-    }
+    // the input rows once as fp16 with a per-row power of two (exact), for
+    // every expert's GEMM
     const MoeWorkspace L(d, T);
     uint16_t *x16 = reinterpret_cast<uint16_t *>(ws + L.x16);
     int32_t *ex = reinterpret_cast<int32_t *>(ws + L.ex);
+    if ((rc = launch_prep_rows(x, 0, T, d->hidden, x16, ex, st))) return rc;
+    if (T < kPrefillMinT) {
+        GemmArgs a = gate_up_args(d, x16, T, sorted, offsets, active, w_gu, sh_gu, h);
+        a.a_f16 = 1;
+        a.a_exp = ex;
+        return launch_qgemm(a, grouped_problems(a, d, T), T, st);
+    }
     int2 *tiles = reinterpret_cast<int2 *>(ws + L.tiles);
     int32_t *nt = reinterpret_cast<int32_t *>(ws + L.ntiles);
-    if ((rc = launch_prep_rows(x, 0, T, d->hidden, x16, ex, st))) return rc;
     int4 *def = reinterpret_cast<int4 *>(ws + L.deferred);
     PrefillArgs a = prefill_args(d, T, true, sorted, offsets, active, w_gu, sh_gu, x16, ex, tiles, nt, def, h);
     if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, {a.max_big, a.max_small}, nt, st)))
@@ -717,17 +722,22 @@ int run_down(const qi4_moe_desc *d, const void *h, int64_t T, const int32_t *off
              const int32_t *active, const void *w_dn, const void *sh_dn, float *y, uint8_t *ws,
              hipStream_t st) {
     int rc;
-    if (T < kPrefillMinT) {
-        GemmArgs a = down_args(d, h, T, offsets, active, w_dn, sh_dn, y);
-        return launch_qgemm(a, grouped_problems(a, d, T), T, st);
-    }
+    // h (hi + lo bf16 pairs) once as fp16 rows with a per-row power of two
     const MoeWorkspace L(d, T);
     const int64_t R = T * d->top_k + (d->has_shared ? T : 0);
     uint16_t *h16 = reinterpret_cast<uint16_t *>(ws + L.h16);
     int32_t *eh = reinterpret_cast<int32_t *>(ws + L.eh);
+    if ((rc = launch_prep_rows(h, 1, R, d->inter, h16, eh, st))) return rc;
+    if (T < kPrefillMinT) {
+        GemmArgs a = down_args(d, h16, T, offsets, active, w_dn, sh_dn, y);
+        a.a_f16 = 1;
+        a.a_exp = eh;
+        a.a_bytes = R * d->inter * 2;
+        a.P = 1;
+        return launch_qgemm(a, grouped_problems(a, d, T), T, st);
+    }
     int2 *tiles = reinterpret_cast<int2 *>(ws + L.tiles);
     int32_t *nt = reinterpret_cast<int32_t *>(ws + L.ntiles);
-    if ((rc = launch_prep_rows(h, 1, R, d->inter, h16, eh, st))) return rc;
     int4 *def = reinterpret_cast<int4 *>(ws + L.deferred);
     PrefillArgs a = prefill_args(d, T, false, nullptr, offsets, active, w_dn, sh_dn, h16, eh, tiles, nt, def, y);
     if ((rc = launch_plan(offsets, active, T, d->has_shared, tiles, {a.max_big, a.max_small}, nt, st)))

@@ -34,16 +34,9 @@
 namespace qi4 {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
-
 // (kOob / kOobS out-of-range offsets and buffer resources: qi4_dev.h)
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
     return make_rsrc(base, bytes);
-}
-
-__device__ inline f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // fp16 operands scale * (q - zero) of the 8 codes in one packed dword, in the
@@ -57,14 +50,6 @@ __device__ inline uint4 dequant_f16(uint32_t d, uint32_t negz, uint32_t s2) {
     r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, ((d >> 4) & m) | magic) + nz) * sc);
     r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, ((d >> 8) & m) | magic) + nz) * sc);
     r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, ((d >> 12) & m) | magic) + nz) * sc);
-    return r;
-}
-
-// (a & m) | c in one VALU instruction (m in a scalar register, c in a vector
-// register: a three-operand VALU op takes no literal here).
-__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
     return r;
 }
 
@@ -403,10 +388,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
         }
     }
 
-    // magic (fp16 1024 in both halves) is produced opaquely so that it stays in
-    // one vector register instead of being rematerialized at every use.
-    uint32_t magic;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+    const uint32_t magic = f16_magic_pair();
 
     // The main loop multiplies the first MU subtiles (MU * 16 >= the tile's
     // rows; rows past its end only feed output rows that are never stored), so

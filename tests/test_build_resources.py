@@ -35,8 +35,8 @@ def test_no_kernel_spills(resources):
 
 @pytest.mark.parametrize("epi", [1, 0])
 def test_grouped_decode_gemms_keep_four_waves(resources, epi):
-    # qgemm_kernel<4 tiles, 1 M tile, bf16 activations, 2 stages, SiLU*up (1) or
-    # none (0: down), 128-wide groups>
-    tag = f"qgemm_kernelILi4ELi1ELi0ELi2ELi{epi}ELi1E"
+    # qgemm_kernel<4 tiles, 1 M tile, fp16 rows with a row exponent, 2 stages,
+    # SiLU*up (1) or none (0: down), 128-wide groups>
+    tag = f"qgemm_kernelILi4ELi1ELi3ELi2ELi{epi}ELi1E"
     hot = [r for _, n, r in resources if tag in n]
     assert hot and all(r["occupancy"] >= 4 and r["vgprs"] <= 128 for r in hot), hot
