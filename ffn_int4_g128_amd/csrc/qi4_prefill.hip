@@ -16,15 +16,14 @@
 //    up to 16, 32 or 64 rows.  Big tiles run on MFMA-bound workgroups (4 waves
 //    x 64 weight rows, two-stage pipeline, two workgroups per CU); small tiles
 //    run on weight-stream-bound workgroups (8 waves x 32 weight rows,
-//    four-stage pipeline, 16 waves per CU), on side streams so that all of
-//    them share the chip;
+//    four-stage pipeline, 16 waves per CU) after the big tiles, on the same
+//    stream;
 //  * the activation tile of each group is copied from memory straight into LDS
 //    (buffer loads with the LDS bit), each 4-lane quad reading 64 contiguous
 //    bytes, in a rotated order that keeps the MFMA operand reads free of bank
 //    conflicts, and shared by all waves of the workgroup;
 //  * a workgroup whose weights hold a scale the 16x operands cannot represent
 //    (|scale| >= 256, inf, NaN) hands its tile to a pass with plain operands.
-#include <mutex>
 #include <type_traits>
 
 #include "qi4_gemm.h"
@@ -602,79 +601,23 @@ int64_t prefill_max_deferred(int64_t N, int flags, const PrefillTiles &m) {
     return gx * (ceil_div(m.big, 8) + 3 * ceil_div(m.small, 8)) * 8;
 }
 
-// The small-tile kernels run on side streams of the device, one per height
-// class, forked from and joined back to the caller's stream with events, so
-// that all of them share the chip with the big-tile kernel (one kind streams
-// weights, the other keeps the MFMAs busy; a class run after the big tiles
-// would leave most of the chip idle).  Three side streams and their events per
-// device, created on first use and kept for the life of the process; a mutex
-// makes each fork/join sequence of enqueues atomic, so calls on different
-// streams cannot pick up each other's events.
+// All four kernels run on the caller's stream, one after the other: the
+// big-tile kernel first (the MFMA-bound bulk of the work, 128-row tiles), then
+// the three small-tile classes (weight-streaming), then the pass for deferred
+// tiles.  The library keeps no streams or events of its own.
 namespace {
-constexpr int kSideStreams = 3;
-struct SideStream {
-    std::mutex mu;
-    hipStream_t s[kSideStreams] = {};
-    hipEvent_t fork = nullptr, join[kSideStreams] = {};
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_init;
-
-int side_stream(SideStream **out) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QI4_ERR_HIP;
-    SideStream &ss = g_side[dev];
-    std::lock_guard<std::mutex> lk(g_side_init);
-    if (!ss.fork) {
-        hipStream_t s[kSideStreams] = {};
-        hipEvent_t f = nullptr, j[kSideStreams] = {};
-        bool ok = hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess;
-        for (int i = 0; ok && i < kSideStreams; ++i)
-            ok = hipStreamCreateWithFlags(&s[i], hipStreamNonBlocking) == hipSuccess &&
-                 hipEventCreateWithFlags(&j[i], hipEventDisableTiming) == hipSuccess;
-        if (!ok) {
-            for (int i = 0; i < kSideStreams; ++i) {
-                if (j[i]) (void)hipEventDestroy(j[i]);
-                if (s[i]) (void)hipStreamDestroy(s[i]);
-            }
-            if (f) (void)hipEventDestroy(f);
-            return QI4_ERR_HIP;
-        }
-        for (int i = 0; i < kSideStreams; ++i) {
-            ss.s[i] = s[i];
-            ss.join[i] = j[i];
-        }
-        ss.fork = f;
-    }
-    *out = &ss;
-    return QI4_OK;
-}
-
 template <int EPI, int H>
 int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsigned gs) {
     const unsigned tb = BigShape::W * 64;
     const unsigned ts0 = SmallShapeC<0, H>::W * 64, ts1 = SmallShapeC<1, H>::W * 64,
                    ts2 = SmallShapeC<2, H>::W * 64;
-    SideStream *ss = nullptr;
     int rc;
-    if ((rc = side_stream(&ss))) return rc;
-    {
-        std::lock_guard<std::mutex> lk(ss->mu);
-        if (hipEventRecord(ss->fork, st) != hipSuccess) return QI4_ERR_HIP;
-        for (int i = 0; i < kSideStreams; ++i)
-            if (hipStreamWaitEvent(ss->s[i], ss->fork, 0) != hipSuccess) return QI4_ERR_HIP;
-        prefill_small_kernel<EPI, 0, H><<<gs, ts0, 0, ss->s[0]>>>(a);
-        prefill_small_kernel<EPI, 1, H><<<gs, ts1, 0, ss->s[1]>>>(a);
-        prefill_small_kernel<EPI, 2, H><<<gs, ts2, 0, ss->s[2]>>>(a);
-        if ((rc = launch_status())) return rc;
-        prefill_big_kernel<EPI, H><<<gb, tb, 0, st>>>(a);
-        if ((rc = launch_status())) return rc;
-        for (int i = 0; i < kSideStreams; ++i) {
-            if (hipEventRecord(ss->join[i], ss->s[i]) != hipSuccess) return QI4_ERR_HIP;
-            if (hipStreamWaitEvent(st, ss->join[i], 0) != hipSuccess) return QI4_ERR_HIP;
-        }
-    }
+    prefill_big_kernel<EPI, H><<<gb, tb, 0, st>>>(a);
+    if ((rc = launch_status())) return rc;
+    prefill_small_kernel<EPI, 0, H><<<gs, ts0, 0, st>>>(a);
+    prefill_small_kernel<EPI, 1, H><<<gs, ts1, 0, st>>>(a);
+    prefill_small_kernel<EPI, 2, H><<<gs, ts2, 0, st>>>(a);
+    if ((rc = launch_status())) return rc;
     // tiles deferred by either kind, after both
     prefill_wide_kernel<EPI, H><<<512, tb, 0, st>>>(a);   // two workgroups per CU
     return launch_status();

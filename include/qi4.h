@@ -38,12 +38,8 @@
  *    of 128 (QI4_ERR_SHAPE).  A packed matrix is read with the group size it
  *    was packed with.  The device must be gfx950 (QI4_ERR_UNSUPPORTED
  *    otherwise).
- *  - Calls are reentrant.  The global state is a cached per-device
- *    architecture check and, for MoE batches of 128 tokens or more, three
- *    internal side streams per device (with their events), created on first
- *    use and kept for the life of the process: part of such a call runs there,
- *    ordered after the work already enqueued on `stream` and before anything
- *    enqueued on `stream` after the call, so the caller sees one stream.
+ *  - Calls are reentrant.  The only global state is a cached per-device
+ *    architecture check; every kernel of a call runs on `stream`.
  *
  * Canonical (interchange) format of a quantized matrix W [N][K] (out x in), with
  * Gs = group size (K when group_size is 0):
@@ -277,10 +273,11 @@ int64_t moe_ffn_int4_workspace_bytes(const qi4_moe_desc *d, int64_t T);
  *      bf16 numbers (hi = bf16(h), lo = bf16(h - hi)), about 16 significant bits
  *   y  [R][H] float32: each expert's down-projection output, before weighting
  * `active` is the array moe_sort_tokens fills.  `workspace` is a buffer of
- * moe_ffn_int4_workspace_bytes(d, T) bytes (256-byte aligned); batches of 128 or
- * more tokens use it for fp16 copies of the activations and the tile lists of the
- * prefill kernels (smaller batches do not touch it).  h and y may lie inside it
- * only if they do not overlap those regions; passing separate buffers is simplest. */
+ * moe_ffn_int4_workspace_bytes(d, T) bytes (256-byte aligned); the stage calls use
+ * it for fp16 copies of their input rows (each row as fp16 times an exact power of
+ * two) and, for batches of 128 or more tokens, the tile lists of the prefill
+ * kernels.  h and y may lie inside it only if they do not overlap those regions;
+ * passing separate buffers is simplest. */
 int moe_expert_gate_up(const qi4_moe_desc *d, const void *x, int64_t T,
                        const int32_t *sorted_pairs, const int32_t *expert_offsets,
                        const int32_t *active, const void *w_gate_up,

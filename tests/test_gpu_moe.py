@@ -1,7 +1,8 @@
 """GPU parity of the MoE path against the oracle: router ids and the token
 permutation bit for bit, combine weights, the stage calls, and moe_ffn_int4 on
-small layers and on the DeepSeek-V3-shaped layer (decode T in {1, 8, 32} and the
-Zipf-skewed prefill T = 2048, the oracle checking sampled tokens).  Output
+small layers and on the DeepSeek-V3-shaped layer (decode T in {1, 8, 32}, every
+token, and the Zipf-skewed prefill T = 2048, a block of 128 tokens that reaches
+every tile class).  Output
 tolerance: the oracle's first-order composite bound (per-linear factor 2e-3
 propagated through SiLU(g)*u, the down projection and the combine)."""
 import numpy as np
@@ -224,26 +225,56 @@ def _check_layer(c, ex, sh, mw, T, logits, x, tag, sample):
 
 @pytest.mark.parametrize("T", workloads.MOE_DECODE["T"])
 def test_dsv3_decode(dsv3, T):
+    """Every token of the decode batch against the oracle."""
     c, ex, sh, mw = dsv3
     logits = workloads.logits_normal(c["seed"], 10 + T, T, c["E"])
     x = workloads.activations(c["seed"], 20 + T, T, c["H"], "bf16")
-    _check_layer(c, ex, sh, mw, T, logits, x, "dsv3 decode", sorted({0, T // 2, T - 1}))
+    _check_layer(c, ex, sh, mw, T, logits, x, "dsv3 decode", list(range(T)))
+
+
+def _prefill_tile_classes(ids, E, tokens, big=128, small_max=64):
+    """Tile class of each (token, slot) in the prefill planner's cut of each
+    expert's rows: 'big' for rows in a 65..128-row tile, else the small-tile
+    class of its expert's remainder (<=16, <=32, <=64 rows).  Computed from the
+    oracle's permutation: a pair's row within its expert's segment and the
+    segment's length."""
+    sp, off, _ = oracle.sort_tokens(ids, E)
+    k = ids.shape[1]
+    pos = np.empty(ids.size, dtype=np.int64)
+    pos[sp] = np.arange(ids.size)
+    classes = set()
+    for t in tokens:
+        for j in range(k):
+            e = ids[t, j]
+            n = off[e + 1] - off[e]
+            r = pos[t * k + j] - off[e]
+            full, rem = n // big, n % big
+            if r < full * big or rem > small_max:
+                classes.add("big")
+            else:
+                classes.add("le16" if rem <= 16 else "le32" if rem <= 32 else "le64")
+    return classes
 
 
 def test_dsv3_prefill_zipf(dsv3):
+    """The Zipf-skewed T=2048 prefill: 128 consecutive tokens (the last ones, in
+    the shared expert's last tile) plus the first, against the oracle.  The
+    block reaches rows in big tiles and in small tiles of every height class."""
     c, ex, sh, mw = dsv3
     p = workloads.MOE_PREFILL
     T = p["T"]
     logits = workloads.logits_zipf(p["seed"], 5, T, p["E"], p["zipf"])
     x = workloads.activations(p["seed"], 6, T, p["H"], "bf16")
-    _check_layer(c, ex, sh, mw, T, logits, x, "dsv3 prefill zipf", [0, 777, T - 1])
+    tokens = [0] + list(range(T - 128, T))
+    oids, _ = oracle.topk_softmax(logits, p["top_k"])
+    assert _prefill_tile_classes(oids, p["E"], tokens) == {"big", "le16", "le32", "le64"}
+    _check_layer(c, ex, sh, mw, T, logits, x, "dsv3 prefill zipf", tokens)
 
 
 @pytest.mark.parametrize("T", [32, 2048])
 def test_dsv3_layer_is_deterministic(dsv3, T):
     """Two calls on the same inputs give bit-identical outputs on the decode path
-    and on the prefill path (every output element is reduced in a fixed order;
-    the prefill side streams change only when work runs, not what it adds)."""
+    and on the prefill path (every output element is reduced in a fixed order)."""
     import torch
     import ffn_int4_g128_amd as q
     c, ex, sh, mw = dsv3
