@@ -91,6 +91,7 @@ def lib():
             "moe_ffn_w4a8_workspace_bytes": (i64, [dp, i64]),
             "moe_ffn_w4a8": (ci, [dp, vp, ctypes.c_float, ctypes.c_float, i64, vp, vp, vp, vp, vp,
                                   vp, vp, vp, vp, i64, vp]),
+            "moe_ffn_int4_noalloc": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -106,7 +107,11 @@ EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pac
             "moe_route_topk",
             "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
-            "moe_combine", "moe_ffn_int4", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_w4a8"]
+            "moe_combine", "moe_ffn_int4", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_w4a8",
+            "moe_ffn_int4_noalloc"]
+
+#: bytes of the scratch array moe_ffn_int4_noalloc holds on each GPU
+NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
 def _check(rc: int, what: str):
@@ -414,6 +419,28 @@ def moe_ffn(x, w: MoeWeights, top_k: int, logits=None, ids=None, weights=None, w
                               _ptr(w.w_gate_up), _ptr(w.w_down), _ptr(w.shared_gate_up),
                               _ptr(w.shared_down), _ptr(out), _ptr(workspace),
                               workspace.numel(), _stream(stream)), "moe_ffn_int4")
+    if return_routing:
+        return out, ids, weights
+    return out
+
+
+def moe_ffn_noalloc(x, w: MoeWeights, top_k: int, logits=None, ids=None, weights=None,
+                    out=None, return_routing: bool = False, stream=None):
+    """moe_ffn through moe_ffn_int4_noalloc: no workspace argument; the library's
+    per-GPU scratch array serves instead (calls overlapping on one GPU race)."""
+    import torch
+    _need(x, torch.bfloat16, "x")
+    T = x.shape[0]
+    d = w.desc(top_k)
+    if out is None:
+        out = torch.empty((T, w.H), dtype=torch.bfloat16, device=x.device)
+    if logits is not None and return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+        weights = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_ffn_int4_noalloc(ctypes.byref(d), _ptr(x), T, _ptr(logits), _ptr(ids),
+                                      _ptr(weights), _ptr(w.w_gate_up), _ptr(w.w_down),
+                                      _ptr(w.shared_gate_up), _ptr(w.shared_down), _ptr(out),
+                                      _stream(stream)), "moe_ffn_int4_noalloc")
     if return_routing:
         return out, ids, weights
     return out

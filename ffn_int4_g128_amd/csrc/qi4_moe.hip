@@ -12,6 +12,8 @@
 // Only touched experts' weights are read.
 #include <limits.h>
 
+#include <mutex>
+
 #include <type_traits>
 
 #include "qi4_gemm.h"
@@ -1028,3 +1030,59 @@ int moe_ffn_w4a8(const qi4_moe_desc *d, const void *x, float x_scale, float h_sc
 }
 
 }  // extern "C"
+
+// ---- the layer without a caller workspace ----------------------------------------
+//
+// Scratch of moe_ffn_int4_noalloc: a file-scope device array, one copy per GPU
+// (part of the code object, so it lives until the process ends).  Host code
+// never passes the array's name to a kernel: that name is a host-side stand-in.
+// The device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is used.  Nothing in it has
+// to start at zero: every region is written before it is read within a call
+// (routing, permutation, fp16 rows, h, y; the prefill tile counters are reset
+// by the planner).  Calls that overlap in time on one GPU share it and race.
+namespace {
+__device__ __align__(256) uint8_t scratch[QI4_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+    std::once_flag once;
+    void *ptr = nullptr;
+    int rc = QI4_ERR_HIP;
+};
+constexpr int kScratchDevices = 64;
+ScratchAddr g_scratch[kScratchDevices];
+
+int scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return QI4_ERR_HIP;
+    ScratchAddr &sa = g_scratch[dev];
+    std::call_once(sa.once, [&sa] {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) {
+            sa.ptr = p;
+            sa.rc = QI4_OK;
+        }
+    });
+    *out = sa.ptr;
+    return sa.rc;
+}
+}  // namespace
+
+extern "C" int moe_ffn_int4_noalloc(const qi4_moe_desc *d, const void *x, int64_t T,
+                                    const float *router_logits, int32_t *topk_ids,
+                                    float *topk_weights, const void *w_gate_up,
+                                    const void *w_down, const void *shared_gate_up,
+                                    const void *shared_down, void *out, void *stream) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_T(T, d))) return rc;
+    if (MoeWorkspace(d, T).total > (int64_t)QI4_NOALLOC_SCRATCH_BYTES) return QI4_ERR_WORKSPACE;
+    if (T == 0) return QI4_OK;
+    if ((rc = check_device())) return rc;
+    void *ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    return moe_ffn_impl(d, x, T, router_logits, topk_ids, topk_weights, w_gate_up, w_down,
+                        shared_gate_up, shared_down, out, ws, (int64_t)QI4_NOALLOC_SCRATCH_BYTES,
+                        stream, nullptr);
+}
+

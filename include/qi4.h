@@ -325,6 +325,25 @@ int moe_ffn_w4a8(const qi4_moe_desc *d, const void *x, float x_scale, float h_sc
                  const void *shared_gate_up, const void *shared_down,
                  void *out, void *workspace, int64_t ws_bytes, void *stream);
 
+/* moe_ffn_int4 for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, results (bit for bit), routing outputs
+ * and errors as moe_ffn_int4, minus the workspace: the call uses a scratch
+ * array of QI4_NOALLOC_SCRATCH_BYTES (48 MiB) that the library holds on each
+ * GPU it runs on until the process ends, and never allocates or frees.  A
+ * layer whose moe_ffn_int4_workspace_bytes(d, T) exceeds that size returns
+ * QI4_ERR_WORKSPACE before anything is enqueued (the DeepSeek-V3 shape, 7168 x
+ * 2048 with 256 + 1 experts and top-8, fits up to T = 128).  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller. */
+#define QI4_NOALLOC_SCRATCH_BYTES (48ll << 20)
+int moe_ffn_int4_noalloc(const qi4_moe_desc *d, const void *x, int64_t T,
+                         const float *router_logits, int32_t *topk_ids, float *topk_weights,
+                         const void *w_gate_up, const void *w_down,
+                         const void *shared_gate_up, const void *shared_down,
+                         void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
