@@ -29,6 +29,8 @@ struct GemmArgs {
     int a_f16;                 // fp16 rows from prep_rows: value = fp16 * 2^a_exp[row], with
                                // k = 2, 3, 6, 7 (mod 8) stored times 2^-4
     const int32_t *a_exp;      // a_f16: per-row exponent
+    int a_lds;                 // bf16 rows converted into LDS by each workgroup (dense
+                               // calls whose T * K * 2 bytes fit kLdsActBytes)
     float a_scale;             // W4A8: the activations' scale, applied at the store
     int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
     int a_shift;               // weight block b reads activation block b >> a_shift
@@ -55,6 +57,10 @@ struct GemmArgs {
     // set by launch_qgemm
     int blocks_per_wg;         // consecutive tile blocks one workgroup streams
 };
+
+// Largest activation matrix (bytes of its fp16 rows) a dense call converts into
+// LDS per workgroup; larger ones convert in registers per (row, block).
+constexpr int64_t kLdsActBytes = 32 * 1024;
 
 // Launch the GEMM for `n_problems` problems (grid.y); `max_slots` bounds the
 // slots of any one problem and picks the M tiling.  Returns a QI4 status.

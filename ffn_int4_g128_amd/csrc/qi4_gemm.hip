@@ -68,13 +68,16 @@ __device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
 // step; float32: two).
 // AM: activation mode -- 0 bf16 rows, 1 float32 rows (split into bf16 terms),
 // 2 int8 rows in operand order (W4A8; 32 bytes per lane per block), 3 fp16
-// rows with a per-row power of two (prep_rows).
+// rows with a per-row power of two (prep_rows), 4 bf16 rows that each
+// workgroup first converts into LDS as fp16 rows with a per-row power of two
+// (few short rows: the whole activation matrix fits in LDS).
 template <int NB, int MT, int AM, int H>
 struct Stage {
     uint4 cw[NB];
     uint32_t sc[H][(NB + 1) / 2];   // per half: binary16 scales of tiles 2i, 2i+1 in dword i
     uint32_t zb[H];                 // per half: zero of tile nb in nibble nb (+ the slot offset)
-    uint4 af[MT][AM == 2 ? 2 : 4][AM == 1 ? 2 : 1];
+    uint4 af[MT][AM == 2 ? 2 : AM == 4 ? 1 : 4][AM == 1 ? 2 : 1];
+    uint32_t ag;                    // AM 4: byte offset of the step's block in an LDS row
 };
 
 
@@ -92,8 +95,11 @@ template <int NB, int MT, int AM, int S, int EPI, int H>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI, H>)))
 qgemm_kernel(const GemmArgs args) {
-    constexpr bool AF32 = AM == 1, AI8 = AM == 2, AF16 = AM == 3;
+    constexpr bool AF32 = AM == 1, AI8 = AM == 2, AF16 = AM == 3, ALDS = AM == 4;
     __shared__ float red[kRedSlotsFor<NB, MT> * 256];
+    // AM 4: [rows][lda] fp16 activation rows, 16 zero bytes, int32 [rows] (the
+    // row's largest |bits|, then its shift)
+    extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -170,6 +176,77 @@ qgemm_kernel(const GemmArgs args) {
         return args.top_k == 1 ? pr : __umulhi(pr, args.topk_magic);
     };
 
+    // AM 4: the n activation rows (bf16) once into LDS as fp16 rows times 2^sh,
+    // sh from the row's largest magnitude (|v * 2^sh| < 2^14, exact for normal
+    // values; columns k = 2, 3, 6, 7 (mod 8) times a further 2^-4, as the weight
+    // operands there are 16x).  A thread keeps its first chunk of 8 values in
+    // registers between the maximum and the conversion and reads the others
+    // again (from cache); called once the first weight loads are in flight.
+    const int64_t xrow_bytes = args.lda * 2;
+    const uint32_t zoff = (uint32_t)(n * xrow_bytes);
+    auto fill_lds = [&]() {
+        constexpr int kFillRegs = 1;   // more held chunks cost registers that slow the whole kernel
+        int *ri = reinterpret_cast<int *>(xlds + zoff + 16);
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) ri[i] = 0;
+        if (threadIdx.x < 4) reinterpret_cast<uint32_t *>(xlds + zoff)[threadIdx.x] = 0u;
+        __syncthreads();
+        const int64_t cpr = args.lda / 8, nch = n * cpr;
+        const uint16_t *xg = static_cast<const uint16_t *>(args.a);
+        auto row_of = [&](int64_t c) { return c / cpr; };
+        auto ld = [&](int64_t c) {
+            const int64_t r = row_of(c);
+            return *reinterpret_cast<const uint4 *>(xg + r * args.lda + 8 * (c - r * cpr));
+        };
+        auto absmax = [](uint4 v) {
+            uint32_t mx = pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                                     pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
+            return (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+        };
+        uint4 keep[kFillRegs];
+#pragma unroll
+        for (int i = 0; i < kFillRegs; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * blockDim.x;
+            if (c < nch) keep[i] = ld(c);
+        }
+#pragma unroll
+        for (int i = 0; i < kFillRegs; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * blockDim.x;
+            if (c < nch) atomicMax(reinterpret_cast<unsigned *>(ri) + row_of(c), absmax(keep[i]));
+        }
+        for (int64_t c = threadIdx.x + (int64_t)kFillRegs * blockDim.x; c < nch; c += blockDim.x)
+            atomicMax(reinterpret_cast<unsigned *>(ri) + row_of(c), absmax(ld(c)));
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const float mxf = bf16_to_f32((uint32_t)ri[i]);
+            int E = 0;
+            if (mxf > 0.f) frexpf(mxf, &E);     // mxf in [2^(E-1), 2^E)
+            ri[i] = mxf > 0.f ? 14 - E : 0;
+        }
+        __syncthreads();
+        auto cvt = [&](int64_t c, uint4 v) {
+            const int64_t r = row_of(c), k8 = 8 * (c - r * cpr);
+            const int sh = ri[r];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int se = (p & 1) ? sh - 4 : sh;
+                const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(bf16_to_f32(w4[p] & 0xFFFFu), se));
+                const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(bf16_to_f32(w4[p] >> 16), se));
+                o[p] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4 *>(xlds + r * xrow_bytes + 2 * k8) = make_uint4(o[0], o[1], o[2], o[3]);
+        };
+#pragma unroll
+        for (int i = 0; i < kFillRegs; ++i) {
+            const int64_t c = threadIdx.x + (int64_t)i * blockDim.x;
+            if (c < nch) cvt(c, keep[i]);
+        }
+        for (int64_t c = threadIdx.x + (int64_t)kFillRegs * blockDim.x; c < nch; c += blockDim.x)
+            cvt(c, ld(c));
+        __syncthreads();
+    };
+
     for (int64_t c0 = 0; c0 < n; c0 += chunk) {
         // M tiles of this chunk that hold at least one slot (uniform per workgroup)
         const int64_t mt_left = (n - c0 + spt - 1) >> (4 - plog);
@@ -216,6 +293,10 @@ qgemm_kernel(const GemmArgs args) {
         };
         auto load_a = [&](Stage<NB, MT, AM, H> &q) {
             const bool in = lnt > 0 && gb + li < ge;
+            if constexpr (ALDS) {   // the rows are in LDS: only the block offset
+                q.ag = in ? loa : 0u;
+                return;
+            }
             const uint32_t oa = in ? loa : kOobS;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -304,7 +385,7 @@ qgemm_kernel(const GemmArgs args) {
             float f[MT][4];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if (AF16 || m >= m_used) break;
+                if (AF16 || ALDS || m >= m_used) break;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
                     raw[m][s4] = AF32 ? split_frag(q.af[m][s4][0], q.af[m][s4][AF32 ? 1 : 0], apart[m])
@@ -325,7 +406,9 @@ qgemm_kernel(const GemmArgs args) {
                 if (m >= m_used) break;
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    a[m][s] = AF16 ? __builtin_bit_cast(f16x8, q.af[m][s][0])
+                    a[m][s] = ALDS ? *reinterpret_cast<const f16x8 *>(
+                                         xlds + (abase[m] != kOob ? abase[m] + q.ag + 64u * s : zoff))
+                            : AF16 ? __builtin_bit_cast(f16x8, q.af[m][s][0])
                                    : bf16_to_f16_scaled(raw[m][s], cc[m], cc4[m]);
             }
             // tile by tile: one accumulator (per M tile and half) live at a time
@@ -361,7 +444,7 @@ qgemm_kernel(const GemmArgs args) {
                     for (int v = 0; v < 4; ++v) {
                         float g = s0 * acc[m][0][v];
                         if constexpr (H == 2) g += s1 * acc[m][H - 1][v];
-                        if constexpr (AF16) res[m][nb][v] += g;
+                        if constexpr (AF16 || ALDS) res[m][nb][v] += g;
                         else res[m][nb][v] += f[m][v] * g;
                     }
                 }
@@ -390,6 +473,10 @@ qgemm_kernel(const GemmArgs args) {
                 }
                 if constexpr (AF16) {   // the row's power of two
                     const int e = args.a_exp[src_row(slot)];
+                    val = ldexpf(val, e);
+                    uval = ldexpf(uval, e);
+                } else if constexpr (ALDS) {
+                    const int e = -reinterpret_cast<const int *>(xlds + zoff + 16)[src_row(slot)];
                     val = ldexpf(val, e);
                     uval = ldexpf(uval, e);
                 }
@@ -505,6 +592,9 @@ qgemm_kernel(const GemmArgs args) {
             load_w(st[q]);
             advance();
         }
+        if constexpr (ALDS) {
+            if (c0 == 0) fill_lds();
+        }
         // ---- byte offset of this lane's activation row (operand row r16 of each M tile)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -515,7 +605,8 @@ qgemm_kernel(const GemmArgs args) {
             const int64_t src = src_row(slot_c);
             const int64_t row = AF32 ? src : src * P + part;
             apart[m] = part;
-            // (int8 rows: a lane's 32 bytes of a block sit at 32 j)
+            // (int8 rows: a lane's 32 bytes of a block sit at 32 j; AM 4: an
+            // offset into the LDS rows)
             abase[m] = ok ? (uint32_t)(row * args.lda * ES + (AI8 ? 32 * j : 8 * j * ES)) : kOob;
         }
         lr = 0;
@@ -556,12 +647,16 @@ qgemm_kernel(const GemmArgs args) {
 template <int NB, int MT, int S, int H>
 int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
     if (a.a_f32 && NB > 2) return QI4_ERR_UNSUPPORTED;
+    // AM 4: the fp16 rows, 16 zero bytes and one int per row in dynamic LDS
+    const size_t dyn = a.a_lds ? (size_t)(a.T * a.lda * 2 + 16 + 4 * a.T) : 0;
     if (a.epi == QI4_EPI_SILU_MUL) {
         if constexpr (NB % 2 == 0) {
             if (a.a_i8)
                 qgemm_kernel<NB, MT, 2, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
             else if (a.a_f16)
                 qgemm_kernel<NB, MT, 3, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+            else if (a.a_lds)
+                qgemm_kernel<NB, MT, 4, S, QI4_EPI_SILU_MUL, H><<<grid, threads, dyn, st>>>(a);
             else if (NB <= 2 && a.a_f32)
                 qgemm_kernel<NB <= 2 ? NB : 2, MT, 1, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
             else
@@ -573,6 +668,8 @@ int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
         qgemm_kernel<NB, MT, 2, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     } else if (a.a_f16) {
         qgemm_kernel<NB, MT, 3, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
+    } else if (a.a_lds) {
+        qgemm_kernel<NB, MT, 4, S, QI4_EPI_NONE, H><<<grid, threads, dyn, st>>>(a);
     } else if (NB <= 2 && a.a_f32) {
         qgemm_kernel<NB <= 2 ? NB : 2, MT, 1, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     } else {
@@ -772,6 +869,8 @@ int qlinear_impl(const void *x, int x_dtype, int64_t T, int64_t K, const void *p
     }
     a.moe = 0;
     a.T = T;
+    // few short bf16 rows: each workgroup converts them into LDS once
+    if (!w4a8 && !a.a_f32 && T * K * 2 + 16 + 4 * T <= kLdsActBytes) a.a_lds = 1;
     a.out = y;
     a.ldo = n_out;
     a.out_mode = y_dtype == QI4_F32 ? OUT_F32 : OUT_BF16;
