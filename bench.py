@@ -19,9 +19,13 @@ reports tokens/s of the main batch size, the roofline of the dominant kernel (gr
 and the oracle's CPU time on a bounded sample as a baseline.  Extra fields
 report the other decode batch sizes, the T=2048 prefill step (Zipf-skewed
 routing), with a cold last-level cache the dense linears (the Llama-7B-shaped
-decode stack at T=1 and the skinny sweep), the load-time quantizer, the router
-projection with its top-k, and the main decode step with 64-wide groups and with
-one group per row.
+decode stack at T=1 and the skinny sweep), the latency of the small float32
+GEMV, the load-time quantizer, the router projection with its top-k, and the
+main decode step with 64-wide groups and with one group per row.  `probes`
+holds the ceilings measured on the same machine (a 2 GiB streaming read and
+the fp16 matrix cores with no memory traffic), beside the published peaks the
+fractions are quoted against.  The CPU baseline gives the host's CPU model and
+a one-thread leg beside the all-thread one.
 """
 from __future__ import annotations
 
@@ -610,9 +614,21 @@ def run_quantize(q, torch, reps=10):
             "weights_per_s": N * K / t, "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(c, T, target_s):
     """The oracle (fp64 C, OpenMP over output rows) on a bounded sample of the
-    same workload: n tokens of layer 0, n chosen for about target_s seconds."""
+    same workload: n tokens of layer 0, n chosen for about target_s seconds on
+    all the host threads this process may use; then one token (or more, for
+    about target_s / 4 seconds) on a single thread."""
     import numpy as np
     import oracle
     import workloads
@@ -632,10 +648,24 @@ def cpu_baseline(c, T, target_s):
     t0 = time.perf_counter()
     oracle.moe(x64[:n], ids[:n], p[:n], ex, sh, c["H"], c["I"], c["E"], threads=threads)
     dt = time.perf_counter() - t0
+    # one thread: one token, then more tokens if that took under target_s / 4
+    t0 = time.perf_counter()
+    oracle.moe(x64[n:n + 1], ids[n:n + 1], p[n:n + 1], ex, sh, c["H"], c["I"], c["E"], threads=1)
+    one1 = time.perf_counter() - t0
+    n1 = int(max(1, min(Tmax - n - 1, (target_s / 4) // max(one1, 1e-3))))
+    if n1 > 1:
+        t0 = time.perf_counter()
+        oracle.moe(x64[n + 1:n + 1 + n1], ids[n + 1:n + 1 + n1], p[n + 1:n + 1 + n1], ex, sh,
+                   c["H"], c["I"], c["E"], threads=1)
+        dt1 = time.perf_counter() - t0
+    else:
+        n1, dt1 = 1, one1
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} tokens through the full layer 0 (routing, 8 experts + shared each), "
                       "one at a time as in decode",
-            "seconds": dt}
+            "seconds": dt, "cpu_model": cpu_model(),
+            "one_thread": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"{n1} other tokens of the same layer", "seconds": dt1}}
 
 
 def run_copy(torch, mib=1024, reps=20):
@@ -659,6 +689,75 @@ def run_copy(torch, mib=1024, reps=20):
     return {"bytes_per_launch": 2 * n, "us": us, "GBps": 2 * n / (us * 1e-6) / 1e9}
 
 
+def run_probes(q, torch, reps=10):
+    """The two ceilings, measured on this machine with the library's probes
+    (include/qi4_probe.h): a streaming read of a 2 GiB buffer (8x the 256 MB
+    last-level cache, so it comes from HBM) and the fp16 matrix cores on every
+    SIMD with no memory traffic (1024 workgroups of four waves, eight
+    independent MFMA 16x16x32 chains each).  Medians over reps, fence-free events."""
+    import statistics
+    buf = torch.ones(1 << 29, dtype=torch.float32, device="cuda")   # 2 GiB
+    nbytes = buf.numel() * 4
+    sink = torch.empty(q.PROBE_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    q.probe_stream_read(buf, sink)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record()
+        q.probe_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t_read = statistics.median(ts)
+    del buf
+    torch.cuda.empty_cache()
+    fsink = torch.empty(1, dtype=torch.float32, device="cuda")
+    iters, wgs = 4096, 1024
+    q.probe_mfma(64, wgs, fsink)
+    ts = []
+    for _ in range(5):
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record()
+        flops = q.probe_mfma(iters, wgs, fsink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t_mfma = statistics.median(ts)
+    return {"stream_read": {"bytes": nbytes, "us": t_read * 1e6, "GBps": nbytes / t_read / 1e9,
+                            "frac_of_published": nbytes / t_read / 1e9 / HBM_PEAK_GBPS},
+            "mfma_f16": {"flops": flops, "us": t_mfma * 1e6, "TFLOPs": flops / t_mfma / 1e12,
+                         "frac_of_published": flops / t_mfma / BF16_MFMA_PEAK}}
+
+
+def run_gemv_small(q, torch, reps=200):
+    """The small GEMV (T=1, K=256, N=128, float32 in and out, groups of 128):
+    a latency figure only (its 18.6 KB take nanoseconds at HBM speed).  Median of
+    single launches (warm), fence-free events enqueued behind a GPU spin."""
+    import statistics
+    import workloads
+    c = workloads.GEMV_SMALL
+    w = workloads.weights(c["seed"], 0, c["N"], c["K"], *c["scale"])
+    pw = _dense_pack(q, torch, w)
+    x = torch.from_numpy(workloads.activations(c["seed"], 0, c["T"], c["K"], "f32")).cuda()
+    y = torch.empty((c["T"], c["N"]), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        q.qlinear(x, pw, c["N"], out=y)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = TimingEvent(), TimingEvent()
+        # the GPU spins while the events and the launch are enqueued, so the
+        # interval holds the kernel and not the host's call
+        torch.cuda._sleep(200000)
+        e0.record()
+        q.qlinear(x, pw, c["N"], out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return {"workload": c["name"], "us_median": statistics.median(ts),
+            "us_p10": ts[len(ts) // 10], "us_p90": ts[(9 * len(ts)) // 10]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -676,6 +775,8 @@ def main():
 
     copy = run_copy(torch)
     log(f"copy: {json.dumps(copy)}")
+    probes = run_probes(q, torch)
+    log(f"probes: {json.dumps(probes)}")
     main_r = run_batch(q, torch, layers, c, args.T, args.steps, args.warmup)
     log(f"T={args.T}: {json.dumps(main_r)}")
     sweep = []
@@ -689,6 +790,8 @@ def main():
     prefill = None
     if args.prefill_steps > 0:
         prefill = run_prefill(q, torch, layers, args.prefill_steps, 2)
+        mfma_probe = probes["mfma_f16"]["TFLOPs"] * 1e12
+        prefill["mfma_frac_of_probe"] = prefill["mfma_frac_step"] * BF16_MFMA_PEAK / mfma_probe
         log(f"prefill: {json.dumps(prefill)}")
 
     dense = None
@@ -698,6 +801,9 @@ def main():
 
     quant = run_quantize(q, torch)
     log(f"quantize: {json.dumps(quant)}")
+
+    gemv = run_gemv_small(q, torch)
+    log(f"gemv small: {json.dumps(gemv)}")
 
     router = run_router(q, torch)
     log(f"router: {json.dumps(router)}")
@@ -741,7 +847,10 @@ def main():
                      "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gu_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "launch_us": main_r["gate_up_us"], "bytes_per_launch": main_r["gate_up_bytes"],
-                     "copy_GBps": copy["GBps"], "frac_of_copy": gu_gbps / copy["GBps"]},
+                     "copy_GBps": copy["GBps"], "frac_of_copy": gu_gbps / copy["GBps"],
+                     "probe_read_GBps": probes["stream_read"]["GBps"],
+                     "frac_of_probe_read": gu_gbps / probes["stream_read"]["GBps"]},
+        "probes": probes,
         "step_GBps": main_r["step_GBps"],
         "experts_touched_mean": main_r["experts_touched_mean"],
         "down_GBps": main_r["down_GBps"],
@@ -749,6 +858,7 @@ def main():
                                      "down_GBps", "experts_touched_mean")} for r in sweep],
         "prefill": prefill,
         "dense": dense,
+        "gemv_small_latency": gemv,
         "quantize": quant,
         "format_variants": groups,
         "w4a8_moe_decode": w4a8,

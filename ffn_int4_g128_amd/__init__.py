@@ -92,6 +92,9 @@ def lib():
             "moe_ffn_w4a8": (ci, [dp, vp, ctypes.c_float, ctypes.c_float, i64, vp, vp, vp, vp, vp,
                                   vp, vp, vp, vp, i64, vp]),
             "moe_ffn_int4_noalloc": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "qi4_probe_stream_read": (ci, [vp, i64, vp, vp]),
+            "qi4_probe_mfma": (ci, [i64, i64, vp, vp]),
+            "qi4_probe_mfma_flops": (i64, [i64, i64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -108,7 +111,11 @@ EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pac
             "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
             "moe_combine", "moe_ffn_int4", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_w4a8",
-            "moe_ffn_int4_noalloc"]
+            "moe_ffn_int4_noalloc",
+            # include/qi4_probe.h
+            "qi4_probe_stream_read", "qi4_probe_mfma", "qi4_probe_mfma_flops"]
+
+PROBE_READ_SINK_WORDS = 8192
 
 #: bytes of the scratch array moe_ffn_int4_noalloc holds on each GPU
 NOALLOC_SCRATCH_BYTES = 48 << 20
@@ -515,3 +522,24 @@ def moe_combine(y, weights, pair_to_sorted, T: int, w: MoeWeights, top_k: int, o
     _check(lib().moe_combine(ctypes.byref(d), _ptr(y), _ptr(weights), _ptr(pair_to_sorted), T,
                              _ptr(out), _stream(stream)), "moe_combine")
     return out
+
+
+# ---- measurement probes (include/qi4_probe.h) -----------------------------------
+
+def probe_stream_read(buf, sink=None, stream=None):
+    """Read every byte of the device tensor `buf` once (qi4_probe_stream_read)."""
+    import torch
+    if sink is None:
+        sink = torch.empty(PROBE_READ_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _check(lib().qi4_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                       _stream(stream)), "qi4_probe_stream_read")
+    return sink
+
+
+def probe_mfma(iters: int, workgroups: int, sink=None, stream=None) -> int:
+    """Run the matrix-core probe; returns the flops the launch performs."""
+    import torch
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    _check(lib().qi4_probe_mfma(iters, workgroups, _ptr(sink), _stream(stream)), "qi4_probe_mfma")
+    return int(lib().qi4_probe_mfma_flops(iters, workgroups))

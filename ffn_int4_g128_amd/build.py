@@ -13,7 +13,7 @@ BUILD = os.path.join(HERE, "_build")
 # per-kernel registers, scratch (spills), occupancy and LDS, from the compiler
 RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
 SOURCES = ["qi4_api.cpp", "qi4_pack.hip", "qi4_gemm.hip", "qi4_moe.hip", "qi4_prefill.hip",
-           "qi4_quant.hip"]
+           "qi4_quant.hip", "qi4_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are kept out of the generated code on purpose.

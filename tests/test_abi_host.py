@@ -7,13 +7,18 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qi4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("qi4.h", "qi4_probe.h")]
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)
+    """Functions declared in include/*.h, in header order."""
+    assert sorted(HEADERS) == sorted(os.path.join(ROOT, "include", h)
+                                     for h in os.listdir(os.path.join(ROOT, "include")))
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)
     kw = {"if", "sizeof", "defined"}
     return [n for n in dict.fromkeys(names) if n not in kw]
 
