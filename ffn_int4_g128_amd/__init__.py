@@ -91,6 +91,8 @@ def lib():
             "moe_ffn_w4a8_workspace_bytes": (i64, [dp, i64]),
             "moe_ffn_w4a8": (ci, [dp, vp, ctypes.c_float, ctypes.c_float, i64, vp, vp, vp, vp, vp,
                                   vp, vp, vp, vp, i64, vp]),
+            "moe_ffn_int4_share": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                        vp]),
             "moe_ffn_int4_noalloc": (ci, [dp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "qi4_probe_stream_read": (ci, [vp, i64, vp, vp]),
             "qi4_probe_mfma": (ci, [i64, i64, vp, vp]),
@@ -110,8 +112,8 @@ EXPORTED = ["qi4_abi_version", "qi4_status_string", "qi4_packed_bytes", "qi4_pac
             "moe_route_topk",
             "moe_route_sort", "moe_router_topk", "moe_sort_tokens",
             "moe_ffn_int4_workspace_bytes", "moe_expert_gate_up", "moe_expert_down",
-            "moe_combine", "moe_ffn_int4", "moe_ffn_w4a8_workspace_bytes", "moe_ffn_w4a8",
-            "moe_ffn_int4_noalloc",
+            "moe_combine", "moe_ffn_int4", "moe_ffn_int4_share", "moe_ffn_w4a8_workspace_bytes",
+            "moe_ffn_w4a8", "moe_ffn_int4_noalloc",
             # include/qi4_probe.h
             "qi4_probe_stream_read", "qi4_probe_mfma", "qi4_probe_mfma_flops"]
 
@@ -426,6 +428,33 @@ def moe_ffn(x, w: MoeWeights, top_k: int, logits=None, ids=None, weights=None, w
                               _ptr(w.w_gate_up), _ptr(w.w_down), _ptr(w.shared_gate_up),
                               _ptr(w.shared_down), _ptr(out), _ptr(workspace),
                               workspace.numel(), _stream(stream)), "moe_ffn_int4")
+    if return_routing:
+        return out, ids, weights
+    return out
+
+
+def moe_ffn_share(x, w: MoeWeights, top_k: int, gpu_experts, logits=None, ids=None,
+                  weights=None, workspace=None, out=None, return_routing: bool = False,
+                  stream=None):
+    """This device's share of the layer: the routed experts with gpu_experts[e]
+    nonzero (device uint8 [E]) plus the shared expert if w has one."""
+    import torch
+    _need(x, torch.bfloat16, "x")
+    _need(gpu_experts, torch.uint8, "gpu_experts")
+    T = x.shape[0]
+    d = w.desc(top_k)
+    if workspace is None:
+        workspace = moe_workspace(w, top_k, T, x.device)
+    if out is None:
+        out = torch.empty((T, w.H), dtype=torch.bfloat16, device=x.device)
+    if logits is not None and return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+        weights = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_ffn_int4_share(ctypes.byref(d), _ptr(x), T, _ptr(logits), _ptr(ids),
+                                    _ptr(weights), _ptr(w.w_gate_up), _ptr(w.w_down),
+                                    _ptr(w.shared_gate_up), _ptr(w.shared_down), _ptr(gpu_experts),
+                                    _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_ffn_int4_share")
     if return_routing:
         return out, ids, weights
     return out

@@ -175,8 +175,82 @@ router_gemm_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     }
 }
 
+// Router logits of decode batches (T <= kGemvMaxT): one workgroup per (expert,
+// group of up to four tokens), its four waves each taking a quarter of the
+// expert's row in 16-byte chunks (8 bf16, all loads of a lane issued before
+// they are used), float32 products summed in k order per lane, then a
+// fixed-pattern wave sum and the four waves added in order: deterministic, and
+// 256 experts keep 1024 waves or more streaming the matrix where the MFMA
+// kernel above has 16 workgroups.  Later token groups read the row from cache.
+constexpr int kGemvTokens = 4;
+constexpr int64_t kGemvMaxT = 64;
+constexpr int kGemvChunks = 8;   // chunks of 8 values per lane held in flight
+
+template <int TT>
+__global__ void __launch_bounds__(256)
+router_gemv_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int64_t T,
+                   int64_t H, int E, float *__restrict__ logits) {
+    __shared__ float part[4][TT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.y * TT;
+    const int nt = (int)(T - t0 < TT ? T - t0 : TT);   // tokens of this group
+    x += t0 * H;
+    logits += t0 * E;
+    const int64_t nch = H / 8, per = (nch + 3) / 4;
+    const int64_t c0 = wave * per, c1 = c0 + per < nch ? c0 + per : nch;
+    const uint16_t *wr = w + (int64_t)e * H;
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+    auto dot8 = [](uint4 a, uint4 b, float s) {
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s = fmaf(bf16_to_f32(av[i] & 0xFFFFu), bf16_to_f32(bv[i] & 0xFFFFu), s);
+            s = fmaf(bf16_to_f32(av[i] >> 16), bf16_to_f32(bv[i] >> 16), s);
+        }
+        return s;
+    };
+    for (int64_t c = c0 + lane; c < c1; c += 64 * kGemvChunks) {
+        uint4 wv[kGemvChunks], xv[kGemvChunks][TT];
+#pragma unroll
+        for (int u = 0; u < kGemvChunks; ++u) {
+            const int64_t cu = c + 64 * u;
+            const bool ok = cu < c1;
+            wv[u] = ok ? *reinterpret_cast<const uint4 *>(wr + 8 * cu) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                xv[u][t] = ok && t < nt ? *reinterpret_cast<const uint4 *>(x + t * H + 8 * cu)
+                                        : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kGemvChunks; ++u)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[t] = dot8(wv[u], xv[u][t], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) part[wave][t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+        const int t = threadIdx.x;
+        logits[(int64_t)t * E + e] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    }
+}
+
 int launch_router_gemm(const uint16_t *x, const uint16_t *w, int64_t T, int64_t H, int E,
                        float *logits, hipStream_t st) {
+    if (T <= kGemvMaxT) {
+        const dim3 g((unsigned)E, (unsigned)ceil_div(T, kGemvTokens));
+        if (T == 1) router_gemv_kernel<1><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
+        else if (T == 2) router_gemv_kernel<2><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
+        else if (T == 3) router_gemv_kernel<3><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
+        else router_gemv_kernel<4><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
+        return launch_status();
+    }
     const int MT = T <= 16 ? 1 : T <= 32 ? 2 : 4;
     const int64_t gy = ceil_div(T, 16 * MT);
     if (gy > 65535) return QI4_ERR_SHAPE;
@@ -442,6 +516,18 @@ combine_kernel(const float *__restrict__ y, const float *__restrict__ wts,
     *reinterpret_cast<uint2 *>(out + t * H + n4) = o;
 }
 
+// The routed pairs whose expert runs elsewhere get the id -1: the permutation
+// leaves them out and the combine skips them, so this device computes only its
+// own experts' share of the layer and reads only their weights.
+__global__ void __launch_bounds__(256)
+mask_ids_kernel(const int32_t *__restrict__ ids, int64_t npairs, const uint8_t *__restrict__ here,
+                int E, int32_t *__restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < npairs; i += (int64_t)gridDim.x * 256) {
+        const int32_t e = ids[i];
+        out[i] = (e >= 0 && e < E && here[e]) ? e : -1;
+    }
+}
+
 // ---- host helpers ------------------------------------------------------------------------
 
 int check_desc(const qi4_moe_desc *d) {
@@ -495,7 +581,7 @@ int64_t prefill_deferred_capacity(const qi4_moe_desc *d, const PrefillTiles &mt)
 // and every batch runs the decode GEMMs (no prefill regions).
 struct MoeWorkspace {
     int64_t ids, wts, sorted, offsets, p2s, active, h, y, x16, ex, h16, eh, tiles, ntiles, deferred,
-        x8, total;
+        x8, mids, total;
     MoeWorkspace(const qi4_moe_desc *d, int64_t T, bool w4a8 = false) {
         const int64_t P = T * d->top_k;
         const int64_t R = P + (d->has_shared ? T : 0);
@@ -520,6 +606,7 @@ struct MoeWorkspace {
         ntiles = o;  o += pf ? 256 : 0;
         deferred = o; o += pf ? align256(prefill_deferred_capacity(d, mt) * 16) : 0;
         x8 = o;      o += w4a8 ? align256(T * d->hidden) : 0;
+        mids = o;    o += align256(P * 4);   // ids with the experts of another device dropped
         total = o;
     }
 };
@@ -927,7 +1014,8 @@ bool good_scale(float s) { return s > 0.f && s < INFINITY && 1.0f / s < INFINITY
 int moe_ffn_impl(const qi4_moe_desc *d, const void *x, int64_t T, const float *router_logits,
                  int32_t *topk_ids, float *topk_weights, const void *w_gate_up, const void *w_down,
                  const void *shared_gate_up, const void *shared_down, void *out, void *workspace,
-                 int64_t ws_bytes, void *stream, const float *w4a8_scales) {
+                 int64_t ws_bytes, void *stream, const float *w4a8_scales,
+                 const uint8_t *gpu_experts = nullptr) {
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_T(T, d))) return rc;
@@ -966,7 +1054,17 @@ int moe_ffn_impl(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
     void *h = ws + L.h;
     float *y = reinterpret_cast<float *>(ws + L.y);
 
-    if (router_logits) {
+    if (gpu_experts) {
+        // a share of the experts: route in full (the caller's routing outputs
+        // keep every pair), then sort only the pairs of this device's experts
+        int32_t *mids = reinterpret_cast<int32_t *>(ws + L.mids);
+        if (router_logits && (rc = launch_route(router_logits, T, E, k, ids, wts, st))) return rc;
+        const int64_t np = T * k;
+        const unsigned gm = (unsigned)(ceil_div(np, 256) < 1024 ? ceil_div(np, 256) : 1024);
+        mask_ids_kernel<<<gm, 256, 0, st>>>(ids, np, gpu_experts, E, mids);
+        if ((rc = launch_status())) return rc;
+        if ((rc = launch_sort(mids, np, E, sorted, offsets, p2s, active, st))) return rc;
+    } else if (router_logits) {
         if ((rc = launch_route_sort(router_logits, T, E, k, ids, wts, sorted, offsets, p2s, active,
                                     st)))
             return rc;
@@ -1010,6 +1108,17 @@ int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
                  int64_t ws_bytes, void *stream) {
     return moe_ffn_impl(d, x, T, router_logits, topk_ids, topk_weights, w_gate_up, w_down,
                         shared_gate_up, shared_down, out, workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_ffn_int4_share(const qi4_moe_desc *d, const void *x, int64_t T,
+                       const float *router_logits, int32_t *topk_ids, float *topk_weights,
+                       const void *w_gate_up, const void *w_down, const void *shared_gate_up,
+                       const void *shared_down, const uint8_t *gpu_experts, void *out,
+                       void *workspace, int64_t ws_bytes, void *stream) {
+    if (!gpu_experts) return QI4_ERR_NULL;
+    return moe_ffn_impl(d, x, T, router_logits, topk_ids, topk_weights, w_gate_up, w_down,
+                        shared_gate_up, shared_down, out, workspace, ws_bytes, stream, nullptr,
+                        gpu_experts);
 }
 
 int64_t moe_ffn_w4a8_workspace_bytes(const qi4_moe_desc *d, int64_t T) {

@@ -308,6 +308,27 @@ int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T,
                  const void *shared_gate_up, const void *shared_down,
                  void *out, void *workspace, int64_t ws_bytes, void *stream);
 
+/* This device's share of the layer, for a layer whose experts are split
+ * between devices (the fastllm README's --moe_device places a share of the MoE
+ * work on the GPU and the rest on the CPU; the tencentcloud guide's single-GPU
+ * plus CPU configuration splits it as {'cuda':1,'cpu':19}):
+ *   out[t] = sum over j with gpu_experts[ids[t][j]] != 0 of p[t][j] * FFN_{ids[t][j]}(x_t)
+ *            + FFN_shared(x_t) if d->has_shared.
+ * gpu_experts: device uint8 [E], nonzero for the routed experts computed here;
+ * only their weights are read (the others' blocks of w_gate_up / w_down may
+ * hold anything).  The routing is computed (or given) in full, and when the
+ * logits are given topk_ids / topk_weights, if not NULL, receive all of it, so
+ * the other device can compute the remaining experts; the outputs of the two
+ * shares add up to moe_ffn_int4's output.  Arguments, workspace
+ * (moe_ffn_int4_workspace_bytes) and errors otherwise as moe_ffn_int4;
+ * gpu_experts NULL is QI4_ERR_NULL. */
+int moe_ffn_int4_share(const qi4_moe_desc *d, const void *x, int64_t T,
+                       const float *router_logits, int32_t *topk_ids, float *topk_weights,
+                       const void *w_gate_up, const void *w_down,
+                       const void *shared_gate_up, const void *shared_down,
+                       const uint8_t *gpu_experts, void *out, void *workspace, int64_t ws_bytes,
+                       void *stream);
+
 /* W4A8 MoE layer: moe_ffn_int4 with int8 activations in both projections (the
  * FastDeploy page, x-techcon, applies W4A8 static quantization to MoE layers).
  * Static scales, as in qlinear_w4a8: the layer input x is quantized with

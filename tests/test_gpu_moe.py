@@ -287,7 +287,9 @@ def test_dsv3_layer_is_deterministic(dsv3, T):
 
 
 @pytest.mark.parametrize("T,E,H,k", [(1, 256, 7168, 8), (32, 256, 7168, 8), (5, 64, 512, 4),
-                                     (70, 300, 1024, 8), (2048, 256, 7168, 8), (3, 8, 32, 8)])
+                                     (70, 300, 1024, 8), (2048, 256, 7168, 8), (3, 8, 32, 8),
+                                     # the decode path's last token count and the first past it
+                                     (64, 256, 1024, 8), (65, 256, 1024, 8), (2, 17, 96, 3)])
 def test_router_logits_and_topk(T, E, H, k):
     """Router projection within 2e-3 * sum|x*w| of the oracle; the selection on the
     GPU's logits bit for bit (the same decision in the same precision), and valid
