@@ -21,7 +21,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libqi4_oracle.so")
+#: the compiled oracle; QI4O_LIB names another build of it (the sanitizer build,
+#: or a deliberately broken copy that the pins must reject)
+_LIB_PATH = os.environ.get("QI4O_LIB") or os.path.join(_HERE, "libqi4_oracle.so")
 _lib = None
 
 #: relative tolerance factor of one linear layer: |gpu - oracle| <= C_TOL * sum|w*x|
