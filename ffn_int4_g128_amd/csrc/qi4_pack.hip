@@ -2,9 +2,9 @@
 // into the device layout, its exact inverse, and an exact float32
 // dequantization.
 //
-// The pages store the codes "group by group, so inference reads one contiguous
-// span" ("FastLLM: zero-dependency CPU inference framework", section 3.1).  On
-// CDNA4 the unit that must be contiguous is one wave load: 64 lanes x 16 bytes.
+// The FastLLM page (section 3.1) keeps the codes of a group together in memory
+// so that the product streams through contiguous bytes.  On CDNA4 the unit
+// that must be contiguous is one wave load: 64 lanes x 16 bytes.
 // Each (16-row tile, 128-wide group) block is exactly that kilobyte, ordered so
 // that lane 16*j + r receives row r's codes for the k values its MFMA operand
 // fragment consumes (see qi4.h for the full description).

@@ -4,11 +4,11 @@
  * and routed mixture-of-experts FFN for AMD MI355X (gfx950).
  *
  * What is computed follows these pages:
- *  - "FastLLM: zero-dependency CPU inference framework ..." (pgsm.cn),
- *    section 3.1 "4-bit quantization and weight reordering": weights are 4-bit
- *    codes in groups of 128 that share one scale and one zero point, stored
- *    group by group so the product reads contiguous memory, and the product
- *    runs "read 4-bit weight -> dequantize -> multiply" with no extra pass;
+ *  - FastLLM: zero-dependency CPU inference framework (pgsm.cn), section 3.1
+ *    (4-bit quantization and weight reordering): weights are 4-bit codes in
+ *    groups of 128 sharing one scale and one zero point, kept group after group
+ *    in memory so the product reads them contiguously, and each weight is
+ *    dequantized on the fly inside the product rather than in a separate pass;
  *    section 2.3: the matrix multiply is a core operator below the model layer.
  *    Section 4.2 "model conversion and format": the group size defaults to 128;
  *    64 and 256 are allowed; codes are 4 or 8 bits wide (--quant-bit).
@@ -154,7 +154,11 @@ int qi4_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int group_siz
 int qi4_quantize_int8(const void *w, int w_dtype, int64_t N, int64_t K, int group_size,
                       uint8_t *qweight, uint16_t *scales, uint8_t *zeros, void *stream);
 
-/* The linear layer: y[t][n'] = epilogue( sum_k x[t][k] * dequant(W)[n][k] ).
+/* The linear layer: y[t][n'] = epilogue( sum_k x[t][k] * dequant(W)[n][k] ), with
+ * dequant(W)[n][k] = scale * (q - zero) for the 128-wide group of k in row n
+ * (FastLLM page, section 3.1: 4-bit weights in groups of 128 with a scale and a
+ * zero point, dequantized inside the product; decode reads every weight again
+ * for every token, which makes this call bound by the weight stream).
  *   x        [T][K] of x_dtype (QI4_BF16 or QI4_F32), row-major, contiguous
  *   packed_w packed N x K matrix (flags as given to qi4_pack)
  *   y        [T][N'] of y_dtype (QI4_BF16 or QI4_F32);
@@ -220,7 +224,9 @@ typedef struct {
 } qi4_moe_desc;            /* host struct                                       */
 
 /* Router: for each token the top_k largest logits in descending order (ties to
- * the lower expert index) and softmax weights over those top_k only.
+ * the lower expert index) and softmax weights over those top_k only (the
+ * FastLLM notes, wmrh.cn, part 1: each token activates a few of a MoE layer's
+ * experts; the fastllm README's --moe_experts sets how many).
  *   logits [T][E] float32;  topk_ids [T][top_k] int32;  topk_weights [T][top_k] float32
  * Logits must not be NaN. */
 int moe_route_topk(const float *logits, int64_t T, int64_t E, int32_t top_k,
@@ -247,7 +253,9 @@ int moe_router_topk(const void *x, int64_t T, int64_t H, const void *w_router, i
                     void *stream);
 
 /* Token-by-expert permutation (stable counting sort of the T*top_k pairs
- * p = t*top_k + j by expert):
+ * p = t*top_k + j by expert), so that each touched expert's weights are read
+ * once for all of its tokens (the MoE layer activates few experts per token:
+ * FastLLM notes, wmrh.cn, part 1):
  *   sorted_pairs   [T*top_k]  pairs grouped by expert ascending, tokens ascending
  *   expert_offsets [E+1]      segment starts; expert_offsets[E] = T*top_k
  *   pair_to_sorted [T*top_k]  inverse permutation
@@ -292,7 +300,10 @@ int moe_expert_down(const qi4_moe_desc *d, const void *h, int64_t T,
 int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights,
                 const int32_t *pair_to_sorted, int64_t T, void *out, void *stream);
 
-/* out[t] = sum_j p[t][j] * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t).
+/* The MoE expert FFN layer (the fastllm README's MoE options: --moe_experts
+ * routed experts per token, --cuda_se the shared expert; FastLLM notes, wmrh.cn,
+ * part 1), with every expert int4 group-quantized as in qlinear_int4_g128:
+ * out[t] = sum_j p[t][j] * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t).
  *   x    [T][H] bf16 bits;  out [T][H] bf16 bits
  *   router_logits [T][E] float32, or NULL: then topk_ids/topk_weights
  *                 ([T][top_k] int32 / float32) supply the routing.  When the

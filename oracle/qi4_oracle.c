@@ -8,10 +8,10 @@
  * (ffn_int4_g128_amd/csrc); neither includes nor links the other.
  *
  * Sources (cited by page title and section):
- *  [P3] "FastLLM: zero-dependency CPU inference framework ..." (pgsm.cn),
- *       section 3.1 "4-bit quantization and weight reordering": 4-bit weights in
- *       groups of 128 that share one scale and one zero point; the pipeline
- *       "read 4-bit weight -> dequantize to FP32 -> matrix multiply";
+ *  [P3] FastLLM: zero-dependency CPU inference framework (pgsm.cn),
+ *       section 3.1 (4-bit quantization and weight reordering): 4-bit weights in
+ *       groups of 128 that share one scale and one zero point; each weight is
+ *       dequantized to float32 and then enters the matrix product;
  *       section 4.2 "model conversion and format": --quant-bit 4/8,
  *       --group-size default 128, 64/256 allowed.
  *  [P1] fastllm README (gittoolsai.com), "other parameters": --moe_experts
