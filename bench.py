@@ -10,9 +10,12 @@ reads its experts from HBM rather than from the 256 MB last-level cache, and
 every step routes a different batch of tokens.  Inputs are seeded synthetic
 data already resident in HBM when timing starts.
 
-The step runs the five stages through the C ABI (route, sort, grouped
-gate/up + SiLU, grouped down, combine); HIP events on the launch stream time
-each grouped GEMM inside the timed region.  The events are created without a
+The timed step is one `moe_ffn_int4` call through the C ABI (routing with the
+permutation and the layer input's fp16 rows in one launch, grouped gate/up +
+SiLU, h rows, grouped down, combine).  The same steps then run once more as
+the stage calls (`moe_route_sort`, `moe_expert_gate_up`, `moe_expert_down`,
+`moe_combine`: the same kernels and launch shapes), where HIP events on the
+launch stream time each grouped GEMM; those times give the roofline.  The events are created without a
 system-scope fence (TimingEvent): a fenced event writes back and invalidates the
 caches at every record, a 5-6 us gap that no real forward pays.  The JSON line
 reports tokens/s of the main batch size, the roofline of the dominant kernel (grouped gate/up),
@@ -197,9 +200,10 @@ def run_group_variants(q, torch, c, T, steps, warmup):
 
 
 class Stepper:
-    """Runs the stages of one MoE forward through the C ABI (routing with the
-    permutation, gate/up, down, combine), with events around the two grouped
-    GEMMs."""
+    """One MoE forward through the C ABI, either as the one call
+    (`moe_ffn_int4`: routing with the permutation and the input rows, gate/up,
+    down, combine) or as the stage calls with events around the two grouped
+    GEMMs (the same kernels and launch shapes)."""
 
     def __init__(self, q, torch, layers, T, top_k, n_batches, c, zipf=None):
         import numpy as np
@@ -258,6 +262,31 @@ class Stepper:
         q._check(L.moe_combine(dref, P(self.y), P(self.wts), P(self.inv), T, P(self.out), st),
                  "combine")
 
+    def call(self, i):
+        """Step i as one moe_ffn_int4 call."""
+        q = self.q
+        mw = self.layers[i % len(self.layers)]
+        b = (i // len(self.layers)) % self.n_batches
+        import ctypes
+        d = mw.desc(self.k)
+        P = q._ptr
+        q._check(q.lib().moe_ffn_int4(ctypes.byref(d), P(self.x[b]), self.T, P(self.logits[b]),
+                                      None, None, P(mw.w_gate_up), P(mw.w_down),
+                                      P(mw.shared_gate_up), P(mw.shared_down), P(self.out),
+                                      P(self.ws), self.ws.numel(), q._stream()), "moe_ffn_int4")
+
+    def timed_calls(self, steps, warmup):
+        """Wall seconds of `steps` one-call steps after `warmup` untimed ones,
+        bracketed by device synchronizations."""
+        for i in range(warmup):
+            self.call(i)
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.call(i)
+        self.torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
     def touched(self, i):
         """Routed experts touched by step i (read back outside any timed region)."""
         self.step(i)
@@ -276,6 +305,9 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     s = Stepper(q, torch, layers, T, k, n_batches, c)
     period = len(layers) * n_batches
     touched = [s.touched(i) for i in range(period)]
+    # the step: one moe_ffn_int4 call
+    wall = s.timed_calls(steps, warmup)
+    # the same steps through the stage calls, events around the grouped GEMMs
     for i in range(warmup):
         s.step(i)
     torch.cuda.synchronize()
@@ -285,7 +317,7 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     for i in range(steps):
         s.step(i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_stages = time.perf_counter() - t0
     gu_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     H, I = c["H"], c["I"]
@@ -306,6 +338,7 @@ def run_batch(q, torch, layers, c, T, steps, warmup, n_batches=8):
     ms_step = wall * 1e3 / steps
     return {
         "T": T, "ms_per_step": ms_step, "tokens_per_s": T * steps / wall,
+        "stages_ms_per_step": wall_stages * 1e3 / steps,
         "experts_touched_mean": mean([touched[i % period] for i in range(steps)]) + 1,
         "step_GBps": mean(step_bytes) / (ms_step * 1e-3) / 1e9,
         "gate_up_us": mean(gu_ms) * 1e3, "down_us": mean(dn_ms) * 1e3,
@@ -368,6 +401,7 @@ def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
     s = Stepper(q, torch, layers, T, k, n_batches, c, zipf=p["zipf"])
     period = len(layers) * n_batches
     touched = [s.touched(i) for i in range(period)]
+    wall = s.timed_calls(steps, warmup)
     for i in range(warmup):
         s.step(i)
     evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
@@ -376,7 +410,7 @@ def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
     for i in range(steps):
         s.step(i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_stages = time.perf_counter() - t0
     gu = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
     dn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
     per_w = workloads.packed_weight_bytes(1)
@@ -386,6 +420,7 @@ def run_prefill(q, torch, layers, steps, warmup, n_batches=2):
     bytes_step = n_e * 3 * I * H * per_w + 2 * T * H * 2
     ms = wall * 1e3 / steps
     return {"T": T, "workload": "moe_ffn_prefill_deepseekv3_shape_zipf1.1", "ms_per_step": ms,
+            "stages_ms_per_step": wall_stages * 1e3 / steps,
             "tokens_per_s": T * steps / wall, "experts_touched_mean": n_e,
             "mfma_frac_step": (flop_gu + flop_dn) / (ms * 1e-3) / BF16_MFMA_PEAK,
             "hbm_GBps_step": bytes_step / (ms * 1e-3) / 1e9,
@@ -418,6 +453,17 @@ def run_dense(q, torch, reps=100):
     acc = torch.empty((), dtype=torch.float32, device="cuda")
 
     spread = {}
+    sink = torch.empty(q.PROBE_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+
+    def read_probe_us(nbytes):
+        """Cold median (us) of the read probe over a buffer of nbytes: a plain
+        streaming read of the same number of bytes, the floor for one launch
+        that reads a matrix of that size."""
+        buf = torch.ones((nbytes + 15) // 16 * 4, dtype=torch.int32, device="cuda")
+        fn = lambda: q.probe_stream_read(buf, sink)
+        t = timed(fn)
+        spread.pop(fn)
+        return t * 1e6
 
     def timed(fn):
         """Cold median in seconds; its p10 / p90 and the warm mean (us) are kept
@@ -472,8 +518,10 @@ def run_dense(q, torch, reps=100):
         b = N * K * per_w + K * 2 + n_out * 2
         stack_bytes += b
         t = timed(f)
+        pr = read_probe_us(int(N * K * per_w))
         per.append({"linear": name, "N": N, "K": K, "us": t * 1e6,
-                    "GBps": b / t / 1e9, **spread.pop(f)})
+                    "GBps": b / t / 1e9, **spread.pop(f), "read_probe_us": pr,
+                    "frac_of_read_probe": pr / (t * 1e6)})
     del graph, lin, calls
     stack = {"workload": "llama7b_decode_stack_t1", "bytes": stack_bytes,
              "eager_us": t_eager * 1e6, "eager_tokens_per_s": 1.0 / t_eager,
@@ -481,13 +529,16 @@ def run_dense(q, torch, reps=100):
              "graph_us": t_graph * 1e6, "graph_tokens_per_s": 1.0 / t_graph,
              "graph_GBps": stack_bytes / t_graph / 1e9,
              "graph_hbm_frac": stack_bytes / t_graph / 1e9 / HBM_PEAK_GBPS,
-             "eager_spread": eager_spread, "graph_spread": graph_spread, "linears": per}
+             "eager_spread": eager_spread, "graph_spread": graph_spread, "linears": per,
+             "read_probe_us": sum(l["read_probe_us"] for l in per)}
+    stack["frac_of_read_probe"] = stack["read_probe_us"] / stack["eager_us"]
 
     c2 = workloads.SKINNY_SWEEP
     sweep = []
     for i, (K, N) in enumerate(c2["shapes"]):
         w = workloads.weights(c2["seed"], 10 + i, N, K, *c2["scale"])
         pw = _dense_pack(q, torch, w)
+        pr = read_probe_us(int(N * K * per_w))
         for T in c2["T"]:
             x = q_bf16(torch, workloads.activations(c2["seed"], 20 + 10 * i + T, T, K, "bf16",
                                                     c2["x_scale"]))
@@ -497,7 +548,8 @@ def run_dense(q, torch, reps=100):
             b = N * K * per_w + T * K * 2 + T * N * 2
             sweep.append({"K": K, "N": N, "T": T, "us": t * 1e6,
                           "GBps": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBPS,
-                          "tokens_per_s": T / t, **spread.pop(fn)})
+                          "tokens_per_s": T / t, **spread.pop(fn), "read_probe_us": pr,
+                          "frac_of_read_probe": pr / (t * 1e6)})
         del pw
     # the same shapes with 8-bit codes (groups of 128), quantized on the GPU
     # from N(0, 0.02^2) bf16 weights
@@ -545,7 +597,8 @@ def run_dense(q, torch, reps=100):
     torch.cuda.empty_cache()
     return {"protocol": "1 GiB read before each rep (outside the events); median of "
                         f"{reps} reps (us), with p10_us / p90_us; warm_us: mean of 50 launches "
-                        "back to back without the flush", "llama7b_stack": stack, "skinny_sweep": sweep,
+                        "back to back without the flush; read_probe_us: the read probe over "
+                        "the matrix's packed bytes, same protocol", "llama7b_stack": stack, "skinny_sweep": sweep,
             "skinny_sweep_int8": sweep8, "skinny_sweep_w4a8": sweep_w4a8}
 
 

@@ -56,6 +56,7 @@ struct GemmArgs {
     int64_t n_out;             // valid output columns
     // set by launch_qgemm
     int blocks_per_wg;         // consecutive tile blocks one workgroup streams
+    int64_t m_rows;            // dense: rows per workgroup along grid.y (0: all T in one)
 };
 
 // Largest activation matrix (bytes of its fp16 rows) a dense call converts into

@@ -36,6 +36,7 @@ namespace qi4 {
 namespace {
 
 constexpr int kMaxWaves = 8;
+constexpr bool kDenseMSplit = true;   // see launch_qgemm
 // (wave, m, nb) partial tiles the LDS reduction buffer holds: 16 (16 KiB), or
 // 32 for a quad of tiles over two M tiles (the only shape that needs more; the
 // others keep the smaller buffer so that LDS never caps their occupancy).
@@ -112,9 +113,11 @@ qgemm_kernel(const GemmArgs args) {
     int64_t row0, n, src0 = 0;
     const int32_t *gather = nullptr;
     if (!args.moe) {
+        // one dense problem; with m_rows, grid.y splits its rows
         w = args.w;
-        row0 = 0;
-        n = args.T;
+        row0 = args.m_rows > 0 ? (int64_t)blockIdx.y * args.m_rows : 0;
+        n = args.m_rows > 0 && args.T - row0 > args.m_rows ? args.m_rows : args.T - row0;
+        src0 = row0;
     } else {
         const int py = blockIdx.y;
         if (py < args.routed_slots) {
@@ -706,7 +709,7 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     // Expert problems mostly hold a few slots each: one M tile per pass keeps
     // registers low; a problem with more slots (the shared expert) takes more
     // passes.  A single matrix with more than 16 rows uses two M tiles.
-    const int MT = (n_problems == 1 && max_slots > spt) ? 2 : 1;
+    int MT = (n_problems == 1 && max_slots > spt) ? 2 : 1;
     const bool silu = args.epi == QI4_EPI_SILU_MUL;
     // (a single matrix takes two tiles per workgroup from 320 tiles up: cold-cache
     // sweeps of 4096..22016-row matrices put the crossover between 256 and 320)
@@ -730,16 +733,29 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
     }
-    while (W > 1 && W * MT * NB > red_slots(NB, MT)) W /= 2;
+    // a dense matrix whose rows span two M tiles and whose activations are
+    // converted in registers: one M tile per workgroup, grid.y over the M
+    // tiles (twice the workgroups, each converting half the rows).  The
+    // workgroups of one tile block are gx apart in dispatch order: on the same
+    // XCD when gx is a multiple of 8, where the later ones find the weights in
+    // that XCD's L2.
+    int64_t gy = n_problems;
     GemmArgs a = args;
+    a.m_rows = 0;
+    if (!args.moe && MT == 2 && !args.a_lds && kDenseMSplit) {
+        MT = 1;
+        a.m_rows = spt;
+        gy = ceil_div(max_slots, (int64_t)spt);
+    }
+    while (W > 1 && W * MT * NB > red_slots(NB, MT)) W /= 2;
     a.blocks_per_wg = R;
     // pair / top_k as a multiply-high: with m = floor((2^32 - 1) / k) + 1,
     // floor(p * m / 2^32) = floor(p / k) whenever p * k < 2^32 (pairs are below
     // 2^31 / 32 and top_k is at most 32); k = 1 (m = 2^32) is taken apart
     a.topk_magic = a.top_k > 1 ? (uint32_t)(0xFFFFFFFFull / (uint32_t)a.top_k + 1ull) : 0u;
     const int64_t gx = ceil_div(ceil_div(nt, NB), R);
-    if (gx > 0x7fffffff || n_problems > 65535) return QI4_ERR_SHAPE;
-    dim3 grid((unsigned)gx, (unsigned)n_problems);
+    if (gx > 0x7fffffff || gy > 65535) return QI4_ERR_SHAPE;
+    dim3 grid((unsigned)gx, (unsigned)gy);
     const int threads = W * 64;
     if (MT == 1) {
         if (NB == 4) return launch_cfg<4, 1, 2>(a, grid, threads, st);

@@ -19,6 +19,7 @@
 #include "qi4_gemm.h"
 #include "qi4_host.h"
 #include "qi4_prefill.h"
+#include "qi4_rows.h"
 
 namespace qi4 {
 namespace {
@@ -313,11 +314,29 @@ __device__ inline void route_token(const float *__restrict__ logits, int64_t t, 
     }
 }
 
-// One wave per token.
+// The layer input's rows as fp16 with per-row exponents (prep_row), done by
+// the workgroups of a routing launch past its routing ones, so the layer call
+// needs no launch of its own for them.  x == nullptr: none.
+struct RowPrep {
+    const uint16_t *x;
+    int64_t len;
+    uint16_t *x16;
+    int32_t *ex;
+};
+
+// One wave per token; workgroups from route_blocks on prepare row
+// blockIdx.x - route_blocks of the layer input.
 template <int VPL>
 __global__ void __launch_bounds__(kRouteWaves * 64)
 route_kernel(const float *__restrict__ logits, int64_t T, int E, int k,
-             int32_t *__restrict__ ids, float *__restrict__ wts) {
+             int32_t *__restrict__ ids, float *__restrict__ wts, int64_t route_blocks,
+             RowPrep prep) {
+    if (blockIdx.x >= route_blocks) {
+        __shared__ float wmax[kRouteWaves];
+        prep_row<kRouteWaves * 64>(prep.x, 0, prep.len, blockIdx.x - route_blocks, prep.x16,
+                                   prep.ex, wmax);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
     if (t >= T) return;   // whole waves leave: the rest stay fully active
@@ -448,12 +467,19 @@ sort_kernel(const int32_t *__restrict__ ids, int64_t npairs, int E, int nbits,
 // tables and to pass the barriers.
 constexpr int kFusedWaves = 16;
 constexpr int kFusedPairs = kFusedWaves * kMaxTopK;
+// Workgroups 1 .. T (when prep.x is given) prepare the layer input's rows.
 template <int VPL, int W>
 __global__ void __launch_bounds__(W * 64)
 route_sort_kernel(const float *__restrict__ logits, int64_t T, int E, int k, int nbits,
                   int32_t *__restrict__ ids, float *__restrict__ wts,
                   int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ offsets,
-                  int32_t *__restrict__ pair_to_sorted, int32_t *__restrict__ active) {
+                  int32_t *__restrict__ pair_to_sorted, int32_t *__restrict__ active,
+                  RowPrep prep) {
+    if (blockIdx.x > 0) {
+        __shared__ float wmax[W];
+        prep_row<W * 64>(prep.x, 0, prep.len, blockIdx.x - 1, prep.x16, prep.ex, wmax);
+        return;
+    }
     __shared__ int cnt[W][kMaxExperts];
     __shared__ int off_s[kMaxExperts + 1];
     __shared__ int tot_s[kMaxExperts];
@@ -617,17 +643,19 @@ int bits_for(int64_t E) {
     return b;
 }
 
+// prep.x given: T more workgroups prepare the layer input's rows.
 int launch_route(const float *logits, int64_t T, int E, int k, int32_t *ids, float *wts,
-                 hipStream_t st) {
-    const int64_t blocks = ceil_div(T, kRouteWaves);
+                 hipStream_t st, RowPrep prep = {}) {
+    const int64_t rb = ceil_div(T, kRouteWaves);
+    const int64_t blocks = rb + (prep.x ? T : 0);
     if (blocks > 0x7fffffff) return QI4_ERR_SHAPE;
     const int vpl = (E + 63) / 64;
     const dim3 g((unsigned)blocks), b(kRouteWaves * 64);
-    if (vpl <= 1) route_kernel<1><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
-    else if (vpl <= 2) route_kernel<2><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
-    else if (vpl <= 4) route_kernel<4><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
-    else if (vpl <= 8) route_kernel<8><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
-    else route_kernel<16><<<g, b, 0, st>>>(logits, T, E, k, ids, wts);
+    if (vpl <= 1) route_kernel<1><<<g, b, 0, st>>>(logits, T, E, k, ids, wts, rb, prep);
+    else if (vpl <= 2) route_kernel<2><<<g, b, 0, st>>>(logits, T, E, k, ids, wts, rb, prep);
+    else if (vpl <= 4) route_kernel<4><<<g, b, 0, st>>>(logits, T, E, k, ids, wts, rb, prep);
+    else if (vpl <= 8) route_kernel<8><<<g, b, 0, st>>>(logits, T, E, k, ids, wts, rb, prep);
+    else route_kernel<16><<<g, b, 0, st>>>(logits, T, E, k, ids, wts, rb, prep);
     return launch_status();
 }
 
@@ -643,24 +671,27 @@ int launch_sort(const int32_t *ids, int64_t npairs, int E, int32_t *sorted, int3
     return launch_status();
 }
 
-// Routing then sort: one fused workgroup for decode batches, else the two kernels.
+// Routing then sort: one fused workgroup for decode batches, else the two
+// kernels.  prep.x given: the same launch also prepares the layer input's rows
+// (T more workgroups).
 int launch_route_sort(const float *logits, int64_t T, int E, int k, int32_t *ids, float *wts,
                       int32_t *sorted, int32_t *offsets, int32_t *p2s, int32_t *active,
-                      hipStream_t st) {
+                      hipStream_t st, RowPrep prep = {}) {
     if (T > kFusedWaves || T * k > kFusedPairs) {
-        int rc = launch_route(logits, T, E, k, ids, wts, st);
+        int rc = launch_route(logits, T, E, k, ids, wts, st, prep);
         if (rc) return rc;
         return launch_sort(ids, T * k, E, sorted, offsets, p2s, active, st);
     }
     const int vpl = (E + 63) / 64, nb = bits_for(E);
+    const unsigned g = 1 + (prep.x ? (unsigned)T : 0u);
     auto go = [&](auto w) {
         constexpr int W = decltype(w)::value;
         const unsigned tb = W * 64;
-        if (vpl <= 1) route_sort_kernel<1, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-        else if (vpl <= 2) route_sort_kernel<2, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-        else if (vpl <= 4) route_sort_kernel<4, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-        else if (vpl <= 8) route_sort_kernel<8, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
-        else route_sort_kernel<16, W><<<1, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active);
+        if (vpl <= 1) route_sort_kernel<1, W><<<g, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active, prep);
+        else if (vpl <= 2) route_sort_kernel<2, W><<<g, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active, prep);
+        else if (vpl <= 4) route_sort_kernel<4, W><<<g, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active, prep);
+        else if (vpl <= 8) route_sort_kernel<8, W><<<g, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active, prep);
+        else route_sort_kernel<16, W><<<g, tb, 0, st>>>(logits, T, E, k, nb, ids, wts, sorted, offsets, p2s, active, prep);
     };
     if (T <= 4) go(std::integral_constant<int, 4>());
     else go(std::integral_constant<int, kFusedWaves>());
@@ -782,16 +813,18 @@ int grouped_problems(GemmArgs &a, const qi4_moe_desc *d, int64_t T) {
 
 // The two projections of the expert FFN on either path.  `ws` is the moe_ffn_int4
 // workspace (only its prefill regions are used here).
+// x_ready: the workspace already holds the input rows as fp16 (prepared by the
+// routing launch).
 int run_gate_up(const qi4_moe_desc *d, const void *x, int64_t T, const int32_t *sorted,
                 const int32_t *offsets, const int32_t *active, const void *w_gu, const void *sh_gu,
-                void *h, uint8_t *ws, hipStream_t st) {
+                void *h, uint8_t *ws, hipStream_t st, bool x_ready = false) {
     int rc;
     // the input rows once as fp16 with a per-row power of two (exact), for
     // every expert's GEMM
     const MoeWorkspace L(d, T);
     uint16_t *x16 = reinterpret_cast<uint16_t *>(ws + L.x16);
     int32_t *ex = reinterpret_cast<int32_t *>(ws + L.ex);
-    if ((rc = launch_prep_rows(x, 0, T, d->hidden, x16, ex, st))) return rc;
+    if (!x_ready && (rc = launch_prep_rows(x, 0, T, d->hidden, x16, ex, st))) return rc;
     if (T < kPrefillMinT) {
         GemmArgs a = gate_up_args(d, x16, T, sorted, offsets, active, w_gu, sh_gu, h);
         a.a_f16 = 1;
@@ -1054,20 +1087,35 @@ int moe_ffn_impl(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
     void *h = ws + L.h;
     float *y = reinterpret_cast<float *>(ws + L.y);
 
+    bool x_ready = false;
     if (gpu_experts) {
         // a share of the experts: route in full (the caller's routing outputs
         // keep every pair), then sort only the pairs of this device's experts
         int32_t *mids = reinterpret_cast<int32_t *>(ws + L.mids);
-        if (router_logits && (rc = launch_route(router_logits, T, E, k, ids, wts, st))) return rc;
+        if (router_logits) {
+            RowPrep prep = {};
+            if (!w4a8)
+                prep = {static_cast<const uint16_t *>(x), H,
+                        reinterpret_cast<uint16_t *>(ws + L.x16),
+                        reinterpret_cast<int32_t *>(ws + L.ex)};
+            if ((rc = launch_route(router_logits, T, E, k, ids, wts, st, prep))) return rc;
+            x_ready = !w4a8;
+        }
         const int64_t np = T * k;
         const unsigned gm = (unsigned)(ceil_div(np, 256) < 1024 ? ceil_div(np, 256) : 1024);
         mask_ids_kernel<<<gm, 256, 0, st>>>(ids, np, gpu_experts, E, mids);
         if ((rc = launch_status())) return rc;
         if ((rc = launch_sort(mids, np, E, sorted, offsets, p2s, active, st))) return rc;
     } else if (router_logits) {
+        // the bf16 path's input rows are prepared by the routing launch
+        RowPrep prep = {};
+        if (!w4a8)
+            prep = {static_cast<const uint16_t *>(x), H, reinterpret_cast<uint16_t *>(ws + L.x16),
+                    reinterpret_cast<int32_t *>(ws + L.ex)};
         if ((rc = launch_route_sort(router_logits, T, E, k, ids, wts, sorted, offsets, p2s, active,
-                                    st)))
+                                    st, prep)))
             return rc;
+        x_ready = !w4a8;
     } else if ((rc = launch_sort(ids, T * k, E, sorted, offsets, p2s, active, st))) {
         return rc;
     }
@@ -1092,7 +1140,8 @@ int moe_ffn_impl(const qi4_moe_desc *d, const void *x, int64_t T, const float *r
         if ((rc = launch_qgemm(b, grouped_problems(b, d, T), T, st))) return rc;
         return launch_combine(d, y, wts, p2s, T, out, st);
     }
-    if ((rc = run_gate_up(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h, ws, st)))
+    if ((rc = run_gate_up(d, x, T, sorted, offsets, active, w_gate_up, shared_gate_up, h, ws, st,
+                          x_ready)))
         return rc;
     if ((rc = run_down(d, h, T, offsets, active, w_down, shared_down, y, ws, st))) return rc;
     return launch_combine(d, y, wts, p2s, T, out, st);

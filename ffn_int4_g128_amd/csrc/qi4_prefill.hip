@@ -29,6 +29,7 @@
 #include "qi4_gemm.h"
 #include "qi4_host.h"
 #include "qi4_prefill.h"
+#include "qi4_rows.h"
 
 namespace qi4 {
 namespace {
@@ -73,90 +74,14 @@ __device__ inline uint4 dequant_f16_x16(uint32_t d, uint32_t negz, uint32_t negz
 
 // ---- row preparation: fp16 with a per-row power-of-two prescale ----------------
 
-// src_kind 0: bf16 rows [rows][len]; 1: hi/lo bf16 pairs [rows][2][len] (the
-// value is hi + lo).  One workgroup per row: each thread loads its chunks of 8
-// consecutive elements (16-byte accesses) once into registers, the workgroup
-// takes the row's largest magnitude, and the same registers are converted and
-// stored, so a row costs one round trip to memory however long it is (rows of
-// up to kPrepThreads * 8 * kPrepChunks elements; longer rows run the loop
-// below again from memory).  len is a multiple of 128, rows 16-byte aligned.
+// One workgroup per row (prep_row).
 constexpr int kPrepThreads = 256;
-constexpr int kPrepChunks = 8;
 
 __global__ void __launch_bounds__(kPrepThreads)
 prep_rows_kernel(const uint16_t *__restrict__ src, int src_kind, int64_t len,
                  uint16_t *__restrict__ dst, int32_t *__restrict__ exps) {
     __shared__ float wmax[kPrepThreads / 64];
-    const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const uint16_t *s = src + row * len * (src_kind ? 2 : 1);
-    const int64_t nch = len / 8;
-    auto load8 = [&](int64_t i, float (&v)[8]) {   // elements i .. i + 7
-        const uint4 a = *reinterpret_cast<const uint4 *>(s + i);
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            v[2 * c] = bf16_to_f32(w[c] & 0xFFFFu);
-            v[2 * c + 1] = bf16_to_f32(w[c] >> 16);
-        }
-        if (src_kind) {
-            const uint4 b = *reinterpret_cast<const uint4 *>(s + len + i);
-            const uint32_t u[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                v[2 * c] += bf16_to_f32(u[c] & 0xFFFFu);
-                v[2 * c + 1] += bf16_to_f32(u[c] >> 16);
-            }
-        }
-    };
-    float v[kPrepChunks][8];
-    float mx = 0.f;
-#pragma unroll
-    for (int q = 0; q < kPrepChunks; ++q) {
-        const int64_t ch = tid + (int64_t)q * kPrepThreads;
-        if (ch < nch) {
-            load8(8 * ch, v[q]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[q][e]));
-        }
-    }
-    for (int64_t ch = tid + (int64_t)kPrepChunks * kPrepThreads; ch < nch; ch += kPrepThreads) {
-        float w[8];
-        load8(8 * ch, w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(w[e]));
-    }
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kPrepThreads / 64; ++w) mx = fmaxf(mx, wmax[w]);
-    int E = 0;
-    if (mx > 0.f) frexpf(mx, &E);          // mx in [2^(E-1), 2^E)
-    const int sh = mx > 0.f ? 14 - E : 0;  // |v * 2^sh| < 2^14
-    auto store8 = [&](int64_t i, const float (&w)[8]) {
-        uint32_t o[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // k = 2, 3, 6, 7 (mod 8) carry an extra 2^-4 (the weights there are 16x)
-            const int se = (c & 1) ? sh - 4 : sh;
-            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(w[2 * c], se));
-            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(w[2 * c + 1], se));
-            o[c] = lo | (hi << 16);
-        }
-        *reinterpret_cast<uint4 *>(dst + row * len + i) = make_uint4(o[0], o[1], o[2], o[3]);
-    };
-#pragma unroll
-    for (int q = 0; q < kPrepChunks; ++q) {
-        const int64_t ch = tid + (int64_t)q * kPrepThreads;
-        if (ch < nch) store8(8 * ch, v[q]);
-    }
-    for (int64_t ch = tid + (int64_t)kPrepChunks * kPrepThreads; ch < nch; ch += kPrepThreads) {
-        float w[8];
-        load8(8 * ch, w);
-        store8(8 * ch, w);
-    }
-    if (tid == 0) exps[row] = -sh;
+    prep_row<kPrepThreads>(src, src_kind, len, blockIdx.x, dst, exps, wmax);
 }
 
 // ---- tile planner ---------------------------------------------------------------
