@@ -158,6 +158,7 @@ plan_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ act
 
 constexpr int kABlock = 1024;          // one MFMA operand fragment of a wave (16 rows x 32 k, fp16)
 constexpr int kRowsPerWG = 256;        // weight rows (16 tiles) of one workgroup
+constexpr bool kMergeSmall = true;     // see prefill_small12_kernel
 
 // Shapes of the two kernels.  Big tiles: 128 activation rows, 4 waves of 64
 // weight rows, 2 pipeline stages, two workgroups per CU (256 registers a wave).
@@ -514,30 +515,56 @@ __device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int
 // Workgroup ids are dealt to the 8 XCDs in turn (id mod 8): tile tix goes to
 // XCD tix mod 8 and all its column blocks run there back to back, so the
 // activation tile they share is fetched once into that XCD's L2.
+// bid: the workgroup's index in its region of the grid (regions start at
+// multiples of 8, so bid & 7 is still its XCD).
 template <int EPI, class SH, int MU, int H>
-__device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *tiles, int count) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SH::kLds];
-    __shared__ int wg_flag;
+__device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *tiles, int count,
+                                          uint32_t bid, uint8_t *lds, int *wg_flag) {
     const int64_t nt = num_tiles(args.N, args.flags);
     const uint32_t gx = (uint32_t)((nt * 16 + kRowsPerWG - 1) / kRowsPerWG);
-    const uint32_t kx = blockIdx.x >> 3;
-    const int tix = (int)((kx / gx) * 8 + (blockIdx.x & 7));
+    const uint32_t kx = bid >> 3;
+    const int tix = (int)((kx / gx) * 8 + (bid & 7));
     if (tix >= count) return;
-    tile_entry<EPI, SH, MU, false, H>(args, tiles[tix], kx % gx, lds, &wg_flag);
+    tile_entry<EPI, SH, MU, false, H>(args, tiles[tix], kx % gx, lds, wg_flag);
 }
 
 template <int EPI, int H>
 __global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
 prefill_big_kernel(const PrefillArgs args) {
-    fast_pass<EPI, BigShape, BigShape::MS, H>(args, args.tiles, args.tile_count[0]);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[BigShape::kLds];
+    __shared__ int wg_flag;
+    fast_pass<EPI, BigShape, BigShape::MS, H>(args, args.tiles, args.tile_count[0], blockIdx.x, lds,
+                                               &wg_flag);
 }
 
 // Small tiles of class C: at most 16 << C rows, 1 << C subtiles multiplied.
 template <int EPI, int C, int H>
 __global__ void __launch_bounds__((SmallShapeC<C, H>::W * 64), (SmallShapeC<C, H>::OCC))
 prefill_small_kernel(const PrefillArgs args) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SmallShapeC<C, H>::kLds];
+    __shared__ int wg_flag;
     fast_pass<EPI, SmallShapeC<C, H>, 1 << C, H>(args, args.tiles + args.max_big + C * args.max_small,
-                                      args.tile_count[1 + C]);
+                                                  args.tile_count[1 + C], blockIdx.x, lds, &wg_flag);
+}
+
+// The 17-32- and 33-64-row classes in one launch (128-wide groups; both use
+// 8 waves of 32 weight rows): the 33-64-row tiles in the first region_blocks
+// workgroups, the others after them, so the first class's last workgroups
+// share the chip with the second's first ones instead of leaving CUs idle at
+// the end of a launch of their own.
+template <int EPI>
+__global__ void __launch_bounds__(8 * 64, 4)
+prefill_small12_kernel(const PrefillArgs args, uint32_t region_blocks) {
+    static_assert(SmallShapeC<1, 1>::W == 8 && SmallShapeC<2, 1>::W == 8, "8-wave shapes");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SmallShapeC<2, 1>::kLds];
+    __shared__ int wg_flag;
+    const int2 *t = args.tiles + args.max_big;
+    if (blockIdx.x < region_blocks)
+        fast_pass<EPI, SmallShapeC<2, 1>, 4, 1>(args, t + 2 * args.max_small, args.tile_count[3],
+                                               blockIdx.x, lds, &wg_flag);
+    else
+        fast_pass<EPI, SmallShapeC<1, 1>, 2, 1>(args, t + args.max_small, args.tile_count[2],
+                                               blockIdx.x - region_blocks, lds, &wg_flag);
 }
 
 // Deferred (tile, column block) pairs, with the plain operands (big-tile shape
@@ -600,9 +627,14 @@ int launch_prefill_epi(const PrefillArgs &a, hipStream_t st, unsigned gb, unsign
     int rc;
     prefill_big_kernel<EPI, H><<<gb, tb, 0, st>>>(a);
     if ((rc = launch_status())) return rc;
-    prefill_small_kernel<EPI, 0, H><<<gs, ts0, 0, st>>>(a);
-    prefill_small_kernel<EPI, 1, H><<<gs, ts1, 0, st>>>(a);
-    prefill_small_kernel<EPI, 2, H><<<gs, ts2, 0, st>>>(a);
+    if (H == 1 && kMergeSmall) {
+        prefill_small_kernel<EPI, 0, H><<<gs, ts0, 0, st>>>(a);
+        prefill_small12_kernel<EPI><<<2 * gs, 8 * 64, 0, st>>>(a, gs);
+    } else {
+        prefill_small_kernel<EPI, 0, H><<<gs, ts0, 0, st>>>(a);
+        prefill_small_kernel<EPI, 1, H><<<gs, ts1, 0, st>>>(a);
+        prefill_small_kernel<EPI, 2, H><<<gs, ts2, 0, st>>>(a);
+    }
     if ((rc = launch_status())) return rc;
     // tiles deferred by either kind, after both
     prefill_wide_kernel<EPI, H><<<512, tb, 0, st>>>(a);   // two workgroups per CU
@@ -614,7 +646,7 @@ int launch_prefill(const PrefillArgs &a, hipStream_t st) {
     const int64_t nt = num_tiles(a.N, a.flags);
     const int64_t gx = ceil_div(nt * 16, kRowsPerWG);
     const int64_t gb = gx * ceil_div(a.max_big, 8) * 8, gs = gx * ceil_div(a.max_small, 8) * 8;
-    if (gb > 0x7fffffff || gs > 0x7fffffff) return QI4_ERR_SHAPE;
+    if (gb > 0x7fffffff || 2 * gs > 0x7fffffff) return QI4_ERR_SHAPE;
     if (gb + 3 * gs > a.max_deferred) return QI4_ERR_SHAPE;
     const bool h2 = halves_for(a.group_size) == 2;
     if (a.epi == QI4_EPI_SILU_MUL)
