@@ -94,6 +94,20 @@ __device__ inline uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// The same load with the non-temporal cache policy (the nt bit, 2 in the
+// buffer instruction's cache-policy operand): for data read once per call,
+// the weight codes of the decode GEMMs.  Measured on MI355X at MoE decode
+// T = 32: the grouped gate/up GEMM 5.89 -> 6.29 TB/s, the step 47.5K -> 50.0K
+// tokens/s; the streaming-read probe 6.0 -> 6.8-6.9 TB/s.  Not for the
+// scale/zero records or the activations, which other waves and workgroups
+// read again (measured: no gain or a loss), nor for the prefill weights, which
+// the tiles of one expert read again.
+constexpr int kCpolNonTemporal = 2;
+__device__ inline uint4 buf_b128_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpolNonTemporal));
+}
+
 // Scale and zero records of NB (1, 2 or 4) aligned tiles of one quad for one
 // row, one load each: lane offsets vs = 8 r + 2 slot0 and vz = 2 r + slot0 / 2
 // (slot0 = first tile's slot in its quad), record starts os and oz in soffset.

@@ -288,7 +288,7 @@ qgemm_kernel(const GemmArgs args) {
             const bool in = lnt > 0 && gb + li < ge;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                q.cw[nb] = buf_b128(wr, vc, in && nb < lnt ? loc + nb * tstride : kOobS);
+                q.cw[nb] = buf_b128_stream(wr, vc, in && nb < lnt ? loc + nb * tstride : kOobS);
 #pragma unroll
             for (int h = 0; h < H; ++h)
                 load_meta<NB>(wr, vs, vz, in ? los + h * kQuadScaleBytes : kOobS,

@@ -1,8 +1,8 @@
 // Measurement probes: what the chip delivers on the two resources the kernels
 // of this library are bound by, measured on the same machine as the kernels.
 //  * qi4_probe_stream_read: every byte of a large buffer read once with
-//    16-byte loads, eight in flight per lane, one contiguous span per
-//    workgroup; the achieved bytes per second is the practical HBM read
+//    16-byte non-temporal loads, eight in flight per lane, one contiguous span
+//    per workgroup; the achieved bytes per second is the practical HBM read
 //    ceiling.
 //  * qi4_probe_mfma: independent chains of fp16 16x16x32 MFMAs on every SIMD
 //    (eight accumulators per wave), no memory traffic; the achieved flops per
@@ -17,6 +17,14 @@ namespace qi4 {
 namespace {
 
 constexpr int kReadThreads = 256;
+
+// A 16-byte load with the non-temporal hint (each byte is read once): on
+// MI355X this reads 6.8-6.9 TB/s against 6.0 TB/s with ordinary loads.
+__device__ inline uint4 load_nt(const uint4 *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
 constexpr int kReadUnroll = 8;
 constexpr int kReadBlocks = QI4_PROBE_READ_SINK_WORDS / (kReadThreads / 64);
 
@@ -37,12 +45,12 @@ stream_read_kernel(const uint4 *__restrict__ buf, int64_t n16, uint32_t *__restr
     for (; i + (kReadUnroll - 1) * kReadThreads < end; i += step) {
         uint4 v[kReadUnroll];
 #pragma unroll
-        for (int u = 0; u < kReadUnroll; ++u) v[u] = buf[i + u * kReadThreads];
+        for (int u = 0; u < kReadUnroll; ++u) v[u] = load_nt(buf + i + u * kReadThreads);
 #pragma unroll
         for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < end; i += kReadThreads) {
-        const uint4 v = buf[i];
+        const uint4 v = load_nt(buf + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     // one value per wave, the xor of its lanes, so the loads stay

@@ -21,8 +21,8 @@ extern "C" {
 /* Words of the `sink` buffer qi4_probe_stream_read writes (one per wave). */
 #define QI4_PROBE_READ_SINK_WORDS 8192
 
-/* Read every byte of buf[0, bytes) once (16-byte loads, one contiguous span per
- * workgroup, eight loads in flight per lane).  bytes a positive multiple of 16, buf
+/* Read every byte of buf[0, bytes) once (16-byte loads with the non-temporal
+ * hint, one contiguous span per workgroup, eight loads in flight per lane).  bytes a positive multiple of 16, buf
  * 16-byte aligned (QI4_ERR_SHAPE otherwise); `sink` receives
  * QI4_PROBE_READ_SINK_WORDS uint32 words (an xor of the data, so the loads are
  * kept).  Time it with events around the call: bytes / time is the achieved
