@@ -100,8 +100,8 @@ __device__ inline uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
 // T = 32: the grouped gate/up GEMM 5.89 -> 6.29 TB/s, the step 47.5K -> 50.0K
 // tokens/s; the streaming-read probe 6.0 -> 6.8-6.9 TB/s.  Not for the
 // scale/zero records or the activations, which other waves and workgroups
-// read again (measured: no gain or a loss), nor for the prefill weights, which
-// the tiles of one expert read again.
+// read again (measured: no gain or a loss), nor for the prefill's big tiles,
+// whose expert's other tiles read the same weights again.
 constexpr int kCpolNonTemporal = 2;
 __device__ inline uint4 buf_b128_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint4,
