@@ -88,22 +88,34 @@ __device__ inline void scale_zero(float lo, float hi, uint32_t &sb, double &s, d
 // bits), 8-bit codes one per byte.  rint(w / s) is formed from x = w * (1/s)
 // in float32 (w and s are exact in float32; two roundings: |x - w/s| <= |x| 2^-23,
 // at most 6.2e-5 for |x| <= 2 (L + 1)).  Away from the half-integers x rounds
-// like w/s; within 1e-4 of one the decision is taken on the binary64 quotient.
-// Beyond 2 (L + 1) both clamp alike (z <= L).
+// like w/s; within 1e-4 of one (|x - rint(x)| > 0.4999) the decision is taken
+// on the binary64 quotient, in a branch that the lanes needing it take alone
+// (a wave where none does skips it).  The sum with the zero point is exact in
+// float32 for |x| <= 2^24, and beyond 2 (L + 1) any value clamps alike, so
+// the clamp to [0, L] is taken on the float sum.
 template <int BITS>
 __device__ inline uint64_t codes8(const float (&v)[8], double s, double z) {
     constexpr float XMAX = 2.0f * (1 << BITS);
+    constexpr float L = (float)((1 << BITS) - 1);
     const float rs = 1.0f / (float)s;
-    uint64_t codes = 0;
+    const float zf = (float)z;
+    uint32_t c[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = v[e] * rs;
-        const float r = rintf(x);
-        const double qf = (fabsf(x) > XMAX || fabsf(fabsf(x - r) - 0.5f) > 1e-4f)
-                              ? (double)r : rint((double)v[e] / s);
-        codes |= (uint64_t)clampL<BITS>(qf + z) << (BITS * e);
+        float r = rintf(x);
+        if (fabsf(x - r) > 0.4999f && fabsf(x) <= XMAX) r = (float)rint((double)v[e] / s);
+        c[e] = (uint32_t)fminf(fmaxf(r + zf, 0.0f), L);
     }
-    return codes;
+    if constexpr (BITS == 8) {
+        return (uint64_t)(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24)) |
+               ((uint64_t)(c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)) << 32);
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= c[e] << (4 * e);
+        return w;
+    }
 }
 
 // Store the codes of eight weights starting at weight k of row n.
@@ -140,30 +152,57 @@ quantize_kernel(const void *__restrict__ w, int64_t N, int64_t K, uint8_t *__res
         const int64_t n = grp / G, g = grp - n * G;
         load8<F32>(w, n * K + g * GS + 8 * j, v[p]);
     }
+    // ranges of the wave's kQuantPasses * SPW groups (every lane of a segment
+    // holds its group's)
+    float lo[kQuantPasses], hi[kQuantPasses];
+#pragma unroll
+    for (int p = 0; p < kQuantPasses; ++p) {
+        // fminf/fmaxf skip NaN operands; min/max are exact in float32
+        lo[p] = 0.0f;
+        hi[p] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo[p] = fminf(lo[p], v[p][e]);
+            hi[p] = fmaxf(hi[p], v[p][e]);
+        }
+        for (int o = SEG / 2; o >= 1; o >>= 1) {   // within the segment
+            lo[p] = fminf(lo[p], __shfl_xor(lo[p], o));
+            hi[p] = fmaxf(hi[p], __shfl_xor(hi[p], o));
+        }
+    }
+    // scale and zero once per group: lane l < kQuantPasses * SPW takes group
+    // (pass l / SPW, segment l % SPW); the binary64 work is then done by one
+    // lane per group instead of all SEG lanes of its segment
+    constexpr int NG = kQuantPasses * SPW;
+    static_assert(NG <= 64, "one lane per group");
+    const int mp = lane / SPW < kQuantPasses ? lane / SPW : 0, ms = lane % SPW;
+    float mlo = 0.0f, mhi = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kQuantPasses; ++p) {
+        const float a = __shfl(lo[p], ms * SEG), b = __shfl(hi[p], ms * SEG);
+        if (p == mp) {
+            mlo = a;
+            mhi = b;
+        }
+    }
+    uint32_t msb = 0;
+    double msd = 1.0, mz = 0.0;
+    if (lane < NG) scale_zero<BITS>(mlo, mhi, msb, msd, mz);
+    if (lane < NG) {
+        const int64_t grp = grp0 + lane;   // = grp0 + SPW * mp + ms
+        if (grp < total) {
+            scales[grp] = (uint16_t)msb;
+            zeros[grp] = (uint8_t)mz;
+        }
+    }
 #pragma unroll
     for (int p = 0; p < kQuantPasses; ++p) {
         const int64_t grp = grp0 + SPW * p + seg;
-        // fminf/fmaxf skip NaN operands; min/max are exact in float32
-        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lo = fminf(lo, v[p][e]);
-            hi = fmaxf(hi, v[p][e]);
-        }
-        for (int o = SEG / 2; o >= 1; o >>= 1) {   // within the segment
-            lo = fminf(lo, __shfl_xor(lo, o));
-            hi = fmaxf(hi, __shfl_xor(hi, o));
-        }
+        const int src = SPW * p + seg;   // the lane holding this group's scale and zero
+        const double sd = __shfl(msd, src), z = __shfl(mz, src);
         if (grp >= total) continue;
         const int64_t n = grp / G, g = grp - n * G;
-        uint32_t sb;
-        double sd, z;
-        scale_zero<BITS>(lo, hi, sb, sd, z);
         store_codes<BITS>(qweight, n, K, g * GS + 8 * j, codes8<BITS>(v[p], sd, z));
-        if (j == 0) {
-            scales[n * G + g] = (uint16_t)sb;
-            zeros[n * G + g] = (uint8_t)z;
-        }
     }
 }
 
