@@ -176,6 +176,83 @@ router_gemm_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     }
 }
 
+// Large batches: a workgroup owns 16 NE experts x 16 MT tokens (64 x 32 for
+// T >= kRouterWideMinT), so each token row is read by E / (16 NE) workgroups
+// instead of E / 16; its kRouterWideWaves waves split K and add their partial
+// sums in LDS in wave order (deterministic, as above); 64 KiB of LDS for the
+// partial sums.  T = 2048, E = 256, H = 7168 on MI355X: 79 -> 50 us for the
+// projection and top-k (64 x 64 tiles: 75 us, 16 x 128: 73 us, 4 waves: 52 us).
+constexpr int kRouterWideWaves = 8;
+constexpr int64_t kRouterWideMinT = 256;
+template <int MT, int NE>
+__global__ void __launch_bounds__(kRouterWideWaves * 64)
+router_gemm_wide_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int64_t T,
+                        int64_t H, int E, float *__restrict__ logits) {
+    constexpr int CH = 2;
+    __shared__ float red[kRouterWideWaves * MT * NE * 256];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, j = lane >> 4;
+    const int64_t e0 = (int64_t)blockIdx.x * 16 * NE, t0 = (int64_t)blockIdx.y * (16 * MT);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(T * H * 2));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)(E * H * 2));
+    const int nks = (int)(H / 32);
+    const int kb = nks * wave / kRouterWideWaves, ke = nks * (wave + 1) / kRouterWideWaves;
+    uint32_t wo[NE], xo[MT];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        const int64_t e = e0 + 16 * n + r16;
+        wo[n] = e < E ? (uint32_t)((e * H + 8 * j) * 2) : kOob;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int64_t t = t0 + 16 * m + r16;
+        xo[m] = t < T ? (uint32_t)((t * H + 8 * j) * 2) : kOob;
+    }
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[MT][NE];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NE; ++n) acc[m][n] = zero4;
+    for (int k0 = kb; k0 < ke; k0 += CH) {
+        bf16x8 bv[CH][NE], av[CH][MT];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const uint32_t ko = k0 + c < ke ? (uint32_t)(k0 + c) * 64u : kOobS;
+#pragma unroll
+            for (int n = 0; n < NE; ++n) bv[c][n] = as_bf16x8(buf_b128(wr, wo[n], ko));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) av[c][m] = as_bf16x8(buf_b128(xr, xo[m], ko));
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NE; ++n) acc[m][n] = mfma16x16x32(av[c][m], bv[c][n], acc[m][n]);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NE; ++n)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[(((wave * MT + m) * NE + n) * 4 + v) * 64 + lane] = acc[m][n][v];
+    __syncthreads();
+    // one output per thread: tile (m, n), register v, lane l -> token 16 m +
+    // 4 (l >> 4) + v, expert 16 n + (l & 15)
+    for (int it = threadIdx.x; it < MT * NE * 256; it += kRouterWideWaves * 64) {
+        const int mn = it >> 8, v = (it >> 6) & 3, l = it & 63;
+        float sum = 0.f;
+        for (int ww = 0; ww < kRouterWideWaves; ++ww)
+            sum += red[((ww * MT * NE + mn) * 4 + v) * 64 + l];
+        const int m = mn / NE, n = mn % NE;
+        const int64_t t = t0 + 16 * m + 4 * (l >> 4) + v, e = e0 + 16 * n + (l & 15);
+        if (t < T && e < E) logits[t * E + e] = sum;
+    }
+}
+
 // Router logits of decode batches (T <= kGemvMaxT): one workgroup per (expert,
 // group of up to four tokens), its four waves each taking a quarter of the
 // expert's row in 16-byte chunks (8 bf16, all loads of a lane issued before
@@ -250,6 +327,13 @@ int launch_router_gemm(const uint16_t *x, const uint16_t *w, int64_t T, int64_t 
         else if (T == 2) router_gemv_kernel<2><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
         else if (T == 3) router_gemv_kernel<3><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
         else router_gemv_kernel<4><<<g, 256, 0, st>>>(x, w, T, H, E, logits);
+        return launch_status();
+    }
+    if (T >= kRouterWideMinT) {
+        const int64_t gy = ceil_div(T, 16 * 2);
+        if (gy > 65535) return QI4_ERR_SHAPE;
+        const dim3 g((unsigned)ceil_div(E, 16 * 4), (unsigned)gy);
+        router_gemm_wide_kernel<2, 4><<<g, kRouterWideWaves * 64, 0, st>>>(x, w, T, H, E, logits);
         return launch_status();
     }
     const int MT = T <= 16 ? 1 : T <= 32 ? 2 : 4;
