@@ -196,11 +196,28 @@ using SmallShapeC = std::conditional_t<
 // outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// The LDS buffers of the pipeline stages, each its own variable.  The copies
+// into a stage are memory requests that write LDS; a read of LDS that may
+// overlap them must wait for them.  With one array for all stages the compiler
+// cannot tell the stages apart and makes every step's first operand read wait
+// for the copies just issued for a later group (one memory latency exposed per
+// group); with one variable per stage it can, and waits only where the code
+// does.  Stage index: a constant once the pipeline loop is unrolled.
+struct Stages {
+    uint8_t *p[4];
+};
+#define QI4_STAGE_LDS(SH_, VAR_)                                                               \
+    __shared__ __attribute__((aligned(16))) uint8_t VAR_##0[SH_::kStageBytes];                 \
+    __shared__ __attribute__((aligned(16))) uint8_t VAR_##1[SH_::S > 1 ? SH_::kStageBytes : 16]; \
+    __shared__ __attribute__((aligned(16))) uint8_t VAR_##2[SH_::S > 2 ? SH_::kStageBytes : 16]; \
+    __shared__ __attribute__((aligned(16))) uint8_t VAR_##3[SH_::S > 3 ? SH_::kStageBytes : 16]; \
+    const Stages VAR_ = {{VAR_##0, VAR_##1, VAR_##2, VAR_##3}}
+
 // One tile: SH::MS 16-row activation subtiles times this workgroup's 256
 // weight rows, over the whole K.
 // H = 2: 64-wide quantization groups (two scale/zero records per block).
 template <int EPI, class SH, int MU, bool WIDE, int H>
-__device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLayout &L, uint8_t *lds,
+__device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLayout &L, const Stages &lds,
                                          int *wg_flag, int2 te, const uint8_t *w, int64_t row0,
                                          int64_t n, int64_t src0, const int32_t *gather, int64_t bx,
                                          int wave, int lane) {
@@ -256,7 +273,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     auto fill = [&](int stage, int g) {
         const bool in = g < G;
         const uint32_t so = in ? (uint32_t)(g >> args.a_shift) * 256u : 0u;
-        uint8_t *buf = lds + stage * SH::kStageBytes;
+        uint8_t *buf = lds.p[stage];
 #pragma unroll
         for (int i = 0; i < FPW; ++i) {
             if (S == 2 && frag_sub(i) >= m_used) continue;
@@ -352,7 +369,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     {
         static_assert(MU >= 1 && MU <= MS, "subtiles");
         auto compute = [&](const WStage &q, int stage) {
-            const uint8_t *buf = lds + stage * SH::kStageBytes;
+            const uint8_t *buf = lds.p[stage];
             uint32_t negz[H][NBW], negz16[H][NBW], s2[H][NBW];
 #pragma unroll
             for (int h = 0; h < H; ++h)
@@ -493,7 +510,7 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
 
 // Tile list entry -> problem, then run_tile.
 template <int EPI, class SH, int MU, bool WIDE, int H>
-__device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int64_t bx, uint8_t *lds,
+__device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int64_t bx, const Stages &lds,
                                            int *wg_flag) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -524,7 +541,7 @@ __device__ __forceinline__ void tile_entry(const PrefillArgs &args, int2 te, int
 // multiples of 8, so bid & 7 is still its XCD).
 template <int EPI, class SH, int MU, int H>
 __device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *tiles, int count,
-                                          uint32_t bid, uint8_t *lds, int *wg_flag) {
+                                          uint32_t bid, const Stages &lds, int *wg_flag) {
     const int64_t nt = num_tiles(args.N, args.flags);
     const uint32_t gx = (uint32_t)((nt * 16 + kRowsPerWG - 1) / kRowsPerWG);
     const uint32_t kx = bid >> 3;
@@ -536,7 +553,7 @@ __device__ __forceinline__ void fast_pass(const PrefillArgs &args, const int2 *t
 template <int EPI, int H>
 __global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
 prefill_big_kernel(const PrefillArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[BigShape::kLds];
+    QI4_STAGE_LDS(BigShape, lds);
     __shared__ int wg_flag;
     fast_pass<EPI, BigShape, BigShape::MS, H>(args, args.tiles, args.tile_count[0], blockIdx.x, lds,
                                                &wg_flag);
@@ -546,7 +563,8 @@ prefill_big_kernel(const PrefillArgs args) {
 template <int EPI, int C, int H>
 __global__ void __launch_bounds__((SmallShapeC<C, H>::W * 64), (SmallShapeC<C, H>::OCC))
 prefill_small_kernel(const PrefillArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SmallShapeC<C, H>::kLds];
+    using SH = SmallShapeC<C, H>;
+    QI4_STAGE_LDS(SH, lds);
     __shared__ int wg_flag;
     fast_pass<EPI, SmallShapeC<C, H>, 1 << C, H>(args, args.tiles + args.max_big + C * args.max_small,
                                                   args.tile_count[1 + C], blockIdx.x, lds, &wg_flag);
@@ -561,7 +579,11 @@ template <int EPI>
 __global__ void __launch_bounds__(8 * 64, 4)
 prefill_small12_kernel(const PrefillArgs args, uint32_t region_blocks) {
     static_assert(SmallShapeC<1, 1>::W == 8 && SmallShapeC<2, 1>::W == 8, "8-wave shapes");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SmallShapeC<2, 1>::kLds];
+    // (class 1 stages are smaller and fewer or as many: the class 2 buffers serve both)
+    static_assert(SmallShapeC<1, 1>::S <= SmallShapeC<2, 1>::S &&
+                      SmallShapeC<1, 1>::kStageBytes <= SmallShapeC<2, 1>::kStageBytes, "stages");
+    using SH = SmallShapeC<2, 1>;
+    QI4_STAGE_LDS(SH, lds);
     __shared__ int wg_flag;
     const int2 *t = args.tiles + args.max_big;
     if (blockIdx.x < region_blocks)
@@ -577,7 +599,7 @@ prefill_small12_kernel(const PrefillArgs args, uint32_t region_blocks) {
 template <int EPI, int H>
 __global__ void __launch_bounds__(BigShape::W * 64, BigShape::OCC)
 prefill_wide_kernel(const PrefillArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[BigShape::kLds];
+    QI4_STAGE_LDS(BigShape, lds);
     const int count = *args.deferred_count;
     for (int i = blockIdx.x; i < count; i += gridDim.x) {
         const int4 d = args.deferred[i];
