@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kMaxWaves = 8;
 constexpr bool kDenseMSplit = true;   // see launch_qgemm
+constexpr bool kDownWaveBlocks = true;   // see launch_qgemm
 // (wave, m, nb) partial tiles the LDS reduction buffer holds: 16 (16 KiB), or
 // 32 for a quad of tiles over two M tiles (the only shape that needs more; the
 // others keep the smaller buffer so that LDS never caps their occupancy).
@@ -92,11 +93,15 @@ template <int NB, int MT, int AM, int EPI, int H>
 constexpr int kMinWaves = (AM == 3 && MT == 1 && NB == 4 && H == 1) ? 4 : 1;
 
 // H = 2: 64-wide groups, two scales and zeros per 128-wide block.
-template <int NB, int MT, int AM, int S, int EPI, int H>
+// WB: each wave streams its own tile blocks over the whole K and stores its
+// results from registers (no reduction across waves; fp16 rows, one part per
+// slot); otherwise the waves of a workgroup split K and reduce through LDS.
+template <int NB, int MT, int AM, int S, int EPI, int H, bool WB = false>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<NB, MT, AM, EPI, H>)))
 qgemm_kernel(const GemmArgs args) {
     constexpr bool AF32 = AM == 1, AI8 = AM == 2, AF16 = AM == 3, ALDS = AM == 4;
+    static_assert(!WB || AF16, "wave-owned blocks: fp16 rows only");
     __shared__ float red[kRedSlotsFor<NB, MT> * 256];
     // AM 4: [rows][lda] fp16 activation rows, 16 zero bytes, int32 [rows] (the
     // row's largest |bits|, then its shift)
@@ -147,11 +152,13 @@ qgemm_kernel(const GemmArgs args) {
     // back to back through one register pipeline, so a block's first loads are
     // in flight while the previous block is reduced and stored, and the
     // problem lookup above is paid once per R blocks.
-    const int R = args.blocks_per_wg;
-    const int64_t tile0 = (int64_t)blockIdx.x * R * NB;
+    const int R = WB ? 1 : args.blocks_per_wg;   // (WB: one block per wave)
+    const int64_t owner = WB ? (int64_t)blockIdx.x * W + wave : (int64_t)blockIdx.x;
+    const int64_t tile0 = owner * R * NB;
     const int64_t nblk_all = (nt + NB - 1) / NB;
-    const int64_t blk0 = (int64_t)blockIdx.x * R;
+    const int64_t blk0 = owner * R;
     const int nblk = (int)(nblk_all - blk0 < R ? nblk_all - blk0 : R);
+    if (WB && nblk <= 0) return;   // (no barriers on this path)
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)L.bytes);
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(args.a, (uint32_t)args.a_bytes);
 
@@ -163,8 +170,8 @@ qgemm_kernel(const GemmArgs args) {
     // block (ngp, a multiple of S) so that all reach each block's reduction
     // together.  Steps past a wave's range load out-of-range offsets (zero
     // codes, scales and activations), so computing them adds exactly 0.
-    const int gb = (int)((G * wave) / W), ge = (int)((G * (wave + 1)) / W);
-    const int ngp = (((int)((G + W - 1) / W) + S - 1) / S) * S;
+    const int gb = WB ? 0 : (int)((G * wave) / W), ge = WB ? (int)G : (int)((G * (wave + 1)) / W);
+    const int ngp = WB ? (((int)G + S - 1) / S) * S : (((int)((G + W - 1) / W) + S - 1) / S) * S;
     const int steps = nblk * ngp;
     const int P = args.P;                   // 1, 2 or 4
     const int plog = P == 4 ? 2 : P == 2 ? 1 : 0;
@@ -458,6 +465,7 @@ qgemm_kernel(const GemmArgs args) {
         // ---- reduction of the waves' partial sums of block r in a fixed
         // order, epilogue and store
         auto finish_block = [&](int r) {
+          if constexpr (!WB) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -466,6 +474,7 @@ qgemm_kernel(const GemmArgs args) {
                     for (int v = 0; v < 4; ++v)
                         red[((wave * MT + m) * NB + nb) * 256 + v * 64 + lane] = res[m][nb][v];
             __syncthreads();
+          }
 
             const int64_t tile_b = tile0 + (int64_t)r * NB;
             const int pairs = EPI == QI4_EPI_SILU_MUL ? NB / 2 : NB;
@@ -509,7 +518,31 @@ qgemm_kernel(const GemmArgs args) {
                 if (EPI == QI4_EPI_SILU_MUL) return (tile >> 1) * 16 + col;
                 return tile < nt ? tile_row(tile, col, args.N, args.flags) : -1;
             };
-            if constexpr (NB == 4) {
+            if constexpr (WB) {
+                // this wave's results, straight from its registers: lane
+                // 16 j + col holds rows 4 j + v of column col of each tile
+                // (one part per slot).  The column index passes through an
+                // empty asm statement, so the compiler computes the store
+                // addresses here rather than holding them across the loop.
+                int col = r16;
+                __asm__ volatile("" : "+v"(col));
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                    for (int pi = 0; pi < pairs; ++pi) {
+                        const int nbA = EPI == QI4_EPI_SILU_MUL ? 2 * pi : pi;
+                        const int64_t oc = out_col(nbA, col);
+                        if (oc < 0 || oc >= args.n_out) continue;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int64_t slot = c0 + (int64_t)m * 16 + 4 * j + v;
+                            if (slot >= n) continue;
+                            store(slot, oc, res[m][nbA][v],
+                                  EPI == QI4_EPI_SILU_MUL ? res[m][EPI == QI4_EPI_SILU_MUL ? nbA + 1 : nbA][v] : 0.f);
+                        }
+                    }
+                }
+            } else if constexpr (NB == 4) {
                 // grouped expert GEMMs: one thread per result lane, its four rows
                 // together (the register budget of these kernels is tight)
                 const int items = MT * pairs * 64;
@@ -580,7 +613,7 @@ qgemm_kernel(const GemmArgs args) {
                 store(slot, oc, val, uval);
             }
             }
-            __syncthreads();
+            if constexpr (!WB) __syncthreads();
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -637,11 +670,14 @@ qgemm_kernel(const GemmArgs args) {
             }
             ci += S;   // S divides ngp: a block ends at an iteration boundary
             if (ci == ngp) {
-                finish_block(cr);
+                if constexpr (!WB) finish_block(cr);
                 ci = 0;
                 ++cr;
             }
         }
+        // WB: the wave's one block, after its loop (kept out of the loop so that
+        // the compiler does not hold the store addresses across it)
+        if constexpr (WB) finish_block(0);
     }
 }
 
@@ -697,8 +733,10 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 //    from 9 rows on, a whole quad (NB = 4) when that still gives >= 192
 //    workgroups: the activation fragments, re-read per block of tiles, are
 //    then shared by four tiles (5120 -> 13824 at T = 32: 30.4 -> 23.7 us);
-//    the grouped expert GEMMs take a whole quad (NB = 4), and the down
-//    projection two quads per workgroup (R = 2) once the grid is large;
+//    the grouped expert GEMMs take a whole quad (NB = 4); the down
+//    projection with fp16 rows gives each wave a quad of its own over the
+//    whole K once there are 3000 quads or more, else splits K over the waves
+//    (two quads per workgroup, R = 2, from 12000 quads on);
 //  * one M tile per pass (16 activation rows), two for a single matrix with
 //    more rows.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t st) {
@@ -714,14 +752,22 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     // (a single matrix takes two tiles per workgroup from 320 tiles up: cold-cache
     // sweeps of 4096..22016-row matrices put the crossover between 256 and 320)
     int NB = (silu || ceil_div(nt, 2) * n_problems >= 160) ? 2 : 1;
-    int W, R = 1;   // R: tile blocks streamed back to back by one workgroup
+    int W, R = 1;   // R: tile blocks streamed back to back by one workgroup (or wave)
+    bool wb = false;   // waves own tile blocks (qgemm_kernel's WB)
     if (n_problems > 1) {
         // grouped expert GEMMs: four tiles (one quad) per block; gate/up over
-        // four waves; down over four waves and two blocks per workgroup when
-        // the grid is large, else two waves
+        // four waves; down as below
         NB = 4;
         if (silu) {
             W = 4;
+        } else if (kDownWaveBlocks && args.a_f16 && args.P == 1 &&
+                   ceil_div(nt, NB) * n_problems >= 3000) {
+            // (fp16 rows) each wave streams a whole quad over K and stores it
+            // without a reduction across waves, two waves per workgroup:
+            // DeepSeek-V3 down at T = 32 5.41 -> 5.75 TB/s, T = 4 and 8
+            // 1-2 % faster; fewer quads (T <= 2) keep K split over the waves
+            W = 2;
+            wb = true;
         } else if (ceil_div(nt, NB) * n_problems >= 12000) {
             W = 4;
             R = 2;
@@ -753,10 +799,17 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     // floor(p * m / 2^32) = floor(p / k) whenever p * k < 2^32 (pairs are below
     // 2^31 / 32 and top_k is at most 32); k = 1 (m = 2^32) is taken apart
     a.topk_magic = a.top_k > 1 ? (uint32_t)(0xFFFFFFFFull / (uint32_t)a.top_k + 1ull) : 0u;
-    const int64_t gx = ceil_div(ceil_div(nt, NB), R);
+    const int64_t gx = wb ? ceil_div(ceil_div(ceil_div(nt, NB), R), W) : ceil_div(ceil_div(nt, NB), R);
     if (gx > 0x7fffffff || gy > 65535) return QI4_ERR_SHAPE;
     dim3 grid((unsigned)gx, (unsigned)gy);
     const int threads = W * 64;
+    if (wb) {
+        if (halves_for(a.group_size) == 2)
+            qgemm_kernel<4, 1, 3, 2, QI4_EPI_NONE, 2, true><<<grid, threads, 0, st>>>(a);
+        else
+            qgemm_kernel<4, 1, 3, 2, QI4_EPI_NONE, 1, true><<<grid, threads, 0, st>>>(a);
+        return launch_status();
+    }
     if (MT == 1) {
         if (NB == 4) return launch_cfg<4, 1, 2>(a, grid, threads, st);
         if (NB == 2) return launch_cfg<2, 1, 2>(a, grid, threads, st);
