@@ -195,7 +195,7 @@ qgemm_kernel(const GemmArgs args) {
     const int64_t xrow_bytes = args.lda * 2;
     const uint32_t zoff = (uint32_t)(n * xrow_bytes);
     auto fill_lds = [&]() {
-        constexpr int kFillRegs = 1;   // more held chunks cost registers that slow the whole kernel
+        constexpr int kFillRegs = 2;   // (a row of 4096 over 256 threads: two each; more slowed the kernel)
         int *ri = reinterpret_cast<int *>(xlds + zoff + 16);
         for (int64_t i = threadIdx.x; i < n; i += blockDim.x) ri[i] = 0;
         if (threadIdx.x < 4) reinterpret_cast<uint32_t *>(xlds + zoff)[threadIdx.x] = 0u;
@@ -727,7 +727,8 @@ int launch_cfg(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
 
 // Launch shape, from sweeps on MI355X over the decode workloads (dense Llama-7B
 // and 5120/13824 shapes, DeepSeek-V3-shaped experts at T = 1, 8, 32):
-//  * W waves split K; about ten 128-wide groups per wave for a single matrix;
+//  * W waves split K; about ten 128-wide groups per wave for a single matrix
+//    (all eight waves for one row with one tile per workgroup);
 //  * a single matrix takes NB = 2 tiles per workgroup (the gate/up pair)
 //    unless it has fewer than 320 tiles and needs more workgroups (NB = 1);
 //    from 9 rows on, a whole quad (NB = 4) when that still gives >= 192
@@ -778,6 +779,10 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
         if (max_slots > 8 && ceil_div(nt, 4) >= 192 && !args.a_f32) NB = 4;
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
+        // one row, one tile per workgroup: all eight waves (Llama-7B O
+        // projection 4096 -> 4096: 10.6 -> 9.0 us cold; with two tiles per
+        // workgroup the SiLU launch got slower)
+        if (args.a_lds && max_slots == 1 && NB == 1) W = kMaxWaves;
     }
     // a dense matrix whose rows span two M tiles and whose activations are
     // converted in registers: one M tile per workgroup, grid.y over the M
