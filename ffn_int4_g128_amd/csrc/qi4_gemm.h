@@ -63,6 +63,12 @@ struct GemmArgs {
 // LDS per workgroup; larger ones convert in registers per (row, block).
 constexpr int64_t kLdsActBytes = 32 * 1024;
 
+// Dynamic LDS of such a call: the fp16 rows, 16 zero bytes, and a float factor
+// per (128-wide block, row), rows padded to a multiple of 16.
+constexpr int64_t lds_act_bytes(int64_t T, int64_t lda) {
+    return T * lda * 2 + 16 + (lda / 128) * ((T + 15) & ~int64_t(15)) * 4;
+}
+
 // Launch the GEMM for `n_problems` problems (grid.y); `max_slots` bounds the
 // slots of any one problem and picks the M tiling.  Returns a QI4 status.
 int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStream_t stream);

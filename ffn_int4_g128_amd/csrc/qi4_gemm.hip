@@ -103,8 +103,8 @@ qgemm_kernel(const GemmArgs args) {
     constexpr bool AF32 = AM == 1, AI8 = AM == 2, AF16 = AM == 3, ALDS = AM == 4;
     static_assert(!WB || AF16, "wave-owned blocks: fp16 rows only");
     __shared__ float red[kRedSlotsFor<NB, MT> * 256];
-    // AM 4: [rows][lda] fp16 activation rows, 16 zero bytes, int32 [rows] (the
-    // row's largest |bits|, then its shift)
+    // AM 4: [rows][lda] fp16 activation rows, 16 zero bytes, float
+    // [lda / 128][rows padded to 16] (each block's factor; lds_act_bytes)
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
 
     const int lane = threadIdx.x & 63;
@@ -186,74 +186,54 @@ qgemm_kernel(const GemmArgs args) {
         return args.top_k == 1 ? pr : __umulhi(pr, args.topk_magic);
     };
 
-    // AM 4: the n activation rows (bf16) once into LDS as fp16 rows times 2^sh,
-    // sh from the row's largest magnitude (|v * 2^sh| < 2^14, exact for normal
-    // values; columns k = 2, 3, 6, 7 (mod 8) times a further 2^-4, as the weight
-    // operands there are 16x).  A thread keeps its first chunk of 8 values in
-    // registers between the maximum and the conversion and reads the others
-    // again (from cache); called once the first weight loads are in flight.
+    // AM 4: the n activation rows (bf16) once into LDS as fp16 rows, each
+    // 128-wide block of a row with its own power of two (the conversion of the
+    // rows converted in registers, bf16_to_f16_scaled: the block's largest
+    // magnitude lands in [2^14, 2^15), columns k = 2, 3, 6, 7 (mod 8) a further
+    // 2^-4, as the weight operands there are 16x), and the block's factor
+    // 2^(c - 112) as a float in fac[block][row] (rows padded to 16, padding 0).
+    // The 16 chunks of 8 values of a block are held by 16 consecutive lanes,
+    // which find the block's maximum among themselves; no barrier until the end.
+    // Called once the first weight loads are in flight.
     const int64_t xrow_bytes = args.lda * 2;
     const uint32_t zoff = (uint32_t)(n * xrow_bytes);
+    const int64_t fpad = (n + 15) & ~int64_t(15);   // rows of fac per block
+    float *const fac = reinterpret_cast<float *>(xlds + zoff + 16);
     auto fill_lds = [&]() {
-        constexpr int kFillRegs = 2;   // (a row of 4096 over 256 threads: two each; more slowed the kernel)
-        int *ri = reinterpret_cast<int *>(xlds + zoff + 16);
-        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) ri[i] = 0;
+        const int64_t cpr = args.lda / 8, nch = n * cpr;   // (nch a multiple of 16)
+        for (int64_t i = threadIdx.x; i < (args.lda / 128) * (fpad - n); i += blockDim.x)
+            fac[(i / (fpad - n)) * fpad + n + i % (fpad - n)] = 0.f;
         if (threadIdx.x < 4) reinterpret_cast<uint32_t *>(xlds + zoff)[threadIdx.x] = 0u;
-        __syncthreads();
-        const int64_t cpr = args.lda / 8, nch = n * cpr;
         const uint16_t *xg = static_cast<const uint16_t *>(args.a);
-        auto row_of = [&](int64_t c) { return c / cpr; };
-        auto ld = [&](int64_t c) {
-            const int64_t r = row_of(c);
-            return *reinterpret_cast<const uint4 *>(xg + r * args.lda + 8 * (c - r * cpr));
-        };
-        auto absmax = [](uint4 v) {
-            uint32_t mx = pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
-                                     pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
-            return (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
-        };
-        uint4 keep[kFillRegs];
+        for (int64_t b0 = 0; b0 < nch; b0 += 2 * (int64_t)blockDim.x) {   // (uniform)
+            uint4 v[2];
+            int64_t cu[2];
 #pragma unroll
-        for (int i = 0; i < kFillRegs; ++i) {
-            const int64_t c = threadIdx.x + (int64_t)i * blockDim.x;
-            if (c < nch) keep[i] = ld(c);
-        }
-#pragma unroll
-        for (int i = 0; i < kFillRegs; ++i) {
-            const int64_t c = threadIdx.x + (int64_t)i * blockDim.x;
-            if (c < nch) atomicMax(reinterpret_cast<unsigned *>(ri) + row_of(c), absmax(keep[i]));
-        }
-        for (int64_t c = threadIdx.x + (int64_t)kFillRegs * blockDim.x; c < nch; c += blockDim.x)
-            atomicMax(reinterpret_cast<unsigned *>(ri) + row_of(c), absmax(ld(c)));
-        __syncthreads();
-        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-            const float mxf = bf16_to_f32((uint32_t)ri[i]);
-            int E = 0;
-            if (mxf > 0.f) frexpf(mxf, &E);     // mxf in [2^(E-1), 2^E)
-            ri[i] = mxf > 0.f ? 14 - E : 0;
-        }
-        __syncthreads();
-        auto cvt = [&](int64_t c, uint4 v) {
-            const int64_t r = row_of(c), k8 = 8 * (c - r * cpr);
-            const int sh = ri[r];
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int se = (p & 1) ? sh - 4 : sh;
-                const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(bf16_to_f32(w4[p] & 0xFFFFu), se));
-                const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(bf16_to_f32(w4[p] >> 16), se));
-                o[p] = lo | (hi << 16);
+            for (int u = 0; u < 2; ++u) {
+                cu[u] = b0 + u * (int64_t)blockDim.x + threadIdx.x;
+                const int64_t r = cu[u] / cpr;
+                v[u] = cu[u] < nch ? *reinterpret_cast<const uint4 *>(xg + r * args.lda + 8 * (cu[u] - r * cpr))
+                                   : make_uint4(0u, 0u, 0u, 0u);
             }
-            *reinterpret_cast<uint4 *>(xlds + r * xrow_bytes + 2 * k8) = make_uint4(o[0], o[1], o[2], o[3]);
-        };
 #pragma unroll
-        for (int i = 0; i < kFillRegs; ++i) {
-            const int64_t c = threadIdx.x + (int64_t)i * blockDim.x;
-            if (c < nch) cvt(c, keep[i]);
+            for (int u = 0; u < 2; ++u) {
+                uint32_t mx = pk_max_u16(pk_max_u16(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu),
+                                         pk_max_u16(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu));
+                mx = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {   // every lane of the wave takes part
+                    const uint32_t t = (uint32_t)__shfl_xor((int)mx, o);
+                    mx = t > mx ? t : mx;
+                }
+                const uint32_t E = mx >> 7, c = E > 29u ? E - 29u : 0u;
+                if (cu[u] < nch) {
+                    const int64_t r = cu[u] / cpr, k8 = 8 * (cu[u] - r * cpr);
+                    *reinterpret_cast<f16x8 *>(xlds + r * xrow_bytes + 2 * k8) =
+                        bf16_to_f16_scaled(v[u], (c << 7) * 0x00010001u, ((c + 4) << 7) * 0x00010001u);
+                    if ((cu[u] & 15) == 0) fac[(k8 >> 7) * fpad + r] = __int_as_float((int)((c + 15u) << 23));
+                }
+            }
         }
-        for (int64_t c = threadIdx.x + (int64_t)kFillRegs * blockDim.x; c < nch; c += blockDim.x)
-            cvt(c, ld(c));
         __syncthreads();
     };
 
@@ -384,8 +364,9 @@ qgemm_kernel(const GemmArgs args) {
           } else {
             // Exact operands: the codes as fp16 q - zero (16x at k-offsets 2, 3,
             // 6, 7), the activation rows as fp16 times a power of two: one per
-            // (row, block) converted here from bf16 (qi4_dev.h), or one per row
-            // from prep_rows (AM 3, applied at the store).  The products are
+            // (row, block) converted here from bf16 (qi4_dev.h) or by the
+            // workgroup into LDS (AM 4), or one per row from prep_rows (AM 3,
+            // applied at the store).  The products are
             // exact and a code on its zero point adds exactly 0.  One MFMA chain
             // per tile and block (two with 64-wide groups), then the scale (times
             // 2^(c - 112) for the blocks converted here) per output row.
@@ -408,6 +389,19 @@ qgemm_kernel(const GemmArgs args) {
                 const int fb = (int)((c + 15u) << 23);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) f[m][v] = __int_as_float(__shfl(fb, 4 * j + v));
+            }
+            if constexpr (ALDS) {
+                // the block factors of this lane's result rows 4 j .. 4 j + 3
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m >= m_used) break;
+                    const float4 t = *reinterpret_cast<const float4 *>(
+                        fac + (int64_t)(q.ag >> 8) * fpad + c0 + m * spt + 4 * j);
+                    f[m][0] = t.x;
+                    f[m][1] = t.y;
+                    f[m][2] = t.z;
+                    f[m][3] = t.w;
+                }
             }
             // activation operands of the 4 k steps, shared by the tiles
             f16x8 a[MT][4];
@@ -454,7 +448,7 @@ qgemm_kernel(const GemmArgs args) {
                     for (int v = 0; v < 4; ++v) {
                         float g = s0 * acc[m][0][v];
                         if constexpr (H == 2) g += s1 * acc[m][H - 1][v];
-                        if constexpr (AF16 || ALDS) res[m][nb][v] += g;
+                        if constexpr (AF16) res[m][nb][v] += g;
                         else res[m][nb][v] += f[m][v] * g;
                     }
                 }
@@ -485,10 +479,6 @@ qgemm_kernel(const GemmArgs args) {
                 }
                 if constexpr (AF16) {   // the row's power of two
                     const int e = args.a_exp[src_row(slot)];
-                    val = ldexpf(val, e);
-                    uval = ldexpf(uval, e);
-                } else if constexpr (ALDS) {
-                    const int e = -reinterpret_cast<const int *>(xlds + zoff + 16)[src_row(slot)];
                     val = ldexpf(val, e);
                     uval = ldexpf(uval, e);
                 }
@@ -686,8 +676,8 @@ qgemm_kernel(const GemmArgs args) {
 template <int NB, int MT, int S, int H>
 int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
     if (a.a_f32 && NB > 2) return QI4_ERR_UNSUPPORTED;
-    // AM 4: the fp16 rows, 16 zero bytes and one int per row in dynamic LDS
-    const size_t dyn = a.a_lds ? (size_t)(a.T * a.lda * 2 + 16 + 4 * a.T) : 0;
+    // AM 4: the fp16 rows, 16 zero bytes and the block factors in dynamic LDS
+    const size_t dyn = a.a_lds ? (size_t)lds_act_bytes(a.T, a.lda) : 0;
     if (a.epi == QI4_EPI_SILU_MUL) {
         if constexpr (NB % 2 == 0) {
             if (a.a_i8)
