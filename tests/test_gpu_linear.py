@@ -138,3 +138,21 @@ def test_repeat_is_deterministic():
     a = q.qlinear(x, packed, N, out_dtype=torch.float32)
     b = q.qlinear(x, packed, N, out_dtype=torch.float32)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 80, 2048), (3, 48, 1024), (17, 40, 512), (2, 4096, 4096),
+                                   (20, 64, 2048)])
+def test_blocks_of_very_different_magnitude(T, N, K):
+    """Each 128-wide block of a row carries its own power of two (2^-24 .. 2^+24,
+    a different one per block and row), so the rows' fp16 conversion must use
+    one exponent per (row, block): a factor applied to the wrong block or row
+    is off by many orders of magnitude against 2e-3 * sum|w*x|.  Few short rows
+    are converted into LDS by each workgroup, T = 20 x 2048 in registers."""
+    w = workloads.weights(61, T * 100 + K, N, K, 0.005, 0.02)
+    x = workloads.activations(61, N + K, T, K, "bf16")
+    xf = workloads.bf16_bits_to_f32(x).reshape(T, K // 128, 128)
+    e = (np.arange(T)[:, None] * 5 + np.arange(K // 128)[None, :] * 11) % 49 - 24
+    x = workloads.f32_to_bf16_bits((xf * np.exp2(e)[:, :, None]).reshape(T, K).astype(np.float32))
+    got = _run(w, x, "bf16", "f32")
+    ref, S = oracle.linear(oracle.widen(x, "bf16"), w["qweight"], w["scales"], w["zeros"], N, K)
+    assert_within(got, ref, oracle.C_TOL * S, f"wide-range blocks T{T} N{N} K{K}")
