@@ -918,6 +918,21 @@ def main():
         "router": router,
         "cpu_baseline": cpu,
     }
+    # the headline figures of the sections above, rounded, last in the line (a
+    # reader that sees only the end of the output still finds them)
+    r3 = lambda v: None if v is None else round(v, 3)
+    out["summary"] = {
+        "decode_tokens_per_s": {str(r["T"]): round(r["tokens_per_s"]) for r in
+                                [*sweep, {"T": args.T, "tokens_per_s": main_r["tokens_per_s"]}]},
+        "gate_up_hbm_frac": r3(gu_gbps / HBM_PEAK_GBPS),
+        "gate_up_frac_of_probe_read": r3(gu_gbps / probes["stream_read"]["GBps"]),
+        "prefill_ms_per_step": r3(prefill["ms_per_step"]) if prefill else None,
+        "prefill_mfma_frac": r3(prefill["mfma_frac_step"]) if prefill else None,
+        "dense_stack_us": r3(dense["llama7b_stack"]["eager_us"]) if dense else None,
+        "dense_stack_frac_of_read_probe": r3(dense["llama7b_stack"]["frac_of_read_probe"]) if dense else None,
+        "quantize_us": r3(quant["us"]) if quant else None,
+        "cpu_tokens_per_s": r3(cpu["value"]) if cpu else None,
+    }
     print(json.dumps(out), flush=True)
 
 
