@@ -20,8 +20,8 @@
 //    stream;
 //  * the activation tile of each group is copied from memory straight into LDS
 //    (buffer loads with the LDS bit), each 4-lane quad reading 64 contiguous
-//    bytes, in a rotated order that keeps the MFMA operand reads free of bank
-//    conflicts, and shared by all waves of the workgroup;
+//    bytes, in a rotated order that spreads the MFMA operand reads over the
+//    LDS banks, and shared by all waves of the workgroup;
 //  * a workgroup whose weights hold a scale the 16x operands cannot represent
 //    (|scale| >= 256, inf, NaN) hands its tile to a pass with plain operands.
 #include <type_traits>
@@ -246,8 +246,12 @@ __device__ __forceinline__ void run_tile(const PrefillArgs &args, const PackedLa
     // A copy request moves 16 bytes per lane to LDS at 16 * lane.  Lane l
     // copies row l / 4 of the fragment, so every 4 consecutive lanes read 64
     // contiguous bytes (the address unit coalesces them); inside the quad the
-    // four 16-byte chunks are rotated by rot(row), which makes the MFMA operand
-    // reads below hit distinct LDS banks in every 8- or 16-lane phase.
+    // four 16-byte chunks are rotated by rot(row), so that the 16 lanes of each
+    // k quarter of an MFMA operand read (j fixed) hit 16 different 16-byte
+    // bank groups.  On this chip the operand reads still stall 4 cycles per
+    // KiB (counters); reads in lane order (16 * lane) would not, but then each
+    // copy request gathers 16 bytes from 16 rows per 16 lanes, which measured
+    // 7-10 % slower overall.
     auto rot = [](int r) { return ((r >> 1) + (r >> 3)) & 3; };
     auto frag_sub = [&](int i) { return (FPW * wave + i) >> 2; };
     auto frag_k = [&](int i) { return (FPW * wave + i) & 3; };
