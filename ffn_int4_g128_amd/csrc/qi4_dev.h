@@ -86,7 +86,11 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
 }
 // Out-of-range offsets.  Valid lane offsets stay below 2^31 (every buffer is
 // smaller than 2 GiB), so kOob (lane part) and kOobS (wave part) reach past
-// every resource and their sum, at most 2^32 - 1, never wraps around.
+// every resource, and kOob + kOobS = 2^32 - 1 does not wrap around.  (The
+// decode GEMM adds up to a few hundred bytes to a lane part of kOob for the
+// fragments of a row past the end; with a wave part of kOobS such a sum wraps
+// and the load may read the first bytes of the buffer, which only reach a
+// result row that is never stored.)
 constexpr uint32_t kOob = 0x80000000u;
 constexpr uint32_t kOobS = 0x7FFFFFFFu;
 

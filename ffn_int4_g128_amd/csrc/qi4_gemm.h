@@ -31,6 +31,8 @@ struct GemmArgs {
     const int32_t *a_exp;      // a_f16: per-row exponent
     int a_lds;                 // bf16 rows converted into LDS by each workgroup (dense
                                // calls whose T * K * 2 bytes fit kLdsActBytes)
+    int a_tr;                  // bf16 rows converted in registers, loaded row-major and
+                               // put in operand order through LDS (set by the launch)
     float a_scale;             // W4A8: the activations' scale, applied at the store
     int P;                     // A rows per slot: parts summed at the end (1, 2 or 4)
     int a_shift;               // weight block b reads activation block b >> a_shift

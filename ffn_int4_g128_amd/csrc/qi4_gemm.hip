@@ -36,6 +36,7 @@ namespace qi4 {
 namespace {
 
 constexpr int kMaxWaves = 8;
+constexpr int kA5TransposeBytes = 4096;   // per wave and M tile, activation mode 5
 constexpr bool kDenseMSplit = true;   // see launch_qgemm
 constexpr bool kDownWaveBlocks = true;   // see launch_qgemm
 // (wave, m, nb) partial tiles the LDS reduction buffer holds: 16 (16 KiB), or
@@ -72,7 +73,10 @@ __device__ inline uint4 split_frag(uint4 u, uint4 v, int part) {
 // 2 int8 rows in operand order (W4A8; 32 bytes per lane per block), 3 fp16
 // rows with a per-row power of two (prep_rows), 4 bf16 rows that each
 // workgroup first converts into LDS as fp16 rows with a per-row power of two
-// (few short rows: the whole activation matrix fits in LDS).
+// (few short rows: the whole activation matrix fits in LDS), 5 bf16 rows as in
+// mode 0, loaded row-major (16 lanes per row, four rows per load, full cache
+// lines) and put in operand order through 4 KiB of LDS per wave: a load in
+// operand order touches 64 bytes of each of 16 rows.
 template <int NB, int MT, int AM, int H>
 struct Stage {
     uint4 cw[NB];
@@ -252,6 +256,7 @@ qgemm_kernel(const GemmArgs args) {
         // next S - 1 steps are in flight.
         Stage<NB, MT, AM, H> st[S];
         uint32_t abase[MT];
+        uint32_t acol[MT][4];   // AM 5: the lane's row-major chunk of each load (see load_a)
         int apart[MT];
         // Load cursor (wave-uniform): block lr, step li of that block, and the
         // byte offsets of that step's codes (first tile of the block), scale and
@@ -290,7 +295,12 @@ qgemm_kernel(const GemmArgs args) {
             const uint32_t oa = in ? loa : kOobS;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if constexpr (AI8) {
+                if constexpr (AM == 5) {
+                    // row-major: 16 lanes read one row's 256 bytes of the block,
+                    // a load covers four rows (transposed in compute)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) q.af[m][s4][0] = buf_b128(ar, acol[m][s4], oa);
+                } else if constexpr (AI8) {
                     q.af[m][0][0] = buf_b128(ar, abase[m], oa);
                     q.af[m][1][0] = buf_b128(ar, abase[m] + 16u, oa);
                 } else {
@@ -372,15 +382,50 @@ qgemm_kernel(const GemmArgs args) {
             // 2^(c - 112) for the blocks converted here) per output row.
             const uint32_t magic = f16_magic_pair();
             uint4 raw[MT][4];
+            if constexpr (AM == 5) {
+                // the row-major chunks through this wave's 4 KiB of LDS per M
+                // tile into operand order (lane 16 j + r: row r, bytes 64 s +
+                // 16 j of the block for k step s).  Chunk c of row r sits at
+                // 16 (c ^ r) of the row's 256 bytes, so that the 16 lanes of a
+                // write (one row) and of a read (one chunk of 16 rows) touch
+                // 16 different 16-byte bank groups.  One wave's LDS operations
+                // run in order; the fences keep the compiler from moving them.
+                uint8_t *tw = xlds + (uint32_t)(wave * MT * kA5TransposeBytes);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m >= m_used) break;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int rw = (lane >> 4) + 4 * s4;
+                        *reinterpret_cast<uint4 *>(tw + m * kA5TransposeBytes + rw * 256 + 16 * ((lane & 15) ^ rw)) =
+                            q.af[m][s4][0];
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m >= m_used) break;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        raw[m][s4] = *reinterpret_cast<const uint4 *>(
+                            tw + m * kA5TransposeBytes + r16 * 256 + 16 * ((4 * s4 + j) ^ r16));
+                }
+            }
             uint32_t cc[MT], cc4[MT];
             float f[MT][4];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 if (AF16 || ALDS || m >= m_used) break;
+                if constexpr (AF32) {
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    raw[m][s4] = AF32 ? split_frag(q.af[m][s4][0], q.af[m][s4][AF32 ? 1 : 0], apart[m])
-                                      : q.af[m][s4][0];
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        raw[m][s4] = split_frag(q.af[m][s4][0], q.af[m][s4][1], apart[m]);
+                } else if constexpr (AM == 0) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) raw[m][s4] = q.af[m][s4][0];
+                }
                 const uint32_t c = row_block_offset(bf16_absmax_bits(raw[m]));
                 cc[m] = (c << 7) * 0x00010001u;
                 cc4[m] = ((c + 4) << 7) * 0x00010001u;
@@ -634,6 +679,13 @@ qgemm_kernel(const GemmArgs args) {
             // (int8 rows: a lane's 32 bytes of a block sit at 32 j; AM 4: an
             // offset into the LDS rows)
             abase[m] = ok ? (uint32_t)(row * args.lda * ES + (AI8 ? 32 * j : 8 * j * ES)) : kOob;
+            if constexpr (AM == 5) {   // (one part per slot) rows (lane >> 4) + 4 s4 of the tile
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int64_t sl = c0 + (int64_t)m * spt + (lane >> 4) + 4 * s4;
+                    acol[m][s4] = sl < n ? (uint32_t)(src_row(sl) * args.lda * 2 + 16 * (lane & 15)) : kOob;
+                }
+            }
         }
         lr = 0;
         li = 0;
@@ -676,8 +728,10 @@ qgemm_kernel(const GemmArgs args) {
 template <int NB, int MT, int S, int H>
 int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
     if (a.a_f32 && NB > 2) return QI4_ERR_UNSUPPORTED;
-    // AM 4: the fp16 rows, 16 zero bytes and the block factors in dynamic LDS
+    // AM 4: the fp16 rows, 16 zero bytes and the block factors in dynamic LDS;
+    // AM 5: 4 KiB per wave and M tile for the transposition
     const size_t dyn = a.a_lds ? (size_t)lds_act_bytes(a.T, a.lda) : 0;
+    const size_t dyn5 = (size_t)(threads / 64) * MT * kA5TransposeBytes;
     if (a.epi == QI4_EPI_SILU_MUL) {
         if constexpr (NB % 2 == 0) {
             if (a.a_i8)
@@ -688,6 +742,8 @@ int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
                 qgemm_kernel<NB, MT, 4, S, QI4_EPI_SILU_MUL, H><<<grid, threads, dyn, st>>>(a);
             else if (NB <= 2 && a.a_f32)
                 qgemm_kernel<NB <= 2 ? NB : 2, MT, 1, 2, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
+            else if (MT == 1 && a.a_tr)
+                qgemm_kernel<NB, 1, 5, S, QI4_EPI_SILU_MUL, H><<<grid, threads, dyn5, st>>>(a);
             else
                 qgemm_kernel<NB, MT, 0, S, QI4_EPI_SILU_MUL, H><<<grid, threads, 0, st>>>(a);
         } else {
@@ -701,6 +757,8 @@ int launch_cfg_h(const GemmArgs &a, dim3 grid, int threads, hipStream_t st) {
         qgemm_kernel<NB, MT, 4, S, QI4_EPI_NONE, H><<<grid, threads, dyn, st>>>(a);
     } else if (NB <= 2 && a.a_f32) {
         qgemm_kernel<NB <= 2 ? NB : 2, MT, 1, 2, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
+    } else if (MT == 1 && a.a_tr) {
+        qgemm_kernel<NB, 1, 5, S, QI4_EPI_NONE, H><<<grid, threads, dyn5, st>>>(a);
     } else {
         qgemm_kernel<NB, MT, 0, S, QI4_EPI_NONE, H><<<grid, threads, 0, st>>>(a);
     }
@@ -783,12 +841,22 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
     int64_t gy = n_problems;
     GemmArgs a = args;
     a.m_rows = 0;
+    a.a_tr = 0;
     if (!args.moe && MT == 2 && !args.a_lds && kDenseMSplit) {
         MT = 1;
         a.m_rows = spt;
         gy = ceil_div(max_slots, (int64_t)spt);
+        // bf16 rows: loaded row-major and transposed through LDS (activation
+        // mode 5; 13824 -> 5120 at T = 32: 42.7 -> 35.9 us, 8-bit codes 77.0 ->
+        // 63.8 us).  Not below 17 rows: with one M tile of rows per call the
+        // extra LDS round trip cost 1 us at T = 4 and 8.
+        if (!a.a_f32 && !a.a_i8 && !a.a_f16) a.a_tr = 1;
     }
     while (W > 1 && W * MT * NB > red_slots(NB, MT)) W /= 2;
+    // activation mode 5: the transposition buffers and the reduction buffer
+    // within 64 KiB
+    if (a.a_tr)
+        while (W > 1 && W * MT * kA5TransposeBytes + red_slots(NB, MT) * 1024 > 65536) W /= 2;
     a.blocks_per_wg = R;
     // pair / top_k as a multiply-high: with m = floor((2^32 - 1) / k) + 1,
     // floor(p * m / 2^32) = floor(p / k) whenever p * k < 2^32 (pairs are below

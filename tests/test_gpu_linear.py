@@ -1,6 +1,8 @@
 """GPU parity of qlinear_int4_g128 against the oracle: the small GEMV, ragged and
 multi-tile shapes, the fused SiLU(gate)*up epilogue, the Llama-7B-shaped decode
 stack and the skinny decode sweep (every token at full size), plus edge cases.
+Shapes with more than 16 rows and rows too long for LDS (T = 33, 47, 64; the
+SiLU cases at T = 17 and 40) take the row-major activation loads.
 Tolerance: |gpu - oracle| <= 2e-3 * sum_k |w*x| per output element; for the
 fused epilogue its first-order propagation through SiLU(g)*u."""
 import numpy as np
@@ -37,7 +39,8 @@ def test_gemv_small_f32():
 @pytest.mark.parametrize("T,N,K,xd,od", [
     (1, 128, 256, "bf16", "f32"), (3, 17, 128, "bf16", "f32"), (16, 130, 384, "bf16", "bf16"),
     (17, 64, 512, "bf16", "f32"), (33, 48, 1024, "bf16", "f32"), (5, 200, 2048, "f32", "f32"),
-    (7, 33, 256, "f32", "bf16"), (1, 4096, 4096, "bf16", "bf16"), (64, 96, 640, "bf16", "f32")])
+    (7, 33, 256, "f32", "bf16"), (1, 4096, 4096, "bf16", "bf16"), (64, 96, 640, "bf16", "f32"),
+    (47, 4112, 1536, "bf16", "bf16")])
 def test_shapes(T, N, K, xd, od):
     w = workloads.weights(31, T * 1000 + N, N, K, 0.005, 0.02)
     x = workloads.activations(31, N + K, T, K, xd)
@@ -47,7 +50,8 @@ def test_shapes(T, N, K, xd, od):
 
 
 @pytest.mark.parametrize("T,I,K,od", [(1, 64, 256, "f32"), (4, 24, 128, "f32"),
-                                      (19, 40, 384, "bf16"), (1, 11008, 4096, "bf16")])
+                                      (19, 40, 384, "bf16"), (1, 11008, 4096, "bf16"),
+                                      (40, 64, 2048, "f32"), (17, 1000, 1024, "bf16")])
 def test_silu_mul_epilogue(T, I, K, od):
     import ffn_int4_g128_amd as q
     w = workloads.weights(41, I + T, 2 * I, K, 0.005, 0.02)
