@@ -831,7 +831,11 @@ int launch_qgemm(const GemmArgs &args, int n_problems, int64_t max_slots, hipStr
             W = 2;
         }
     } else {
-        if (max_slots > 8 && ceil_div(nt, 4) >= 192 && !args.a_f32) NB = 4;
+        // (W4A8 rows split over grid.y: a quad per workgroup down to 64 quads,
+        // 13824 -> 5120 at T = 32 32.7 -> 28.8 us; bf16 rows there got slower)
+        if (max_slots > 8 && !args.a_f32 &&
+            (ceil_div(nt, 4) >= 192 || (args.a_i8 && max_slots > spt && ceil_div(nt, 4) >= 64)))
+            NB = 4;
         W = 1;
         while (W < kMaxWaves && G / (2 * W) >= 8) W *= 2;
         // one row, one tile per workgroup: all eight waves (Llama-7B O

@@ -57,7 +57,8 @@ def test_int8_activations_bit_exact(xd, T, K, scale):
 @pytest.mark.parametrize("T,N,K,xd", [(1, 130, 768, "bf16"), (5, 64, 1024, "f32"),
                                       (16, 48, 512, "bf16"), (17, 80, 512, "bf16"),
                                       (32, 1000, 2048, "bf16"), (100, 40, 384, "f32"),
-                                      (1, 4096, 4096, "bf16")])
+                                      (1, 4096, 4096, "bf16"), (32, 5120, 1024, "bf16"),
+                                      (20, 4112, 512, "bf16")])
 def test_qlinear_w4a8(group, T, N, K, xd):
     import torch
     import ffn_int4_g128_amd as q
