@@ -132,10 +132,11 @@ def test_zero_scale_rows_and_empty_batch():
     assert y.shape == (0, N)
 
 
-def test_repeat_is_deterministic():
+@pytest.mark.parametrize("T", [9, 40])
+def test_repeat_is_deterministic(T):
     import torch
     import ffn_int4_g128_amd as q
-    T, N, K = 9, 1000, 4096
+    N, K = 1000, 4096
     w = workloads.weights(53, 0, N, K, 0.005, 0.02)
     x = bf16_dev(workloads.activations(53, 1, T, K, "bf16"))
     packed = pack_canonical(w)
