@@ -4,7 +4,7 @@ kernels, the library's per-GPU scratch array in place of the caller's
 workspace), on consecutive calls whose second input is smaller than the first
 (the array keeps the previous call's contents), on the decode and the prefill
 paths, and it must reject a layer too large for the array before launching
-anything."""
+anything.  Captured in a HIP graph, its replays give the eager output."""
 import ctypes
 
 import numpy as np
@@ -72,3 +72,30 @@ def test_noalloc_given_routing_and_dsv3_shape_limit():
     torch.cuda.synchronize()
     assert rc == -5  # QI4_ERR_WORKSPACE
     assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("T", [8, 150])
+def test_noalloc_under_graph_capture(T):
+    """The use the entry point is for: captured in a HIP graph (no allocation
+    inside the call), every replay, with eager work between, gives the eager
+    call's output bit for bit; decode and prefill paths."""
+    import torch
+    import ffn_int4_g128_amd as q
+    E, H, I, k = 8, 512, 256, 2
+    _, _, mw = _layer(E, H, I, 140)
+    xt = bf16_dev(workloads.activations(141, T, T, H, "bf16"))
+    lt = to_dev(workloads.logits_normal(142, T, T, E))
+    print(f"noalloc graph capture: T={T}", flush=True)
+    eager = q.moe_ffn_noalloc(xt, mw, k, logits=lt).clone()
+    out = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.moe_ffn_noalloc(xt, mw, k, logits=lt, out=out)
+    for r in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+    del g
