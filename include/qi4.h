@@ -166,7 +166,9 @@ int qi4_quantize_int8(const void *w, int w_dtype, int64_t N, int64_t K, int grou
  *   epilogue QI4_EPI_SILU_MUL needs flags == QI4_PACK_GATEUP and gives
  *            y[t][i] = SiLU(g) * u with g, u the rows i and N/2 + i of [gate; up].
  * Accumulation is float32; the result is rounded once to y_dtype.  T == 0 is a
- * valid no-op.  float32 activations are used exactly (split into bf16 terms). */
+ * valid no-op.  float32 activations are used exactly (split into bf16 terms).
+ * x must be finite: a row holding an inf or NaN gives unspecified (possibly
+ * finite) values in that row of y, and leaves the other rows as they are. */
 int qlinear_int4_g128(const void *x, int x_dtype, int64_t T, int64_t K,
                       const void *packed_w, int64_t N, int flags,
                       void *y, int y_dtype, int epilogue, void *stream);
@@ -312,7 +314,8 @@ int moe_combine(const qi4_moe_desc *d, const float *y, const float *topk_weights
  *   shared_gate_up / shared_down: NULL iff has_shared == 0.
  *   workspace: moe_ffn_int4_workspace_bytes(d, T) bytes, 256-byte aligned.
  * The combine runs in a fixed order (slots 0..top_k-1, then the shared expert),
- * so results are deterministic. */
+ * so results are deterministic.  x must be finite (as for qlinear_int4_g128: a
+ * token whose row holds an inf or NaN gets unspecified values). */
 int moe_ffn_int4(const qi4_moe_desc *d, const void *x, int64_t T,
                  const float *router_logits, int32_t *topk_ids, float *topk_weights,
                  const void *w_gate_up, const void *w_down,

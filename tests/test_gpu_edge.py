@@ -8,7 +8,8 @@ offset c loses the small difference in the rounding of the two large sums; the
 tolerance 2e-3 * sum|w*x| (per output element) does not allow that.  These
 cases are checked element by element on every kernel family: the decode GEMM
 (bf16 and fp32 activations, plain and SiLU(gate)*up epilogue) and the MoE layer
-on its decode and prefill paths."""
+on its decode and prefill paths.  Also: a row holding an inf or NaN leaves
+every other row's result as the oracle gives it."""
 import numpy as np
 import pytest
 
@@ -125,3 +126,47 @@ def test_moe_sparse_codes_with_outliers(T):
     oids, op = oracle.topk_softmax(logits, k)
     ref, tol = oracle.moe(oracle.widen(x, "bf16"), oids, op, ex, sh, H, I, E)
     assert_within(to_f64(out), ref, tol, f"moe sparse codes T{T}")
+
+
+# bf16 bit patterns of +inf and a quiet NaN
+_BF16_INF, _BF16_NAN = 0x7F80, 0x7FC0
+
+
+@pytest.mark.parametrize("T,K,bad", [(3, 4096, _BF16_INF), (20, 4096, _BF16_NAN),
+                                     (40, 2048, _BF16_INF)])
+def test_nonfinite_row_leaves_other_rows(T, K, bad):
+    """One activation row holding an inf or NaN: the header leaves that row's
+    outputs unspecified; every other row must still match the oracle (rows
+    converted into LDS at T = 3, in registers / row-major beyond 16 rows)."""
+    N = 96
+    w = workloads.weights(18, T, N, K, 0.005, 0.02)
+    x = workloads.activations(19, T, T, K, "bf16").copy()
+    r = T // 2
+    x[r, 5] = bad
+    got = _linear(w, x, "bf16", "f32")
+    keep = [t for t in range(T) if t != r]
+    ref, S = oracle.linear(oracle.widen(x[keep], "bf16"), w["qweight"], w["scales"], w["zeros"],
+                           N, K)
+    assert_within(got[keep], ref, oracle.C_TOL * S, f"nonfinite row {r} of T{T}")
+
+
+@pytest.mark.parametrize("T", [8, 150])
+def test_moe_nonfinite_token_leaves_other_tokens(T):
+    """The MoE layer with one token's input row holding a NaN: every other
+    token matches the oracle (decode GEMMs at T = 8, prefill path at T = 150)."""
+    import torch
+    import ffn_int4_g128_amd as q
+    E, H, I, k = 8, 512, 256, 2
+    ex = workloads.moe_experts(20, 0, E, H, I, 0.005, 0.02)
+    sh = workloads.moe_shared(20, 0, H, I, 0.005, 0.02)
+    x = workloads.activations(21, T, T, H, "bf16").copy()
+    r = 3
+    x[r, 77] = _BF16_NAN
+    logits = workloads.logits_normal(22, T, T, E)
+    mw = q.pack_moe(ex, sh, E, H, I)
+    out = to_f64(q.moe_ffn(bf16_dev(x), mw, k, logits=to_dev(logits)))
+    torch.cuda.synchronize()
+    keep = [t for t in range(T) if t != r]
+    oids, op = oracle.topk_softmax(logits, k)
+    ref, tol = oracle.moe(oracle.widen(x[keep], "bf16"), oids[keep], op[keep], ex, sh, H, I, E)
+    assert_within(out[keep], ref, tol, f"moe nonfinite token {r} of T{T}")
