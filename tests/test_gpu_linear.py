@@ -40,7 +40,8 @@ def test_gemv_small_f32():
     (1, 128, 256, "bf16", "f32"), (3, 17, 128, "bf16", "f32"), (16, 130, 384, "bf16", "bf16"),
     (17, 64, 512, "bf16", "f32"), (33, 48, 1024, "bf16", "f32"), (5, 200, 2048, "f32", "f32"),
     (7, 33, 256, "f32", "bf16"), (1, 4096, 4096, "bf16", "bf16"), (64, 96, 640, "bf16", "f32"),
-    (47, 4112, 1536, "bf16", "bf16")])
+    (47, 4112, 1536, "bf16", "bf16"), (1, 48, 32768, "bf16", "f32"),
+    (3, 40, 20480, "f32", "bf16"), (24, 32, 16384, "bf16", "f32")])
 def test_shapes(T, N, K, xd, od):
     w = workloads.weights(31, T * 1000 + N, N, K, 0.005, 0.02)
     x = workloads.activations(31, N + K, T, K, xd)
